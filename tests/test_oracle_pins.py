@@ -1,0 +1,462 @@
+"""Pins of the CPU oracle to facts outside itself: figures printed on the pages
+(tests/golden/page_figures.json), library routines (torch's float8 codecs,
+numpy's log2 / dot / lexsort, torch's float64 softmax), closed forms,
+invariants and exact-rational brute force on tiny inputs."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_fp4_cache_amd.workloads import to_bf16_bits, bf16_bits_to_f32
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])  # the 8 magnitudes, max 6 (pinned below)
+
+
+def page(key):
+    return GOLD[key]["value"]
+
+
+def schedule_from_golden():
+    s = GOLD["schedule"]
+    modes, ms = [], []
+    modes += ["swa"] * s["encoder"]["swa_only_layers"]
+    ms += [s["encoder"]["m"]] * s["encoder"]["swa_only_layers"]
+    for _ in range(s["encoder"]["groups"]):
+        modes += s["encoder"]["group"]
+        ms += [s["encoder"]["m"]] * len(s["encoder"]["group"])
+    modes += s["decoder"]["first_group"]
+    ms += [s["decoder"]["m"]] * len(s["decoder"]["first_group"])
+    for _ in range(s["decoder"]["groups"]):
+        modes += s["decoder"]["group"]
+        ms += [s["decoder"]["m"]] * len(s["decoder"]["group"])
+    return modes, ms
+
+
+# ------------------------------------------------------------ sizes -------
+def test_entry_sizes_match_pages():
+    assert oracle.entry_bytes(512, 16) == page("main_entry_bytes")
+    assert oracle.entry_bytes(128, 32) == page("index_entry_bytes")
+    assert oracle.bits_per_channel(16) == page("bits_per_channel_main")
+    assert oracle.bits_per_channel(32) == page("bits_per_channel_index")
+    # 512 channels at 8 bits was the FP8 entry; the FP4 entry is a bit more than half of it
+    assert 512 * 8 // 8 == page("fp8_main_entry_bytes")
+    assert 0.5 < page("main_entry_bytes") / page("fp8_main_entry_bytes") < 0.6
+
+
+def test_global_footprint_890_and_087_gib():
+    modes, ms = schedule_from_golden()
+    assert len(modes) == 40
+    writers = [i for i, m in enumerate(modes) if m == "full"]
+    assert writers == page("writer_layers")
+    per_tok = oracle.global_bytes_per_token(modes, ms)
+    assert per_tok == page("global_bytes_per_token")
+    total = per_tok * page("context_tokens")
+    assert total == 933_232_640
+    assert round(total / 2**30, 2) == page("global_gib_at_context")
+    # one m = 2 source cache alone: 178 B/token
+    assert oracle.global_bytes_per_token(["full"], [2]) == 178.0
+
+
+# ---------------------------------------------------------- formats -------
+def test_e2m1_value_set():
+    vals = [oracle.e2m1_value(c) for c in range(16)]
+    mags = sorted(set(abs(v) for v in vals))
+    assert len(mags) == page("e2m1_magnitudes")
+    assert max(mags) == page("e2m1_max")
+    assert np.array_equal(np.array(mags), E2M1)
+    for c in range(8):  # sign bit mirrors the magnitude
+        assert vals[c + 8] == -vals[c] and math.copysign(1, vals[c + 8]) == -1
+
+
+def test_e4m3_decode_matches_torch_float8():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = np.array([oracle.e4m3_value(b) for b in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(ours))
+    assert np.array_equal(ref[~nan], ours[~nan])
+    assert np.nanmax(ours) == page("e4m3_max")
+
+
+def test_e8m0_decode_matches_torch_float8():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    ours = np.array([oracle.e8m0_value(u) for u in range(256)])
+    assert np.isnan(ours[255]) and np.isnan(ref[255])
+    assert np.array_equal(ref[:255], ours[:255])
+
+
+def test_bf16_decode():
+    x = np.float32([1.0, -2.5, 3.140625, 0.0, -0.0, 1e-30])
+    b = to_bf16_bits(x)
+    for bi, xi in zip(b, bf16_bits_to_f32(b)):
+        assert oracle.bf16_value(int(bi)) == float(xi)
+
+
+# ------------------------------------------------------- quantisers -------
+def _blocks(vals, n):
+    """bf16 blocks of length n whose first element fixes the block max."""
+    return to_bf16_bits(np.asarray(vals, np.float32).reshape(-1, n))
+
+
+def test_e2m1_codes_round_trip_all_16():
+    # a block holding 6 has NV16 scale 1 (E4M3 0x38) and MX32 scale 1 (E8M0 127)
+    vals = [oracle.e2m1_value(c) for c in range(16)]
+    nv = _blocks(vals, 16)
+    codes, sc = oracle.quant_nv16(nv)
+    assert sc[0] == 0x38
+    assert list(codes[0]) == list(range(16))
+    mx = _blocks(vals + vals, 32)
+    codes, sc = oracle.quant_mx32(mx)
+    assert sc[0] == 127
+    assert list(codes[0]) == list(range(16)) * 2
+
+
+@pytest.mark.parametrize("kind", ["nv16", "mx32"])
+def test_hand_worked_midpoints_at_scale_one(kind):
+    # value -> expected code at scale 1; exact midpoints go to the even code
+    cases = {0.25: 0x0, 0.75: 0x2, 1.25: 0x2, 1.75: 0x4, 2.5: 0x4, 3.5: 0x6, 5.0: 0x6, 0.3: 0x1, 5.5: 0x7,
+             -0.0: 0x8, -0.2: 0x8, -5.0: 0xE}
+    n = 16 if kind == "nv16" else 32
+    for v, want in cases.items():
+        block = [6.0] + [v] + [0.0] * (n - 2)
+        codes, sc = (oracle.quant_nv16 if kind == "nv16" else oracle.quant_mx32)(_blocks(block, n))
+        assert codes[0][1] == want, (kind, v, codes[0][1])
+
+
+def test_mx32_clips_above_six():
+    # amax 7: floor(log2 7) = 2 -> scale 1, and 7 > 6 clips to code 7
+    codes, sc = oracle.quant_mx32(_blocks([7.0] + [0.0] * 31, 32))
+    assert sc[0] == 127 and codes[0][0] == 7
+
+
+def test_nv16_saturation_matches_page_range():
+    rng = page("fp4_range_max")
+    assert rng == page("e4m3_max") * page("e2m1_max")
+    codes, sc = oracle.quant_nv16(_blocks([rng] + [0.0] * 15, 16))
+    assert sc[0] == 0x7E and oracle.e4m3_value(0x7E) == page("e4m3_max") and codes[0][0] == 7
+    codes, sc = oracle.quant_nv16(_blocks([-5000.0] + [1.0] * 15, 16))
+    assert sc[0] == 0x7E and codes[0][0] == 0xF  # decodes to -2688
+
+
+def test_nv16_zero_and_tiny_blocks():
+    codes, sc = oracle.quant_nv16(_blocks([0.0] * 8 + [-0.0] * 8, 16))
+    assert sc[0] == 0 and list(codes[0]) == [0] * 8 + [8] * 8
+    # amax/6 <= 2^-10 rounds to a zero scale -> signed zeros
+    codes, sc = oracle.quant_nv16(_blocks([6 * 2.0**-10, -1e-4] + [0.0] * 14, 16))
+    assert sc[0] == 0 and codes[0][0] == 0 and codes[0][1] == 8
+    # just above: smallest subnormal scale 2^-9
+    codes, sc = oracle.quant_nv16(_blocks([6 * 2.0**-9] + [0.0] * 15, 16))
+    assert sc[0] == 1 and codes[0][0] == 7
+
+
+def test_nv16_scale_rule_matches_torch_rne():
+    # the scale is the E4M3FN value nearest to amax/6 (torch's float8 rounding is RNE)
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal((4000, 16)) * np.exp(rng.uniform(-9, 6, (4000, 1)))).astype(np.float32)
+    xb = to_bf16_bits(x)
+    amax = np.abs(bf16_bits_to_f32(xb)).max(axis=1).astype(np.float64)
+    amax = np.minimum(amax, 2688.0)
+    xb[:, 0] = np.where(np.abs(bf16_bits_to_f32(xb[:, 0])) > 2688, to_bf16_bits(np.float32(2688.0)), xb[:, 0])
+    amax = np.abs(bf16_bits_to_f32(xb)).max(axis=1).astype(np.float64)
+    _, sc = oracle.quant_nv16(xb)
+    ref = torch.from_numpy((amax / 6.0).astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(sc, ref)
+
+
+def test_mx32_scale_rule_matches_numpy_log2():
+    rng = np.random.default_rng(2)
+    x = (rng.standard_normal((4000, 32)) * np.exp(rng.uniform(-60, 60, (4000, 1)))).astype(np.float32)
+    xb = to_bf16_bits(x)
+    amax = np.abs(bf16_bits_to_f32(xb)).max(axis=1).astype(np.float64)
+    _, sc = oracle.quant_mx32(xb)
+    ref = np.clip(np.floor(np.log2(amax)) - 2 + 127, 0, 254)
+    assert np.array_equal(sc.astype(np.float64), ref)
+    codes, sc = oracle.quant_mx32(_blocks([0.0] * 16 + [-0.0] * 16, 32))
+    assert sc[0] == 0 and list(codes[0]) == [0] * 16 + [8] * 16
+
+
+def _deq(codes, scale):
+    return np.where(codes & 8, -1.0, 1.0) * E2M1[codes & 7] * scale
+
+
+@pytest.mark.parametrize("kind", ["nv16", "mx32"])
+def test_quantiser_invariants(kind):
+    n = 16 if kind == "nv16" else 32
+    q = oracle.quant_nv16 if kind == "nv16" else oracle.quant_mx32
+    dec = (lambda u: oracle.e4m3_value(int(u))) if kind == "nv16" else (lambda u: 2.0 ** (int(u) - 127))
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((2000, n)) * np.exp(rng.uniform(-4, 4, (2000, 1)))).astype(np.float32)
+    xb = to_bf16_bits(x)
+    codes, sc = q(xb)
+    s = np.array([dec(u) for u in sc])[:, None]
+    d = _deq(codes, s)
+    # error bound: within half the local gap of the E2M1 grid when |x| <= 6 s
+    xf = bf16_bits_to_f32(xb).astype(np.float64)
+    gaps = np.array([0.25, 0.25, 0.25, 0.25, 0.5, 0.5, 1.0, 1.0])  # half-gap around each magnitude
+    inside = np.abs(xf) <= 6 * s
+    assert np.all(np.abs(xf - d)[inside] <= (gaps[codes & 7] * s)[inside] + 0.0)
+    # sign symmetry
+    codes_n, sc_n = q(to_bf16_bits(-x))
+    assert np.array_equal(sc_n, sc) and np.array_equal(codes_n, codes ^ 8)
+    # idempotence: re-quantising the dequantised block reproduces the codes
+    if kind == "mx32":
+        codes2, sc2 = q(to_bf16_bits(d.astype(np.float32)))
+        assert np.array_equal(codes2, codes) and np.array_equal(sc2, sc)
+    else:
+        # the scale may move when amax is not a grid point, so fix the max element at 6s
+        keep = (codes & 7).max(axis=1) == 7
+        codes2, sc2 = q(to_bf16_bits(d.astype(np.float32)))
+        assert np.array_equal(codes2[keep & (sc2 == sc)], codes[keep & (sc2 == sc)])
+
+
+def _nearest_code_exact(v: Fraction, s: Fraction) -> int:
+    mag = abs(v)
+    best, bestd = 0, None
+    for i, m in enumerate(E2M1):
+        d = abs(Fraction(m) * s - mag)
+        if bestd is None or d < bestd or (d == bestd and i % 2 == 0 and best % 2 == 1):
+            best, bestd = i, d
+    return best
+
+
+def test_exhaustive_bf16_element_codes_exact_rational():
+    # every finite bf16 value of magnitude <= 6 as a non-max element of a scale-1 block
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = bf16_bits_to_f32(allb)
+    keep = np.isfinite(f) & (np.abs(f) <= 6.0)
+    vals = allb[keep]
+    blocks = np.zeros((vals.size, 16), np.uint16)
+    blocks[:, 0] = to_bf16_bits(np.float32([6.0]))[0]
+    blocks[:, 1] = vals
+    codes, sc = oracle.quant_nv16(blocks)
+    assert np.all(sc == 0x38)
+    fv = bf16_bits_to_f32(vals)
+    sign = np.signbit(fv).astype(np.uint8) * 8
+    # compare against exact rational nearest-with-even-ties on a thinned grid
+    # (every value near a midpoint plus a stride sample of the rest)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    near = np.min(np.abs(np.abs(fv)[:, None] - mids[None, :]), axis=1) < 0.02
+    sel = np.nonzero(near | (np.arange(vals.size) % 7 == 0))[0]
+    for i in sel:
+        want = _nearest_code_exact(Fraction(float(fv[i])), Fraction(1)) | sign[i]
+        assert codes[i, 1] == want, (float(fv[i]), codes[i, 1], want)
+
+
+# ------------------------------------------------------ index score -------
+def _small_cache(rng, n, outlier=False):
+    lat = to_bf16_bits(rng.standard_normal((n, 512)).astype(np.float32))
+    key = rng.standard_normal((n, 128)).astype(np.float32)
+    if outlier:
+        key[:, 5] *= 8
+    key = to_bf16_bits(key)
+    c = oracle.Cache(((n + 63) // 64) * 64)
+    oracle.fp4_cache_write(c, lat, key, np.arange(n))
+    return c
+
+
+def _deq_idx_rows(c, slots):
+    codes = np.stack([c.idx_codes[slots] & 15, c.idx_codes[slots] >> 4], axis=-1).reshape(len(slots), 128)
+    sc = 2.0 ** (np.repeat(c.idx_scales[slots].astype(np.float64), 32, axis=1) - 127)
+    return _deq(codes, sc)
+
+
+def test_index_score_single_head_is_relu_of_dot():
+    rng = np.random.default_rng(4)
+    n = 300
+    c = _small_cache(rng, n)
+    q = to_bf16_bits(rng.standard_normal((1, 1, 128)).astype(np.float32))
+    bt = np.arange(5, dtype=np.int32)[None, :]
+    s, bad, inexact = oracle.index_score(c, q, np.ones((1, 1), np.float32), np.array([n], np.int32), bt)
+    assert bad == 0 and inexact == 0
+    qc, qs = oracle.quant_mx32(q.reshape(4, 32))
+    qd = _deq(qc.reshape(128), np.repeat(2.0 ** (qs.astype(np.float64) - 127), 32))
+    kd = _deq_idx_rows(c, np.arange(n))
+    ref = np.maximum(np.float32(kd @ qd), np.float32(0))
+    assert np.array_equal(s[0], ref.astype(np.float32))
+    bound = 4 * 36 * 32 * 2.0 ** (int(qs.max()) + int(c.idx_scales.max()) - 254)
+    assert np.all(np.abs(kd @ qd) <= bound)
+
+
+def _round_f32(x: Fraction) -> np.float32:
+    """Correctly rounded (nearest-even) float32 of an exact rational (normal range)."""
+    if x == 0:
+        return np.float32(0.0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    # a in [2^e, 2^(e+1)): 24 significant bits -> quantum 2^(e-23)
+    q = Fraction(2) ** (e - 23)
+    m = a / q
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return np.float32(sign * float(fl * q))
+
+
+def test_index_score_fma_chain_exact_rational():
+    rng = np.random.default_rng(5)
+    n, Hi = 40, 16
+    c = _small_cache(rng, n, outlier=True)
+    q = to_bf16_bits(rng.standard_normal((1, Hi, 128)).astype(np.float32))
+    w = rng.random((1, Hi), dtype=np.float32)
+    bt = np.zeros((1, 1), np.int32)
+    s, bad, inexact = oracle.index_score(c, q, w, np.array([n], np.int32), bt)
+    assert bad == 0 and inexact == 0
+    qc, qs = oracle.quant_mx32(q.reshape(Hi * 4, 32))
+    qc = qc.reshape(Hi, 128)
+    qs = qs.reshape(Hi, 4)
+    for j in range(n):
+        kc = np.stack([c.idx_codes[j] & 15, c.idx_codes[j] >> 4], axis=-1).reshape(128)
+        acc = np.float32(0.0)
+        for h in range(Hi):
+            D = Fraction(0)
+            for ch in range(128):
+                b = ch // 32
+                qv = Fraction(float(_deq(qc[h, ch], 1.0))) * Fraction(2) ** (int(qs[h, b]) - 127)
+                kv = Fraction(float(_deq(kc[ch], 1.0))) * Fraction(2) ** (int(c.idx_scales[j, b]) - 127)
+                D += qv * kv
+            d = _round_f32(D)
+            r = d if d > 0 else np.float32(0.0)
+            acc = _round_f32(Fraction(float(w[0, h])) * Fraction(float(r)) + Fraction(float(acc)))
+        assert s[0, j] == acc, (j, s[0, j], acc)
+
+
+def test_index_score_paging_and_visibility():
+    rng = np.random.default_rng(6)
+    n = 200
+    c = _small_cache(rng, 256)
+    q = to_bf16_bits(rng.standard_normal((2, 16, 128)).astype(np.float32))
+    w = rng.random((2, 16), dtype=np.float32)
+    # sequence 1 reads the same physical pages in reverse order
+    bt = np.array([[0, 1, 2, 3], [3, 2, 1, 0]], np.int32)
+    s, bad, _ = oracle.index_score(c, q[[0, 0]], w[[0, 0]], np.array([n, 256], np.int32), bt,
+                                   seq_of_query=np.array([0, 1], np.int32), ld=256)
+    assert bad == 0
+    assert np.all(np.isnan(s[0, n:]))
+    for j in range(256):
+        jp = (3 - j // 64) * 64 + j % 64
+        if jp < n:
+            assert s[1, j] == s[0, jp]
+
+
+# ------------------------------------------------------------ top-K -------
+def test_topk_matches_full_lexsort_with_ties():
+    rng = np.random.default_rng(7)
+    nq, L = 6, 500
+    s = rng.integers(0, 40, (nq, L)).astype(np.float32)  # heavy ties
+    s[2] = rng.standard_normal(L).astype(np.float32)
+    s[3, :] = 1.0  # all tied
+    s[4, 10] = -0.0
+    s[4, 11] = 0.0
+    nv = np.array([500, 500, 37, 500, 12, 0], np.int32)
+    k = 50
+    out = oracle.topk_select(s, nv, k)
+    for q in range(nq):
+        n = nv[q]
+        order = np.lexsort((np.arange(n), -s[q, :n].astype(np.float64)))
+        want = np.sort(order[:min(k, n)])
+        got = out[q]
+        assert np.array_equal(got[:len(want)], want)
+        assert np.all(got[len(want):] == -1)
+    assert list(out[3, :k]) == list(range(k))
+
+
+# -------------------------------------------------------- attention -------
+def _dense_reference(q_bits, rows, scale):
+    qf = torch.from_numpy(bf16_bits_to_f32(q_bits).astype(np.float64))
+    X = torch.from_numpy(rows)
+    z = scale * (qf @ X.T)
+    p = torch.softmax(z, dim=-1)
+    return (p @ X).numpy(), torch.logsumexp(z, dim=-1).numpy()
+
+
+def _deq_main_rows(c, slots):
+    codes = np.stack([c.main_codes[slots] & 15, c.main_codes[slots] >> 4], axis=-1).reshape(len(slots), 512)
+    sc = torch.from_numpy(np.ascontiguousarray(c.main_scales[slots])).view(torch.float8_e4m3fn).double().numpy()
+    return _deq(codes, np.repeat(sc, 16, axis=1))
+
+
+def test_attention_with_k_ge_n_is_dense_attention():
+    rng = np.random.default_rng(8)
+    n, H, W = 100, 16, 20
+    c = _small_cache(rng, n)
+    q = to_bf16_bits(rng.standard_normal((1, H, 512)).astype(np.float32))
+    swa = to_bf16_bits(rng.standard_normal((1, W, 512)).astype(np.float32))
+    idx = np.full((1, 128), -1, np.int32)
+    idx[0, :n] = np.arange(n)
+    bt = np.array([[0, 1]], np.int32)
+    scale = 1 / math.sqrt(512)
+    out, lse = oracle.sparse_attn_decode(c, q, idx, bt, swa, np.array([W], np.int32), scale)
+    rows = np.concatenate([_deq_main_rows(c, np.arange(n)), bf16_bits_to_f32(swa[0]).astype(np.float64)])
+    ro, rl = _dense_reference(q[0], rows, scale)
+    assert np.max(np.abs(out[0] - ro)) < 1e-6
+    assert np.max(np.abs(lse[0] - rl)) < 1e-5
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(9)
+    c = _small_cache(rng, 64)
+    H = 16
+    q = to_bf16_bits(rng.standard_normal((3, H, 512)).astype(np.float32))
+    swa = np.zeros((3, 4, 512), np.uint16)
+    bt = np.zeros((3, 1), np.int32)
+    idx = np.full((3, 8), -1, np.int32)
+    idx[0, 0] = 5  # one row
+    idx[1, :4] = [7, 7, 7, 7]  # the same row four times
+    swa_len = np.array([0, 0, 0], np.int32)  # row 2: nothing at all
+    out, lse = oracle.sparse_attn_decode(c, q, idx, bt, swa, swa_len, 0.05)
+    x5 = _deq_main_rows(c, np.array([5]))[0]
+    x7 = _deq_main_rows(c, np.array([7]))[0]
+    qf = bf16_bits_to_f32(q).astype(np.float64)
+    assert np.allclose(out[0], x5[None, :], atol=1e-6)
+    assert np.allclose(lse[0], 0.05 * qf[0] @ x5, atol=1e-5)
+    assert np.allclose(out[1], x7[None, :], atol=1e-6)
+    assert np.allclose(lse[1], 0.05 * qf[1] @ x7 + math.log(4), atol=1e-5)
+    assert np.all(out[2] == 0) and np.all(np.isneginf(lse[2]))
+
+
+def test_attention_lse_merge_identity():
+    rng = np.random.default_rng(10)
+    c = _small_cache(rng, 128)
+    H = 16
+    q = to_bf16_bits(rng.standard_normal((1, H, 512)).astype(np.float32))
+    swa = to_bf16_bits(rng.standard_normal((1, 8, 512)).astype(np.float32))
+    bt = np.array([[0, 1]], np.int32)
+    A = np.array([[3, 9, 40, 77, 100]], np.int32)
+    Bi = np.array([[1, 2, 64, 127, -1]], np.int32)
+    AB = np.concatenate([A, Bi], axis=1)
+    oA, lA = oracle.sparse_attn_decode(c, q, A, bt, swa, np.array([0], np.int32), 0.07)
+    oB, lB = oracle.sparse_attn_decode(c, q, Bi, bt, swa, np.array([8], np.int32), 0.07)
+    oAB, lAB = oracle.sparse_attn_decode(c, q, AB, bt, swa, np.array([8], np.int32), 0.07)
+    wA = np.exp(lA.astype(np.float64) - lAB)[..., None]
+    wB = np.exp(lB.astype(np.float64) - lAB)[..., None]
+    assert np.allclose(wA + wB, 1.0, atol=1e-6)
+    assert np.max(np.abs(wA * oA + wB * oB - oAB)) < 1e-5
+
+
+def test_prefill_query_equals_decode_with_its_window():
+    rng = np.random.default_rng(11)
+    c = _small_cache(rng, 256)
+    H, T, W, k = 16, 6, 5, 16
+    q = to_bf16_bits(rng.standard_normal((T, H, 512)).astype(np.float32))
+    swa = to_bf16_bits(rng.standard_normal((W - 1 + T, 512)).astype(np.float32))
+    idx = np.sort(rng.choice(200, (T, k)), axis=1).astype(np.int32)
+    idx[:, -3:] = -1
+    bt = np.arange(4, dtype=np.int32)
+    first_valid = 2
+    out, lse = oracle.sparse_attn_prefill_chunk(c, q, idx, bt, swa, first_valid, W, 0.04)
+    for i in range(T):
+        lo = max(i, first_valid)
+        win = np.zeros((1, W, 512), np.uint16)
+        win[0, :i + W - lo] = swa[lo:i + W]
+        o, l = oracle.sparse_attn_decode(c, q[i:i + 1], idx[i:i + 1], bt[None, :], win,
+                                         np.array([i + W - lo], np.int32), 0.04)
+        assert np.array_equal(o[0], out[i]) and np.array_equal(l[0], lse[i])

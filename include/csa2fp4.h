@@ -1,0 +1,178 @@
+/*
+ * csa2fp4.h -- C ABI of libcsa2fp4.so: the decode / prefill-chunk step of CSA2
+ * sparse attention over a sequence-compressed global KV cache stored in FP4,
+ * for AMD MI355X (gfx950).
+ *
+ * What the step computes comes from the pages describing DeepSeek-V4.1-Flash:
+ *   - "DeepSeek-V4.1-Flash, expliqué pas à pas", CSA2 section: a shared global cache
+ *     of compressed entries (m tokens each, disjoint groups), a light indexer that
+ *     scores every entry from an indexer query and one indexer key per entry and
+ *     keeps the best k, and a main attention that reads the selected entries plus
+ *     the layer's own sliding-window KV; the Full / Reindex / Reuse layer modes.
+ *   - same page, FP4 KV cache section: main entries are E2M1 values with one E4M3
+ *     scale per 16 channels (288 B per 512-channel entry), quantised after RoPE and
+ *     dequantised before attention; indexer keys and queries are OCP MXFP4 (E2M1
+ *     values with one E8M0 scale per 32 channels, 68 B per 128-channel key).
+ *   - same page, attention forms: the window covers the last 128 tokens.
+ *   - "Résumé exécutif", CSA2 mode table: Full computes cache, indexer keys and
+ *     indices; Reindex reuses cache and keys and recomputes indices; Reuse reuses all.
+ *
+ * Conventions for every entry point:
+ *   - Array arguments and every pointer inside csa2_fp4_cache are DEVICE pointers,
+ *     allocated and owned by the caller.  The cache descriptor struct itself is a
+ *     host struct.  The library allocates no memory, keeps no global state and
+ *     never synchronises; work is enqueued on `stream` in order.
+ *   - Arguments are validated on the host before anything is enqueued, so a bad
+ *     argument returns a negative csa2_status and enqueues nothing.  A failed
+ *     launch returns CSA2_ERR_LAUNCH (work enqueued before it may have run).
+ *   - Device-side preconditions (not checked): slots unique and in range; every
+ *     block-table entry read is a valid page; n_visible <= ld and covered by the
+ *     block table; indices are < n_visible or -1; inputs are finite.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ */
+#ifndef CSA2FP4_H
+#define CSA2FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA2_OK = 0,
+  CSA2_ERR_NULL = -1,        /* a required pointer is NULL                         */
+  CSA2_ERR_SHAPE = -2,       /* a size or count is out of range                    */
+  CSA2_ERR_UNSUPPORTED = -3, /* a supported-but-not-built configuration            */
+  CSA2_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than the *_workspace_size */
+  CSA2_ERR_LAUNCH = -5       /* a kernel launch failed                              */
+} csa2_status;
+
+#define CSA2_LATENT_DIM 512 /* channels of a main-cache entry and of a window row */
+#define CSA2_INDEX_DIM 128  /* channels of an indexer key / query head             */
+#define CSA2_PAGE_SIZE 64   /* cache slots per page                                */
+#define CSA2_MAX_K 4096     /* largest top-k                                       */
+#define CSA2_MAX_WINDOW 128 /* largest sliding window                              */
+
+/* One global FP4 cache (the cache of one Full layer).  Per slot s:
+ *   main_codes [s*256 .. s*256+255]: 512 E2M1 codes, byte i holds channel 2i in
+ *                                    bits 0-3 and channel 2i+1 in bits 4-7;
+ *                                    code = 8*sign + index into {0,.5,1,1.5,2,3,4,6}
+ *   main_scales[s*32 .. s*32+31]   : OCP E4M3FN scale of channels 16g .. 16g+15
+ *   idx_codes  [s*64 .. s*64+63]   : 128 E2M1 codes of the indexer key, same order
+ *   idx_scales [s*4 .. s*4+3]      : OCP E8M0 scale of channels 32b .. 32b+31
+ * That is 288 + 68 = 356 bytes per slot.  num_slots is a multiple of page_size,
+ * and a sequence's logical entry j lives in slot
+ *   block_table[row][j / page_size] * page_size + j % page_size.            */
+typedef struct {
+  uint8_t* main_codes;
+  uint8_t* main_scales;
+  uint8_t* idx_codes;
+  uint8_t* idx_scales;
+  int64_t num_slots;
+  int32_t page_size; /* must be CSA2_PAGE_SIZE */
+} csa2_fp4_cache;
+
+/* Human-readable name of a status code (static string). */
+const char* csa2_status_string(int status);
+
+/* fp4_cache_write -- quantise n compressed entries into the cache.
+ * Source: "DeepSeek-V4.1-Flash, expliqué pas à pas", FP4 KV cache section (E2M1 with
+ * one E4M3 scale per 16 channels for the main entry; OCP MXFP4 for the indexer key;
+ * quantisation after RoPE, one format for all channels).
+ *   latent  bf16 [n][512] : post-RoPE compressed main entries
+ *   idx_key bf16 [n][128] : indexer keys of the same entries
+ *   slot    int64 [n]     : destination slot of each row, unique, < num_slots
+ * Rounding: per 16-channel block the scale is the E4M3FN value nearest to amax/6
+ * (ties to even, saturating at 448); per 32-channel indexer block the scale is
+ * 2^(floor(log2 amax) - 2) (2^-127 for an all-zero block); each channel takes the
+ * nearest of the 8 E2M1 magnitudes times the scale (ties to the even code), keeps
+ * its sign bit, and a zero E4M3 scale gives signed zeros.  Bit-exact and
+ * deterministic.  n == 0 is a no-op. */
+int fp4_cache_write(const csa2_fp4_cache* cache, const uint16_t* latent, const uint16_t* idx_key,
+                    const int64_t* slot, int64_t n, hipStream_t stream);
+
+/* index_score -- lightning-indexer scores of visible entries.
+ * Source: "DeepSeek-V4.1-Flash, expliqué pas à pas", CSA2 section (the indexer scores
+ * each entry from the query's indexer query and the entry's indexer key) and FP4 KV
+ * cache section (indexer queries and keys are MXFP4).
+ *   q_idx bf16 [nq][Hi][128]  : indexer queries, quantised to MXFP4 inside the call
+ *   w     f32  [nq][Hi]       : per-head weights
+ *   Hi                        : indexer heads, a multiple of 16, 16 <= Hi <= 128
+ *   seq_of_query int32 [nq]   : block-table row of each query (NULL: row q)
+ *   n_visible    int32 [nq]   : entries 0 .. n_visible[q]-1 are scored, <= ld
+ *   block_table  int32 [rows][max_pages]
+ *   scores f32 [nq][ld]       : only positions < n_visible[q] are written
+ * score[q][j] = sum over h of w[q][h] * max(d_h, 0), where d_h is the exact dot
+ * product of the MXFP4-quantised query head and key rounded once to fp32, and the
+ * sum is an fp32 fused-multiply-add chain over h = 0 .. Hi-1 starting from +0.
+ * Bit-exact and deterministic. */
+int index_score(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
+                const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* block_table, int32_t max_pages,
+                int32_t nq, float* scores, int64_t ld, hipStream_t stream);
+
+/* topk_select -- the k best entries per query.
+ * Source: "DeepSeek-V4.1-Flash, expliqué pas à pas", attention forms and CSA2 section
+ * (the indexer keeps only the best-scoring entries).
+ *   scores f32 [nq][ld]  : positions < n_visible[q] are read
+ *   k                    : 1 <= k <= 4096
+ *   topk_idx int32 [nq][k]: the min(k, n_visible[q]) entries with the largest score
+ *                          (numeric compare; ties go to the lower index), in
+ *                          ascending index order, then -1 padding.
+ *   ws, ws_bytes          : device workspace of at least
+ *                          topk_select_workspace_size(nq, ld, k) bytes.  It must be
+ *                          zero-filled before its first use; every call leaves it
+ *                          zero-filled again (in stream order).  Calls sharing one
+ *                          workspace must be stream-ordered.
+ * Bit-exact and deterministic. */
+size_t topk_select_workspace_size(int32_t nq, int64_t ld, int32_t k);
+int topk_select(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq, int32_t k,
+                int32_t* topk_idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* sparse_attn_decode -- one softmax over the selected cache entries and the window.
+ * Source: "DeepSeek-V4.1-Flash, expliqué pas à pas", CSA2 section (the main query
+ * reads the selected entries and the layer's own sliding-window KV; FP4 is only a
+ * storage format, dequantised before attention) and intro (softmax-weighted mean);
+ * "La lignée DeepSeek" (one latent vector shared by all heads).
+ *   q bf16 [B][H][512]        : main queries, H a multiple of 16, 16 <= H <= 128
+ *   topk_idx int32 [B][k]     : selected entries of sequence b (-1 = none)
+ *   block_table int32 [B][max_pages] : row b belongs to sequence b
+ *   swa bf16 [B][window][512] : window rows; rows 0 .. swa_len[b]-1 are valid
+ *   softmax_scale             : logit multiplier (1/sqrt(512) in the workloads)
+ *   out f32 [B][H][512], lse f32 [B][H]
+ * Each dequantised entry and each window row is both key and value for every head:
+ * z = softmax_scale * q_h . x, out_h = sum softmax(z)_x x, lse_h = log sum exp z.
+ * With no rows at all: out = 0, lse = -inf.  Within 2e-3 absolute of an fp64
+ * evaluation on the workloads' data.
+ *   ws, ws_bytes: at least sparse_attn_decode_workspace_size(B, H, k, window). */
+size_t sparse_attn_decode_workspace_size(int32_t B, int32_t H, int32_t k, int32_t window);
+int sparse_attn_decode(const csa2_fp4_cache* cache, const uint16_t* q, int32_t H, const int32_t* topk_idx, int32_t k,
+                       const int32_t* block_table, int32_t max_pages, const uint16_t* swa, const int32_t* swa_len,
+                       int32_t window, float softmax_scale, int32_t B, float* out, float* lse, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/* sparse_attn_prefill_chunk -- decode attention for T consecutive query tokens.
+ * Source: as sparse_attn_decode; each query token has its own top-k selection and
+ * its own causal window of the last `window` tokens.
+ *   q bf16 [T][H][512], topk_idx int32 [T][k]  (row i: query token chunk_start + i)
+ *   block_table int32 [max_pages]               : the one sequence's page table
+ *   swa bf16 [window-1+T][512]                  : row r holds token
+ *                                                 chunk_start - window + 1 + r
+ *   swa_first_valid                             : rows below it do not exist
+ * Query i attends its selected entries plus window rows max(i, swa_first_valid) ..
+ * i + window - 1 under one softmax.  out f32 [T][H][512], lse f32 [T][H].
+ *   ws, ws_bytes: at least sparse_attn_prefill_chunk_workspace_size(T, H, k, window). */
+size_t sparse_attn_prefill_chunk_workspace_size(int32_t T, int32_t H, int32_t k, int32_t window);
+int sparse_attn_prefill_chunk(const csa2_fp4_cache* cache, const uint16_t* q, int32_t H, const int32_t* topk_idx,
+                              int32_t k, const int32_t* block_table, int32_t max_pages, int64_t chunk_start, int32_t T,
+                              const uint16_t* swa, int32_t swa_first_valid, int32_t window, float softmax_scale,
+                              float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2FP4_H */

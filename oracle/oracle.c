@@ -84,6 +84,9 @@ double oracle_e8m0_value(uint8_t u) {
  * byte, i.e. even mantissa), searched over every finite non-negative byte.  Working
  * with |6v - a| keeps the comparison exact in double (v has 4 significant bits). */
 static uint8_t e4m3_nearest_sixth(double a) {
+  /* saturation: beyond the largest finite value the nearest finite value is 448
+   * (also keeps |6v - a| below from being compared at magnitudes where it rounds) */
+  if (a >= 6.0 * 448.0) return 0x7E;
   uint8_t best = 0;
   double bestd = INFINITY;
   for (int b = 0; b <= 0x7E; ++b) {
@@ -98,9 +101,13 @@ static uint8_t e4m3_nearest_sixth(double a) {
 
 /* Nearest of the 8 E2M1 magnitudes times `scale` to |x| (ties to the even index),
  * with the sign bit of x copied into bit 3.  |x|, M_i and scale are all exact in
- * double and M_i*scale - |x| is computed exactly (few significant bits). */
+ * double; for |x| < 6*scale, M_i*scale - |x| is exact wherever two candidates are
+ * close enough to tie (|x| then lies next to a midpoint of similar magnitude). */
 static uint8_t e2m1_nearest(double x, double scale) {
   double mag = fabs(x);
+  /* at or beyond 6*scale the nearest magnitude is 6 (clipping); the differences
+   * below are only compared where they are exact, i.e. |x| within the grid */
+  if (mag >= 6.0 * scale) return (uint8_t)((signbit(x) ? 8 : 0) | 7);
   int best = 0;
   double bestd = INFINITY;
   for (int i = 0; i < 8; ++i) {

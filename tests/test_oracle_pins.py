@@ -141,6 +141,9 @@ def test_nv16_saturation_matches_page_range():
     assert sc[0] == 0x7E and oracle.e4m3_value(0x7E) == page("e4m3_max") and codes[0][0] == 7
     codes, sc = oracle.quant_nv16(_blocks([-5000.0] + [1.0] * 15, 16))
     assert sc[0] == 0x7E and codes[0][0] == 0xF  # decodes to -2688
+    # far beyond the range: everything above 5 * 448 clips to +-2688, smaller values keep their code
+    codes, sc = oracle.quant_nv16(_blocks([1e30, -3e38, 2500.0, 2200.0, 1e20, 1.0] + [0.0] * 10, 16))
+    assert sc[0] == 0x7E and list(codes[0][:6]) == [7, 0xF, 7, 6, 7, 0]
 
 
 def test_nv16_zero_and_tiny_blocks():

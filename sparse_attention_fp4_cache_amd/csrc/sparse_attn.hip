@@ -13,10 +13,13 @@
 // which it walks in tiles of 32 rows with an online softmax:
 //   gather   : 256 threads dequantise the tile into LDS twice, row-major X[32][512]
 //              and transposed XT[512][32] (bf16; E2M1 x E4M3 has at most 6
-//              significant bits in [2^-10, 2688], so the bf16 value is exact).
+//              significant bits in [2^-10, 2688], so the bf16 value is exact).  The
+//              bytes of the next tile are loaded into registers while the current
+//              tile is computed.
 //   logits   : S^T = X Q^T with V_MFMA_F32_16X16X32_BF16; each wavefront covers a
 //              quarter of the 512 channels and the four partial tiles are summed in
-//              LDS in a fixed order.
+//              LDS in a fixed order.  The rows are permuted across the two 16-row
+//              M-tiles so that lane group g holds rows 8g .. 8g+7.
 //   softmax  : per head, running max / sum in fp32 (exp2 of log2e-scaled logits).
 //   values   : O^T += XT P^T; each wavefront owns 128 output channels.  The P
 //              operand comes straight from the logits accumulator registers (the
@@ -62,11 +65,13 @@ struct AttnArgs {
   float* part_ml;            // [nq][nsplit][H][2]
 };
 
+constexpr int kSeg = 512;  // rows whose sources are resolved into LDS at a time
+
 struct __align__(16) AttnSmem {
   uint16_t x[kRT * kXStride];    // X[row][ch]
   uint16_t xt[512 * kXTStride];  // XT[ch][row]
   float red[4][2][4][64];        // partial logits [wave][mtile][r][lane]
-  int rowvalid[kRT];
+  int src[kSeg];                 // row source: slot >= 0, window row -2-r, or -1 (none)
 };
 
 CSA2_DEV uint32_t pack_bf16_hi(float lo, float hi) {  // exact values only (low 16 bits zero)
@@ -78,67 +83,78 @@ CSA2_DEV uint32_t bf16_rne_bits(float f) {  // fp32 -> bf16 bits, round to neare
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Dequantise/copy this thread's 4 rows x 16 channels of the tile into X and XT.
-// Thread t: rows 4*(t/32) .. +3, channels 16*(t%32) .. +15.
-CSA2_DEV void gather_tile(const AttnArgs& a, AttnSmem& sm, int qrow, int bt_row, int row0, int total_rows) {
+// Raw bytes of this thread's 8 rows x 8 channels of one tile, as loaded from HBM.
+// Thread t: rows 8*(t%4) .. +7, channels 8*(t/4) .. +7.
+struct TileRegs {
+  uint32_t w[8][4];  // main row: w[rr][0] = 4 code bytes; window row: 8 bf16
+  uint32_t sc[8];    // main row: E4M3 scale byte
+  int kind[8];       // 0 none, 1 main, 2 window
+};
+
+CSA2_DEV void issue_tile(const AttnArgs& a, const AttnSmem& sm, int tile_row0, int r_local_end, TileRegs& t) {
   const int tid = threadIdx.x;
-  const int rg = tid >> 5, cb = tid & 31;
-  uint32_t w[4][8];  // [row][dword]: 16 bf16 per row
+  const int rg = tid & 3, cb = tid >> 2;
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int r = row0 + 4 * rg + rr;  // candidate row index within this query
-    bool valid = false;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w[rr][i] = 0u;
-    if (r < total_rows) {
-      if (r < a.k) {
-        const int j = a.topk_idx[(int64_t)qrow * a.k + r];
-        if (j >= 0) {
-          valid = true;
-          const int64_t slot =
-              (int64_t)a.block_table[(int64_t)bt_row * a.max_pages + (j >> 6)] * kPage + (j & 63);
-          const uint2 c = *reinterpret_cast<const uint2*>(a.main_codes + slot * kMainRowBytes + 8 * cb);
-          const float s = e4m3_value(a.main_scales[slot * kMainScaleBytes + cb]);
-          const uint32_t cw[2] = {c.x, c.y};
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {  // byte i of the 8 code bytes -> channels 2i, 2i+1
-            const uint32_t byte = (cw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-            const v2f d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, 1.0f, 0);
-            w[rr][i] = pack_bf16_hi(d[0] * s, d[1] * s);
-          }
-        }
-      } else {
-        const int wr = r - a.k;
-        int64_t src_row = -1;
-        if (a.prefill) {
-          if (qrow + wr >= a.swa_first_valid && wr < a.window) src_row = (int64_t)qrow + wr;
-        } else {
-          if (wr < a.swa_len[qrow]) src_row = (int64_t)qrow * a.window + wr;
-        }
-        if (src_row >= 0) {
-          valid = true;
-          const uint4* p = reinterpret_cast<const uint4*>(a.swa + src_row * kLatentDim + 16 * cb);
-          const uint4 v0 = p[0], v1 = p[1];
-          w[rr][0] = v0.x; w[rr][1] = v0.y; w[rr][2] = v0.z; w[rr][3] = v0.w;
-          w[rr][4] = v1.x; w[rr][5] = v1.y; w[rr][6] = v1.z; w[rr][7] = v1.w;
-        }
-      }
+  for (int rr = 0; rr < 8; ++rr) {
+    const int rl = tile_row0 + 8 * rg + rr;  // row index local to this segment
+    const int src = (rl < r_local_end) ? sm.src[rl] : -1;
+    t.kind[rr] = 0;
+    if (src >= 0) {
+      t.kind[rr] = 1;
+      t.w[rr][0] = *reinterpret_cast<const uint32_t*>(a.main_codes + (int64_t)src * kMainRowBytes + 4 * cb);
+      t.sc[rr] = a.main_scales[(int64_t)src * kMainScaleBytes + (cb >> 1)];
+    } else if (src <= -2) {
+      t.kind[rr] = 2;
+      const uint4 v = *reinterpret_cast<const uint4*>(a.swa + (int64_t)(-2 - src) * kLatentDim + 8 * cb);
+      t.w[rr][0] = v.x;
+      t.w[rr][1] = v.y;
+      t.w[rr][2] = v.z;
+      t.w[rr][3] = v.w;
     }
-    if (cb == 0) sm.rowvalid[4 * rg + rr] = valid ? 1 : 0;
-    uint4* xp = reinterpret_cast<uint4*>(sm.x + (4 * rg + rr) * kXStride + 16 * cb);
-    xp[0] = make_uint4(w[rr][0], w[rr][1], w[rr][2], w[rr][3]);
-    xp[1] = make_uint4(w[rr][4], w[rr][5], w[rr][6], w[rr][7]);
   }
-  // transposed copy: channel c of rows 4rg..4rg+3 as 4 consecutive bf16
+}
+
+// Dequantise the loaded bytes into X (row-major) and XT (transposed) in LDS.
+// XT rows are written as 16-byte runs of 8 consecutive tile rows; with a channel
+// stride of 18 dwords the 64 lanes of a wavefront spread over all LDS banks.
+CSA2_DEV void store_tile(AttnSmem& sm, const TileRegs& t) {
+  const int tid = threadIdx.x;
+  const int rg = tid & 3, cb = tid >> 2;
+  uint32_t w[8][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t lo01 = (w[0][i] & 0xFFFFu) | (w[1][i] << 16);
-    const uint32_t lo23 = (w[2][i] & 0xFFFFu) | (w[3][i] << 16);
-    const uint32_t hi01 = (w[0][i] >> 16) | (w[1][i] & 0xFFFF0000u);
-    const uint32_t hi23 = (w[2][i] >> 16) | (w[3][i] & 0xFFFF0000u);
-    const int c = 16 * cb + 2 * i;
-    *reinterpret_cast<uint2*>(sm.xt + c * kXTStride + 4 * rg) = make_uint2(lo01, lo23);
-    *reinterpret_cast<uint2*>(sm.xt + (c + 1) * kXTStride + 4 * rg) = make_uint2(hi01, hi23);
+  for (int rr = 0; rr < 8; ++rr) {
+    if (t.kind[rr] == 1) {
+      const float s = e4m3_value(t.sc[rr]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {  // code byte i -> channels 2i, 2i+1
+        const uint32_t byte = (t.w[rr][0] >> (8 * i)) & 0xFFu;
+        const v2f d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, 1.0f, 0);
+        w[rr][i] = pack_bf16_hi(d[0] * s, d[1] * s);
+      }
+    } else if (t.kind[rr] == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[rr][i] = t.w[rr][i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[rr][i] = 0u;
+    }
+    *reinterpret_cast<uint4*>(sm.x + (8 * rg + rr) * kXStride + 8 * cb) =
+        make_uint4(w[rr][0], w[rr][1], w[rr][2], w[rr][3]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // channels 8cb + 2i (low halves) and 8cb + 2i + 1 (high halves)
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      lo[p] = (w[2 * p][i] & 0xFFFFu) | (w[2 * p + 1][i] << 16);
+      hi[p] = (w[2 * p][i] >> 16) | (w[2 * p + 1][i] & 0xFFFF0000u);
+    }
+    uint2* d0 = reinterpret_cast<uint2*>(sm.xt + (8 * cb + 2 * i) * kXTStride + 8 * rg);
+    uint2* d1 = reinterpret_cast<uint2*>(sm.xt + (8 * cb + 2 * i + 1) * kXTStride + 8 * rg);
+    d0[0] = make_uint2(lo[0], lo[1]);
+    d0[1] = make_uint2(lo[2], lo[3]);
+    d1[0] = make_uint2(hi[0], hi[1]);
+    d1[1] = make_uint2(hi[2], hi[3]);
   }
 }
 
@@ -159,6 +175,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
   const int total_rows = a.k + a.window;
   const int r_begin = split * a.rows_per_split;
   const int r_end = min(r_begin + a.rows_per_split, total_rows);
+  const int nrows = r_end - r_begin;
   const int head = hg * 16 + n16;  // head owned by this lane in every accumulator
 
   // Q^T operand for this wavefront's 128 channels: lane holds head n16, channels
@@ -173,9 +190,33 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
   for (int mt = 0; mt < 8; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  for (int row0 = r_begin; row0 < r_end; row0 += kRT) {
+  for (int seg0 = 0; seg0 < nrows; seg0 += kSeg) {
+  const int seg_n = min(kSeg, nrows - seg0);
+  __syncthreads();  // the previous segment's sources are no longer read
+  // where every row of this segment comes from (one round of index loads)
+  for (int rl = tid; rl < seg_n; rl += 256) {
+    const int r = r_begin + seg0 + rl;
+    int src = -1;
+    if (r < a.k) {
+      const int j = a.topk_idx[(int64_t)qrow * a.k + r];
+      if (j >= 0) src = a.block_table[(int64_t)bt_row * a.max_pages + (j >> 6)] * kPage + (j & 63);
+    } else {
+      const int wr = r - a.k;
+      if (a.prefill) {
+        if (qrow + wr >= a.swa_first_valid) src = -2 - (qrow + wr);
+      } else if (wr < a.swa_len[qrow]) {
+        src = -2 - (qrow * a.window + wr);
+      }
+    }
+    sm.src[rl] = src;
+  }
+  __syncthreads();
+  TileRegs cur;
+  issue_tile(a, sm, 0, seg_n, cur);
+  for (int row0 = 0; row0 < seg_n; row0 += kRT) {
     __syncthreads();  // previous tile fully consumed
-    gather_tile(a, sm, qrow, bt_row, row0, r_end);
+    store_tile(sm, cur);
+    if (row0 + kRT < seg_n) issue_tile(a, sm, row0 + kRT, seg_n, cur);  // next tile in flight
     __syncthreads();
     // ---- partial logits over this wavefront's 128 channels, two 16-row M-tiles
     v4f s[2];
@@ -184,7 +225,10 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
       s[t] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const uint4 xa = *reinterpret_cast<const uint4*>(sm.x + (16 * t + n16) * kXStride + 128 * wid + 32 * ks + 8 * g);
+        // M row n16 of tile t is tile row 8*(n16/4) + 4t + n16%4, so that lane group g
+        // ends up holding the logits of rows 8g .. 8g+7
+        const int xrow = 8 * (n16 >> 2) + 4 * t + (n16 & 3);
+        const uint4 xa = *reinterpret_cast<const uint4*>(sm.x + xrow * kXStride + 128 * wid + 32 * ks + 8 * g);
         s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(qop[ks]), s[t], 0, 0, 0);
       }
 #pragma unroll
@@ -199,8 +243,9 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float v = ((sm.red[0][t][r][lane] + sm.red[1][t][r][lane]) + sm.red[2][t][r][lane]) + sm.red[3][t][r][lane];
-        const int row = 16 * t + 4 * g + r;
-        z[t][r] = sm.rowvalid[row] ? v * a.scale_log2 : -INFINITY;
+        const int rl = row0 + 8 * g + 4 * t + r;
+        const bool valid = rl < seg_n && sm.src[rl] != -1;
+        z[t][r] = valid ? v * a.scale_log2 : -INFINITY;
         tmax = fmaxf(tmax, z[t][r]);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
@@ -220,7 +265,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
     psum += __shfl_xor(psum, 32);
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    // P^T operand: K slot 8g+i <-> row (i<4 ? 4g+i : 16+4g+i-4), i.e. this lane's own p
+    // P^T operand: K slot 8g+i <-> tile row 8g+i = this lane's p[i/4][i%4]
     uint32_t phi[4], plo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -236,13 +281,15 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
     for (int mt = 0; mt < 8; ++mt) {
       acc[mt] *= alpha;
       const int ch = 128 * wid + 16 * mt + n16;
-      const uint2 lo4 = *reinterpret_cast<const uint2*>(sm.xt + ch * kXTStride + 4 * g);
-      const uint2 hi4 = *reinterpret_cast<const uint2*>(sm.xt + ch * kXTStride + 16 + 4 * g);
+      const uint2 lo4 = *reinterpret_cast<const uint2*>(sm.xt + ch * kXTStride + 8 * g);
+      const uint2 hi4 = *reinterpret_cast<const uint2*>(sm.xt + ch * kXTStride + 8 * g + 4);
       const bf16x8 A = as_bf16x8(make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bhi, acc[mt], 0, 0, 0);
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Blo, acc[mt], 0, 0, 0);
     }
   }
+
+  }  // segments
 
   // ---- write: lane holds head `head`, channels 128*wid + 16*mt + 4*g + r
   if (a.nsplit == 1) {
@@ -268,28 +315,70 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
 }
 
 // Combine the row ranges of one (query, head): out = sum_s 2^(m_s-M) O_s / L.
-__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
+// 512 threads: four groups of 128 each sum a quarter of the ranges (all their loads
+// issued together), then the groups are added in a fixed order.
+constexpr int kMergeMaxSplits = 256;
+__global__ __launch_bounds__(512) void attn_merge_kernel(AttnArgs a) {
+  __shared__ float wgt[kMergeMaxSplits];
+  __shared__ float4 part[3][128];
+  __shared__ float Ms, Ls;
   const int head = blockIdx.x, qrow = blockIdx.y, tid = threadIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s)
-    M = fmaxf(M, a.part_ml[2 * (((int64_t)qrow * a.nsplit + s) * a.H + head)]);
-  float L = 0.0f;
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < a.nsplit; ++s) {
-    const int64_t pidx = ((int64_t)qrow * a.nsplit + s) * a.H + head;
-    const float ms = a.part_ml[2 * pidx], ls = a.part_ml[2 * pidx + 1];
-    const float wgt = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
-    L += ls * wgt;
-    const float4 v = reinterpret_cast<const float4*>(a.part_o + pidx * kLatentDim)[tid];
-    o.x += v.x * wgt;
-    o.y += v.y * wgt;
-    o.z += v.z * wgt;
-    o.w += v.w * wgt;
+  const int grp = tid >> 7, t = tid & 127;
+  const int64_t base = (int64_t)qrow * a.nsplit * a.H + head;  // + s * H
+  if (tid < 64) {
+    float M = -INFINITY;
+    for (int s = tid; s < a.nsplit; s += 64) M = fmaxf(M, a.part_ml[2 * (base + (int64_t)s * a.H)]);
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float L = 0.0f;
+    for (int s = tid; s < a.nsplit; s += 64) {
+      const int64_t pidx = base + (int64_t)s * a.H;
+      const float ms = a.part_ml[2 * pidx];
+      const float w = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
+      wgt[s] = w;
+      L += a.part_ml[2 * pidx + 1] * w;
+    }
+    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+    if (tid == 0) {
+      Ms = M;
+      Ls = L;
+    }
   }
-  const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
-  reinterpret_cast<float4*>(a.out + ((int64_t)qrow * a.H + head) * kLatentDim)[tid] =
-      make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
-  if (tid == 0) a.lse[(int64_t)qrow * a.H + head] = (L > 0.0f) ? (M + log2f(L)) / kLog2e : -INFINITY;
+  __syncthreads();
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = grp; s0 < a.nsplit; s0 += 32) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + 4 * u;
+      v[u] = (s < a.nsplit) ? reinterpret_cast<const float4*>(a.part_o + (base + (int64_t)s * a.H) * kLatentDim)[t]
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + 4 * u;
+      const float w = (s < a.nsplit) ? wgt[s] : 0.0f;
+      o.x += v[u].x * w;
+      o.y += v[u].y * w;
+      o.z += v[u].z * w;
+      o.w += v[u].w * w;
+    }
+  }
+  if (grp > 0) part[grp - 1][t] = o;
+  __syncthreads();
+  if (grp == 0) {
+    for (int g2 = 0; g2 < 3; ++g2) {
+      const float4 p = part[g2][t];
+      o.x += p.x;
+      o.y += p.y;
+      o.z += p.z;
+      o.w += p.w;
+    }
+    const float L = Ls;
+    const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+    reinterpret_cast<float4*>(a.out + ((int64_t)qrow * a.H + head) * kLatentDim)[t] =
+        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+    if (t == 0) a.lse[(int64_t)qrow * a.H + head] = (L > 0.0f) ? (Ms + log2f(L)) / kLog2e : -INFINITY;
+  }
 }
 
 // Row ranges per query: enough workgroups to spread a small batch over the chip,
@@ -322,7 +411,7 @@ static int run_attention(AttnArgs a, void* ws, size_t ws_bytes, hipStream_t stre
   const dim3 grid((unsigned)a.nsplit, (unsigned)(a.H / 16), (unsigned)a.nq);
   hipLaunchKernelGGL(sparse_attn_kernel, grid, dim3(256), 0, stream, a);
   if (a.nsplit > 1)
-    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)a.H, (unsigned)a.nq), dim3(128), 0, stream, a);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)a.H, (unsigned)a.nq), dim3(512), 0, stream, a);
   return launch_status();
 }
 

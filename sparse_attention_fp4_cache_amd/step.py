@@ -89,23 +89,28 @@ class DecodeStep:
         self.new_slot = torch.from_numpy(np.array(last_slot, np.int64)).to(self.device)
 
     # -------------------------------------------------------------- step --
-    def run(self, keep_scores: bool = False):
-        """One decode step over the layer schedule (enqueued on the current stream)."""
+    def run(self, keep_scores: bool = False, hook=None):
+        """One decode step over the layer schedule (enqueued on the current stream).
+        hook(phase, name), if given, is called with "start"/"end" around each call."""
+        call = _caller(hook)
         latest = None
         for L in self.layers:
             mode = L["mode"]
             if mode == "full":
-                lib.fp4_cache_write(self.cache, self.new_latent, self.new_key, self.new_slot)
+                call("fp4_cache_write", lib.fp4_cache_write, self.cache, self.new_latent, self.new_key,
+                     self.new_slot)
             if mode in ("full", "reindex"):
-                lib.index_score(self.cache, L["q_idx"], L["w"], self.n_visible, self.block_table, self.scores)
+                call("index_score", lib.index_score, self.cache, L["q_idx"], L["w"], self.n_visible,
+                     self.block_table, self.scores)
                 if keep_scores:
                     L["scores"] = self.scores.clone()
-                lib.topk_select(self.scores, self.n_visible, self.wl.K, L["topk"], self.ws_topk)
+                call("topk_select", lib.topk_select, self.scores, self.n_visible, self.wl.K, L["topk"],
+                     self.ws_topk)
                 latest = L["topk"]
             if latest is None:
                 raise ValueError("a reuse layer needs an earlier full or reindex layer")
-            lib.sparse_attn_decode(self.cache, L["q"], latest, self.block_table, L["swa"], L["swa_len"],
-                                   self.scale, L["out"], L["lse"], self.ws_attn)
+            call("sparse_attn_decode", lib.sparse_attn_decode, self.cache, L["q"], latest, self.block_table,
+                 L["swa"], L["swa_len"], self.scale, L["out"], L["lse"], self.ws_attn)
 
 
 class PrefillStep:
@@ -155,11 +160,24 @@ class PrefillStep:
         self.chunk_key = to_device_bits(key[n:n + nc], self.device)
         self.chunk_slot = torch.from_numpy(slots[n:n + nc]).to(self.device)
 
-    def run(self):
+    def run(self, hook=None):
         wl = self.wl
-        lib.fp4_cache_write(self.cache, self.chunk_latent, self.chunk_key, self.chunk_slot)
-        lib.index_score(self.cache, self.q_idx, self.w, self.n_visible, self.block_table2d, self.scores,
-                        seq_of_query=self.seq_of_query)
-        lib.topk_select(self.scores, self.n_visible, wl.K, self.topk, self.ws_topk)
-        lib.sparse_attn_prefill_chunk(self.cache, self.q, self.topk, self.block_table, int(wl.ctx[0]), self.swa,
-                                      self.swa_first_valid, wl.W, self.scale, self.out, self.lse, self.ws_attn)
+        call = _caller(hook)
+        call("fp4_cache_write", lib.fp4_cache_write, self.cache, self.chunk_latent, self.chunk_key, self.chunk_slot)
+        call("index_score", lib.index_score, self.cache, self.q_idx, self.w, self.n_visible, self.block_table2d,
+             self.scores, seq_of_query=self.seq_of_query)
+        call("topk_select", lib.topk_select, self.scores, self.n_visible, wl.K, self.topk, self.ws_topk)
+        call("sparse_attn_prefill_chunk", lib.sparse_attn_prefill_chunk, self.cache, self.q, self.topk,
+             self.block_table, int(wl.ctx[0]), self.swa, self.swa_first_valid, wl.W, self.scale, self.out, self.lse,
+             self.ws_attn)
+
+
+def _caller(hook):
+    def call(name, fn, *a, **kw):
+        if hook is not None:
+            hook("start", name)
+        fn(*a, **kw)
+        if hook is not None:
+            hook("end", name)
+
+    return call

@@ -94,9 +94,8 @@ def test_topk_validation(L):
     assert L.topk_select(FAKE, 10000, FAKE, 2, 64, FAKE, None, ws, None) == -4
     assert L.topk_select(FAKE, 10000, FAKE, 2, 64, FAKE, FAKE, ws - 1, None) == -4
     assert L.topk_select(FAKE, 10000, FAKE, 0, 64, FAKE, FAKE, ws, None) == 0
-    # workspace grows with the number of queries and the row length
+    # workspace grows with the number of queries
     assert L.topk_select_workspace_size(4, 10000, 64) > ws
-    assert L.topk_select_workspace_size(2, 10_000_000, 64) > ws
 
 
 def test_attention_validation(L):

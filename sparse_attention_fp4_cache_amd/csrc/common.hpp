@@ -78,4 +78,13 @@ CSA2_DEV uint32_t score_key(float s) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also waits for
+// every outstanding global load, which would stall loads issued ahead of time to
+// hide memory latency; this one leaves them in flight.
+CSA2_DEV void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace csa2

@@ -84,11 +84,15 @@ CSA2_DEV uint32_t bf16_rne_bits(float f) {  // fp32 -> bf16 bits, round to neare
 }
 
 // Raw bytes of this thread's 8 rows x 8 channels of one tile, as loaded from HBM.
-// Thread t: rows 8*(t%4) .. +7, channels 8*(t/4) .. +7.
+// Thread t: rows 8*(t%4) .. +7, channels 8*(t/4) .. +7.  Every row issues the same
+// loads whatever its kind (addresses of missing kinds are clamped to row 0), so the
+// compiler keeps all of them in flight together instead of waiting per branch.
 struct TileRegs {
-  uint32_t w[8][4];  // main row: w[rr][0] = 4 code bytes; window row: 8 bf16
-  uint32_t sc[8];    // main row: E4M3 scale byte
-  int kind[8];       // 0 none, 1 main, 2 window
+  uint32_t code[8];   // main row: 4 code bytes (8 channels)
+  uint32_t sc[8];     // main row: E4M3 scale byte
+  uint4 win[8];       // window row: 8 bf16
+  uint32_t mmask[8];  // all ones for a main row
+  uint32_t wmask[8];  // all ones for a window row
 };
 
 CSA2_DEV void issue_tile(const AttnArgs& a, const AttnSmem& sm, int tile_row0, int r_local_end, TileRegs& t) {
@@ -98,46 +102,46 @@ CSA2_DEV void issue_tile(const AttnArgs& a, const AttnSmem& sm, int tile_row0, i
   for (int rr = 0; rr < 8; ++rr) {
     const int rl = tile_row0 + 8 * rg + rr;  // row index local to this segment
     const int src = (rl < r_local_end) ? sm.src[rl] : -1;
-    t.kind[rr] = 0;
-    if (src >= 0) {
-      t.kind[rr] = 1;
-      t.w[rr][0] = *reinterpret_cast<const uint32_t*>(a.main_codes + (int64_t)src * kMainRowBytes + 4 * cb);
-      t.sc[rr] = a.main_scales[(int64_t)src * kMainScaleBytes + (cb >> 1)];
-    } else if (src <= -2) {
-      t.kind[rr] = 2;
-      const uint4 v = *reinterpret_cast<const uint4*>(a.swa + (int64_t)(-2 - src) * kLatentDim + 8 * cb);
-      t.w[rr][0] = v.x;
-      t.w[rr][1] = v.y;
-      t.w[rr][2] = v.z;
-      t.w[rr][3] = v.w;
+    t.mmask[rr] = src >= 0 ? ~0u : 0u;
+    t.wmask[rr] = src <= -2 ? ~0u : 0u;
+    const int64_t slot = src >= 0 ? src : 0;
+    t.code[rr] = *reinterpret_cast<const uint32_t*>(a.main_codes + slot * kMainRowBytes + 4 * cb);
+    t.sc[rr] = a.main_scales[slot * kMainScaleBytes + (cb >> 1)];
+  }
+  if (a.window > 0) {
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const int rl = tile_row0 + 8 * rg + rr;
+      const int src = (rl < r_local_end) ? sm.src[rl] : -1;
+      const int64_t wrow = src <= -2 ? (int64_t)(-2 - src) : 0;
+      t.win[rr] = *reinterpret_cast<const uint4*>(a.swa + wrow * kLatentDim + 8 * cb);
     }
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) t.win[rr] = make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
 // Dequantise the loaded bytes into X (row-major) and XT (transposed) in LDS.
-// XT rows are written as 16-byte runs of 8 consecutive tile rows; with a channel
-// stride of 18 dwords the 64 lanes of a wavefront spread over all LDS banks.
+// Branch-free: E4M3 scale via V_CVT_F32_FP8 (OCP E4M3FN on gfx950), E2M1 pairs via
+// V_CVT_SCALEF32_PK_F32_FP4 with a unit scale, product exact in fp32 and in bf16.
+// XT rows are written as 16-byte runs of 8 consecutive tile rows.
 CSA2_DEV void store_tile(AttnSmem& sm, const TileRegs& t) {
   const int tid = threadIdx.x;
   const int rg = tid & 3, cb = tid >> 2;
   uint32_t w[8][4];
 #pragma unroll
   for (int rr = 0; rr < 8; ++rr) {
-    if (t.kind[rr] == 1) {
-      const float s = e4m3_value(t.sc[rr]);
+    const float s = __builtin_amdgcn_cvt_f32_fp8((int)t.sc[rr], 0);
+    const v2f d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.code[rr], 1.0f, 0);
+    const v2f d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.code[rr], 1.0f, 1);
+    const v2f d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.code[rr], 1.0f, 2);
+    const v2f d3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.code[rr], 1.0f, 3);
+    const uint32_t m[4] = {pack_bf16_hi(d0[0] * s, d0[1] * s), pack_bf16_hi(d1[0] * s, d1[1] * s),
+                           pack_bf16_hi(d2[0] * s, d2[1] * s), pack_bf16_hi(d3[0] * s, d3[1] * s)};
+    const uint32_t wv[4] = {t.win[rr].x, t.win[rr].y, t.win[rr].z, t.win[rr].w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {  // code byte i -> channels 2i, 2i+1
-        const uint32_t byte = (t.w[rr][0] >> (8 * i)) & 0xFFu;
-        const v2f d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, 1.0f, 0);
-        w[rr][i] = pack_bf16_hi(d[0] * s, d[1] * s);
-      }
-    } else if (t.kind[rr] == 2) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[rr][i] = t.w[rr][i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[rr][i] = 0u;
-    }
+    for (int i = 0; i < 4; ++i) w[rr][i] = (m[i] & t.mmask[rr]) | (wv[i] & t.wmask[rr]);
     *reinterpret_cast<uint4*>(sm.x + (8 * rg + rr) * kXStride + 8 * cb) =
         make_uint4(w[rr][0], w[rr][1], w[rr][2], w[rr][3]);
   }
@@ -146,15 +150,15 @@ CSA2_DEV void store_tile(AttnSmem& sm, const TileRegs& t) {
     uint32_t lo[4], hi[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      lo[p] = (w[2 * p][i] & 0xFFFFu) | (w[2 * p + 1][i] << 16);
-      hi[p] = (w[2 * p][i] >> 16) | (w[2 * p + 1][i] & 0xFFFF0000u);
+      lo[p] = __builtin_amdgcn_perm(w[2 * p + 1][i], w[2 * p][i], 0x05040100u);
+      hi[p] = __builtin_amdgcn_perm(w[2 * p + 1][i], w[2 * p][i], 0x07060302u);
     }
-    uint2* d0 = reinterpret_cast<uint2*>(sm.xt + (8 * cb + 2 * i) * kXTStride + 8 * rg);
-    uint2* d1 = reinterpret_cast<uint2*>(sm.xt + (8 * cb + 2 * i + 1) * kXTStride + 8 * rg);
-    d0[0] = make_uint2(lo[0], lo[1]);
-    d0[1] = make_uint2(lo[2], lo[3]);
-    d1[0] = make_uint2(hi[0], hi[1]);
-    d1[1] = make_uint2(hi[2], hi[3]);
+    uint2* dst0 = reinterpret_cast<uint2*>(sm.xt + (8 * cb + 2 * i) * kXTStride + 8 * rg);
+    uint2* dst1 = reinterpret_cast<uint2*>(sm.xt + (8 * cb + 2 * i + 1) * kXTStride + 8 * rg);
+    dst0[0] = make_uint2(lo[0], lo[1]);
+    dst0[1] = make_uint2(lo[2], lo[3]);
+    dst1[0] = make_uint2(hi[0], hi[1]);
+    dst1[1] = make_uint2(hi[2], hi[3]);
   }
 }
 
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
 
   for (int seg0 = 0; seg0 < nrows; seg0 += kSeg) {
   const int seg_n = min(kSeg, nrows - seg0);
-  __syncthreads();  // the previous segment's sources are no longer read
+  lds_barrier();  // the previous segment's sources are no longer read
   // where every row of this segment comes from (one round of index loads)
   for (int rl = tid; rl < seg_n; rl += 256) {
     const int r = r_begin + seg0 + rl;
@@ -210,14 +214,14 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
     }
     sm.src[rl] = src;
   }
-  __syncthreads();
+  lds_barrier();
   TileRegs cur;
   issue_tile(a, sm, 0, seg_n, cur);
   for (int row0 = 0; row0 < seg_n; row0 += kRT) {
-    __syncthreads();  // previous tile fully consumed
+    lds_barrier();  // previous tile fully consumed
     store_tile(sm, cur);
     if (row0 + kRT < seg_n) issue_tile(a, sm, row0 + kRT, seg_n, cur);  // next tile in flight
-    __syncthreads();
+    lds_barrier();
     // ---- partial logits over this wavefront's 128 channels, two 16-row M-tiles
     v4f s[2];
 #pragma unroll
@@ -234,7 +238,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) sm.red[wid][t][r][lane] = s[t][r];
     }
-    __syncthreads();
+    lds_barrier();
     // full logits (same fixed summation order in every wavefront), scaled to log2 units
     float z[2][4];
     float tmax = -INFINITY;
@@ -244,7 +248,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
       for (int r = 0; r < 4; ++r) {
         const float v = ((sm.red[0][t][r][lane] + sm.red[1][t][r][lane]) + sm.red[2][t][r][lane]) + sm.red[3][t][r][lane];
         const int rl = row0 + 8 * g + 4 * t + r;
-        const bool valid = rl < seg_n && sm.src[rl] != -1;
+        const bool valid = (rl < seg_n) & (sm.src[rl & (kSeg - 1)] != -1);  // no short-circuit branch
         z[t][r] = valid ? v * a.scale_log2 : -INFINITY;
         tmax = fmaxf(tmax, z[t][r]);
       }
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[t][r] = (z[t][r] == -INFINITY) ? 0.0f : exp2f(z[t][r] - m_new);
+        p[t][r] = exp2f(z[t][r] - (m_new == -INFINITY ? 0.0f : m_new));  // exp2(-inf) = 0
         psum += p[t][r];
       }
     psum += __shfl_xor(psum, 16);

@@ -34,6 +34,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kMaxSpread = 12;   // exponent-sum span accepted on the MFMA path
 constexpr int kMinExpSum = 130;  // keeps every nonzero dot >= 2^-126 (fp32 normal)
 constexpr int kMaxExpSum = 360;  // keeps every dot far below fp32 overflow
+constexpr int kMaxPagesPerWave = 16;  // pages (of 64 entries) one wavefront scans
 
 // per-query staging record in LDS, for Hi = 16*MT heads
 template <int MT>
@@ -44,8 +45,8 @@ struct QStage {
   float w[16 * MT];
   int row;
   int nvis;
-  int ok_spread;  // 12 - (largest per-head block-exponent span)
-  int umin, umax;
+  int ok_spread;  // largest per-head block-exponent span of the query
+  int umin, umax;  // smallest / largest block exponent of the query
 };
 
 // Head held by row rho of M-tile mt: lane group rho/4 owns heads [(rho/4)*4MT, +4MT).
@@ -53,6 +54,10 @@ template <int MT>
 CSA2_DEV int head_of(int mt, int rho) { return (rho >> 2) * 4 * MT + 4 * mt + (rho & 3); }
 
 // MX32 quantisation of one 32-channel block held by one thread -> 16 packed bytes.
+// For a normal power-of-two scale X the hardware V_CVT_SCALEF32_PK_FP4_F32 computes
+// round-to-nearest-even(x / X) with saturation and a copied sign bit, which is the
+// element rule exactly (checked on gfx950 against every bf16 value); blocks whose
+// shared exponent is near the ends of the range take the compare-based rule.
 CSA2_DEV void mx32_block(const uint16_t* __restrict__ src, uint4& out, uint32_t& u_out) {
   uint32_t raw[16];
 #pragma unroll
@@ -63,21 +68,37 @@ CSA2_DEV void mx32_block(const uint16_t* __restrict__ src, uint4& out, uint32_t&
     raw[4 * i + 2] = t.z;
     raw[4 * i + 3] = t.w;
   }
-  float amax = 0.0f;
+  uint32_t amax_bits = 0;  // |x| as bf16 bits orders like the value
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    amax = fmaxf(amax, fmaxf(fabsf(bf16_to_f32(raw[i] & 0xFFFFu)), fabsf(bf16_to_f32(raw[i] >> 16))));
-  const uint32_t u = mx_exponent(amax);
+  for (int i = 0; i < 16; ++i) {
+    amax_bits = max(amax_bits, raw[i] & 0x7FFFu);
+    amax_bits = max(amax_bits, (raw[i] >> 16) & 0x7FFFu);
+  }
+  const uint32_t u = mx_exponent(bf16_to_f32(amax_bits));
   const float X = ldexpf(1.0f, (int)u - 127);
   uint32_t word[4] = {0u, 0u, 0u, 0u};
+  if (u >= 4u && u <= 250u) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {  // element pair (2i, 2i+1) -> byte i
-    uint32_t c = e2m1_code(bf16_to_f32(raw[i] & 0xFFFFu), X) | (e2m1_code(bf16_to_f32(raw[i] >> 16), X) << 4);
-    word[i >> 2] |= c << (8 * (i & 3));
+    for (int i = 0; i < 16; ++i) {  // element pair (2i, 2i+1) -> byte i
+      const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, bf16_to_f32(raw[i] & 0xFFFFu),
+                                                                   __uint_as_float(raw[i] & 0xFFFF0000u), X, 0);
+      word[i >> 2] |= (c & 0xFFu) << (8 * (i & 3));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint32_t c = e2m1_code(bf16_to_f32(raw[i] & 0xFFFFu), X) | (e2m1_code(bf16_to_f32(raw[i] >> 16), X) << 4);
+      word[i >> 2] |= c << (8 * (i & 3));
+    }
   }
   out = make_uint4(word[0], word[1], word[2], word[3]);
   u_out = u;
 }
+
+// max(d, 0) on the bit pattern: non-negative floats order like signed integers and
+// every negative float (including -0) is a negative integer, so this is one integer
+// max with no canonicalisation (d is never NaN for visible entries).
+CSA2_DEV float relu(float d) { return __int_as_float(max(__float_as_int(d), 0)); }
 
 // Exact d_h for one (query head, entry): integer block sums, fp64 combination in
 // block order, one rounding to fp32 (the definition itself).
@@ -148,6 +169,20 @@ __global__ __launch_bounds__(256) void index_score_kernel(const uint8_t* __restr
   QStage<MT>* st = reinterpret_cast<QStage<MT>*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int q0 = blockIdx.y * qt;
+  const int gfirst = (blockIdx.x * 4 + wid) * groups_per_wave;
+  const int gend = min(gfirst + groups_per_wave, total_groups);
+  const int first_row = (q0 < nq) ? (seq_of_query ? seq_of_query[q0] : q0) : 0;
+
+  // ---- physical pages of this wavefront (one table read), and the first two pages
+  // of keys in flight while the queries are staged
+  int pages[kMaxPagesPerWave];
+#pragma unroll
+  for (int i = 0; i < kMaxPagesPerWave; ++i)
+    pages[i] = (gfirst + i < gend) ? block_table[(int64_t)first_row * max_pages + gfirst + i] : 0;
+  KeyTile t0, t1, t2;
+  int cur_row = first_row;
+  if (gfirst < gend) load_keys(t0, idx_codes, idx_scales, (int64_t)pages[0] * kPage, lane);
+  if (gfirst + 1 < gend) load_keys(t1, idx_codes, idx_scales, (int64_t)pages[1] * kPage, lane);
 
   // ---- stage the tile's queries: MXFP4 operands, scales, weights
   for (int item = tid; item < qt * MT * 64; item += 256) {
@@ -168,46 +203,42 @@ __global__ __launch_bounds__(256) void index_score_kernel(const uint8_t* __restr
     const int q = q0 + tid;
     st[tid].row = (q < nq) ? (seq_of_query ? seq_of_query[q] : q) : 0;
     st[tid].nvis = (q < nq) ? n_visible[q] : 0;
+    st[tid].ok_spread = 0;  // largest per-head span until the reduction below is done
+    st[tid].umin = 255;
+    st[tid].umax = 0;
   }
-  __syncthreads();
-  if (tid < qt) {
-    int span = 0, umin = 255, umax = 0;
-    for (int h = 0; h < HI; ++h) {
-      int lo = 255, hi = 0;
-      for (int b = 0; b < 4; ++b) {
-        const int u = st[tid].u[h][b];
-        lo = u < lo ? u : lo;
-        hi = u > hi ? u : hi;
-      }
-      span = (hi - lo) > span ? (hi - lo) : span;
-      umin = lo < umin ? lo : umin;
-      umax = hi > umax ? hi : umax;
+  lds_barrier();
+  for (int item = tid; item < qt * HI; item += 256) {  // per-head block-exponent span
+    const int qi = item / HI, h = item % HI;
+    int lo = 255, hi = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int u = st[qi].u[h][b];
+      lo = u < lo ? u : lo;
+      hi = u > hi ? u : hi;
     }
-    st[tid].ok_spread = kMaxSpread - span;
-    st[tid].umin = umin;
-    st[tid].umax = umax;
+    atomicMax(&st[qi].ok_spread, hi - lo);
+    atomicMin(&st[qi].umin, lo);
+    atomicMax(&st[qi].umax, hi);
   }
-  __syncthreads();
-
-  // ---- this wavefront's pages
-  const int gfirst = (blockIdx.x * 4 + wid) * groups_per_wave;
-  if (gfirst >= total_groups) return;
-  const int gend = min(gfirst + groups_per_wave, total_groups);
+  lds_barrier();
+  if (gfirst >= gend) return;
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  int loaded_row = -1, loaded_g = -1;
-  KeyTile kt;
-  for (int G = gfirst; G < gend; ++G) {
+#pragma unroll 1
+  for (int i = 0; gfirst + i < gend; ++i) {
+    const int G = gfirst + i;
+    if (G + 2 < gend)  // two pages ahead stay in flight
+      load_keys(t2, idx_codes, idx_scales, (int64_t)pages[(i + 2) & (kMaxPagesPerWave - 1)] * kPage, lane);
+    KeyTile& cur = t0;
     for (int qi = 0; qi < qt; ++qi) {
       const QStage<MT>& s = st[qi];
       if (G * kPage >= s.nvis) continue;  // uniform
-      if (s.row != loaded_row || G != loaded_g) {
-        const int64_t slot0 = (int64_t)block_table[(int64_t)s.row * max_pages + G] * kPage;
-        load_keys(kt, idx_codes, idx_scales, slot0, lane);
-        loaded_row = s.row;
-        loaded_g = G;
+      if (s.row != cur_row) {  // a query of another sequence in this tile: load its page
+        load_keys(cur, idx_codes, idx_scales, (int64_t)block_table[(int64_t)s.row * max_pages + G] * kPage, lane);
+        cur_row = s.row;
       }
-      // 16x16 complete dots per MFMA: acc[mt][nt][r] = d(head(mt, 4*(lane/16)+r), entry 16nt + lane%16)
+      // 16x16 complete dots per MFMA: d[mt][nt][r] = d(head(mt, 4*(lane/16)+r), entry 16nt + lane%16)
       float d[MT][4][4];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -216,14 +247,14 @@ __global__ __launch_bounds__(256) void index_score_kernel(const uint8_t* __restr
         const int asc = (int)s.scale[mt >> 2][lane];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-          const v8i b = {(int)kt.codes[nt].x, (int)kt.codes[nt].y, (int)kt.codes[nt].z, (int)kt.codes[nt].w,
+          const v8i b = {(int)cur.codes[nt].x, (int)cur.codes[nt].y, (int)cur.codes[nt].z, (int)cur.codes[nt].w,
                          0, 0, 0, 0};
           v4f acc;
           switch (mt & 3) {
-            case 0: acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, 0, asc, 0, (int)kt.sc[nt]); break;
-            case 1: acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, 1, asc, 0, (int)kt.sc[nt]); break;
-            case 2: acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, 2, asc, 0, (int)kt.sc[nt]); break;
-            default: acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, 3, asc, 0, (int)kt.sc[nt]); break;
+            case 0: acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, 0, asc, 0, (int)cur.sc[nt]); break;
+            case 1: acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, 1, asc, 0, (int)cur.sc[nt]); break;
+            case 2: acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, 2, asc, 0, (int)cur.sc[nt]); break;
+            default: acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, 3, asc, 0, (int)cur.sc[nt]); break;
           }
 #pragma unroll
           for (int r = 0; r < 4; ++r) d[mt][nt][r] = acc[r];
@@ -236,7 +267,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(const uint8_t* __restr
         for (int r = 0; r < 4; ++r) transpose4(d[mt][0][r], d[mt][1][r], d[mt][2][r], d[mt][3][r]);
 
       const int j = G * kPage + lane;
-      const uint32_t own = kt.own;
+      const uint32_t own = cur.own;
       int kmin = 255, kmax = 0;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
@@ -244,23 +275,26 @@ __global__ __launch_bounds__(256) void index_score_kernel(const uint8_t* __restr
         kmin = u < kmin ? u : kmin;
         kmax = u > kmax ? u : kmax;
       }
-      const bool exact_needed = (j < s.nvis) && ((kmax - kmin) > s.ok_spread || s.umin + kmin < kMinExpSum ||
-                                                  s.umax + kmax > kMaxExpSum);
+      const bool exact_needed = (j < s.nvis) & (((kmax - kmin) + s.ok_spread > kMaxSpread) |
+                                                (s.umin + kmin < kMinExpSum) | (s.umax + kmax > kMaxExpSum));
       float acc = 0.0f;
 #pragma unroll
       for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc = fmaf(s.w[b * 4 * MT + 4 * mt + r], fmaxf(d[mt][b][r], 0.0f), acc);
+          for (int r = 0; r < 4; ++r) acc = fmaf(s.w[b * 4 * MT + 4 * mt + r], relu(d[mt][b][r]), acc);
       if (exact_needed) {  // rare: recompute this entry exactly
         const int64_t slot = (int64_t)block_table[(int64_t)s.row * max_pages + G] * kPage + lane;
         const uint8_t* krow = idx_codes + slot * kIdxRowBytes;
         acc = 0.0f;
-        for (int h = 0; h < HI; ++h) acc = fmaf(s.w[h], fmaxf(exact_dot<MT>(s, h, krow, own), 0.0f), acc);
+        for (int h = 0; h < HI; ++h) acc = fmaf(s.w[h], relu(exact_dot<MT>(s, h, krow, own)), acc);
       }
       if (j < s.nvis) scores[(int64_t)(q0 + qi) * ld + j] = acc;
     }
+    t0 = t1;  // t1 and t2 always hold this wavefront's own (first-row) pages
+    t1 = t2;
+    cur_row = first_row;
   }
 }
 
@@ -278,7 +312,7 @@ static int launch_mt(const csa2_fp4_cache* c, const uint16_t* q_idx, const float
   const long long want_waves = qtiles >= 512 ? 4 * qtiles : 2048;
   int gpw = (int)ceil_div(total_groups * qtiles, want_waves);
   if (gpw < 1) gpw = 1;
-  if (gpw > 64) gpw = 64;
+  if (gpw > kMaxPagesPerWave) gpw = kMaxPagesPerWave;
   const unsigned gx = ceil_div(total_groups, 4LL * gpw);
   const size_t lds = sizeof(QStage<MT>) * qt;
   hipLaunchKernelGGL(index_score_kernel<MT>, dim3(gx, (unsigned)qtiles), dim3(256), lds, stream, c->idx_codes,

@@ -346,3 +346,34 @@ def test_attention_prefill_truncated_windows():
                                   out, lse, ws)
     ro, rl = oracle.sparse_attn_prefill_chunk(o, q, idx, bt, swa, first_valid, W, scale)
     attn_close(out.cpu().numpy(), ro, lse.cpu().numpy(), rl, "prefill")
+
+
+def test_index_score_reveals_query_quantisation():
+    # keys +-1 at one channel each and one-hot head weights make every score equal
+    # max(+-qhat[h][c], 0), so the dequantised query is compared value by value;
+    # random bf16 bit patterns put block exponents across the whole range (both the
+    # hardware-convert and the compare-based quantisation paths run)
+    rng = np.random.default_rng(260)
+    n, Hi, groups = 256, 16, 4
+    key = np.zeros((n, 128), np.float32)
+    for c in range(128):
+        key[2 * c, c] = 1.0
+        key[2 * c + 1, c] = -1.0
+    lat = np.zeros((n, 512), np.float32)
+    g, o = both_caches(bits(lat), bits(key), np.arange(n, dtype=np.int64), n)
+    raw = rng.integers(0, 65536, (groups, Hi, 128)).astype(np.uint16)
+    f = (raw.astype(np.uint32) << 16).view(np.float32)
+    raw[~np.isfinite(f)] = 0x3F80
+    raw[1] = bits(rng.standard_normal((Hi, 128)) * 3.0)  # a typical group as well
+    q = np.repeat(raw, Hi, axis=0)  # [groups*Hi, Hi, 128]
+    w = np.tile(np.eye(Hi, dtype=np.float32), (groups, 1))
+    nq = groups * Hi
+    nvis = np.full(nq, n, np.int32)
+    bt = np.tile(np.arange(4, dtype=np.int32), (nq, 1))
+    scores = torch.full((nq, n), float("nan"), device="cuda")
+    say("case: index_score query quantisation revealed by one-hot keys")
+    lib.index_score(g, dev_bits(q), dev(w), dev(nvis), dev(bt), scores, seq_of_query=dev(np.zeros(nq, np.int32)))
+    ref, _, _ = oracle.index_score(o, q, w, nvis, bt, seq_of_query=np.zeros(nq, np.int32), ld=n)
+    got = scores.cpu().numpy()
+    bad = np.argwhere(got.view(np.int32) != ref.view(np.int32))
+    assert len(bad) == 0, f"{len(bad)} differ, first {bad[:5].tolist()}: {got[tuple(bad[0])]} vs {ref[tuple(bad[0])]}"

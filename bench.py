@@ -1,4 +1,4 @@
-"""Benchmark of the CSA2 FP4-cache decode step on one MI355X.
+"""Benchmark of the CSA2 FP4-cache step on one MI355X.
 
 Default workload: decode at 1,048,576 tokens of context (524,288 compressed
 entries, m = 2), batch 1, 64 heads, top-k 2048, 128-row bf16 window, and the
@@ -6,14 +6,21 @@ entries, m = 2), batch 1, 64 heads, top-k 2048, 128-row bf16 window, and the
 selections + 10 attentions + the Full layer's cache write per step).  Inputs are
 seeded synthetic data already resident in HBM when timing starts.
 
-Prints ONE JSON line: tokens/s (batch / step time), the FP4 cache bytes read per
-step and their rate, a roofline record for the dominant kernel (the indexer scan,
-timed with HIP events on its own stream), and the CPU oracle on a bounded sample.
+Cold mode is the headline: the step rotates over R copies of the cache whose
+total exceeds twice the 256 MB last-level (MALL) cache, so each step starts with
+its cache out of the MALL.  Warm mode (one copy, replayed) is reported beside it.
+
+Prints ONE JSON line: tokens/s (sequences / step time), the FP4 cache bytes read
+per step and their rate, a roofline record for the indexer scan (the kernel that
+carries the FP4 bytes), timed with HIP events on its own stream over graph
+replays of back-to-back launches, and the CPU oracle on a bounded sample.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 import argparse
+import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -22,8 +29,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 MFMA, published
 IDX_ENTRY_BYTES = 68  # 64 B of E2M1 codes + 4 E8M0 scales per indexer key
 MAIN_ENTRY_BYTES = 288  # 256 B of E2M1 codes + 32 E4M3 scales per main entry
+MALL_BYTES = 256 << 20
+METRIC = "decode tokens/sec & achieved HBM GB/s (FP4 cache) at 1M ctx, top-K 2048"
+# sources whose change invalidates a stored counter measurement of the scan kernel
+SCAN_SOURCES = ("sparse_attention_fp4_cache_amd/csrc/index_score.hip", "sparse_attention_fp4_cache_amd/csrc/common.hpp",
+                "sparse_attention_fp4_cache_amd/csrc/Makefile")
 
 
 def parse():
@@ -34,10 +47,44 @@ def parse():
     p.add_argument("--workload", default="decode_1m_10layer")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", type=int, default=1, help="replay the step as one HIP graph (1) or launch eagerly (0)")
+    p.add_argument("--replicas", type=int, default=0,
+                   help="cache copies rotated in cold mode (0: enough to exceed twice the MALL)")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="after timing, run one plain device copy of this size (counter calibration)")
     return p.parse_args()
 
 
+def scan_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in SCAN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(wl_name: str):
+    """HBM bytes per scan launch from the committed counter summary, or None when
+    there is none or the scan kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"index_score_traffic_{wl_name}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != scan_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def fp4_bytes_per_step(wl):
+    if wl.kind == "prefill":
+        return int(wl.n_visible().astype("int64").sum()) * IDX_ENTRY_BYTES + wl.chunk * wl.K * MAIN_ENTRY_BYTES
     idx_layers = sum(1 for m in wl.layers if m in ("full", "reindex"))
     n = [int(x) for x in wl.n_entries]
     b = idx_layers * sum(n) * IDX_ENTRY_BYTES
@@ -46,36 +93,58 @@ def fp4_bytes_per_step(wl):
 
 
 def cpu_baseline(wl):
-    """The oracle, as it is, on a bounded sample of the workload: one index layer
-    (scan + top-k) over the first 1/8 of the entries and one attention, scaled to
-    the whole step (scans and top-k linearly in entries)."""
+    """The oracle, as it is, on a bounded sample of the workload, scaled to one step.
+    Decode: one index layer (scan + top-k) over up to 524,288 entries of the first
+    sequence and one attention.  Prefill: two queries of the chunk end to end."""
     import numpy as np
 
     import oracle
     from sparse_attention_fp4_cache_amd.workloads import small_variant
 
+    if wl.kind == "prefill":
+        n = int(wl.n_entries[0]) + wl.n_chunk_entries
+        lat, key = wl.cache_rows(0, 0, n)
+        c = oracle.Cache(wl.num_slots)
+        oracle.fp4_cache_write(c, lat, key, wl.slots(0, 0, n))
+        d = wl.layer_inputs(0)
+        bt = wl.block_table()
+        which = np.array([0, wl.chunk - 1], np.int32)
+        nv = wl.n_visible()
+        t0 = time.perf_counter()
+        sc, _, _ = oracle.index_score(c, d["q_idx"][which], d["w"][which], nv[which], bt,
+                                      seq_of_query=np.zeros(2, np.int32))
+        idx = np.full((wl.chunk, wl.K), -1, np.int32)
+        idx[which] = oracle.topk_select(sc, nv[which], wl.K)
+        oracle.sparse_attn_prefill_chunk(c, d["q"], idx, bt[0], d["swa"], d["swa_first_valid"], wl.W,
+                                         1.0 / 512 ** 0.5, which=which)
+        dt = time.perf_counter() - t0
+        return {"value": len(which) / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": f"2 of the chunk's {wl.chunk} queries (scan, top-{wl.K}, attention), {dt:.2f} s"}
+
     n_full = int(wl.n_entries[0])
-    frac = 8 if n_full >= 8 * 4096 else 1
+    frac = max(1, math.ceil(n_full / 524288))
     sub = small_variant(wl, ctx=[int(wl.ctx[0]) // frac], name=wl.name + "_sample")
     n = int(sub.n_entries[0])
     lat, key = sub.cache_rows(0, 0, n)
     c = oracle.Cache(sub.num_slots)
     oracle.fp4_cache_write(c, lat, key, sub.slots(0, 0, n))
+    del lat, key
     d = sub.layer_inputs(0)
-    bt = sub.block_table()
-    nv = sub.n_visible()
+    bt = sub.block_table()[:1]
+    nv = sub.n_visible()[:1]
     t0 = time.perf_counter()
-    sc, _, _ = oracle.index_score(c, d["q_idx"], d["w"], nv, bt)
+    sc, _, _ = oracle.index_score(c, d["q_idx"][:1], d["w"][:1], nv, bt)
     idx = oracle.topk_select(sc, nv, sub.K)
     t1 = time.perf_counter()
-    oracle.sparse_attn_decode(c, d["q"], idx, bt, d["swa"], d["swa_len"], 1.0 / 512 ** 0.5)
+    oracle.sparse_attn_decode(c, d["q"][:1], idx, bt, d["swa"][:1], d["swa_len"][:1], 1.0 / 512 ** 0.5)
     t2 = time.perf_counter()
     idx_layers = sum(1 for m in wl.layers if m in ("full", "reindex"))
-    step_s = idx_layers * (t1 - t0) * frac + len(wl.layers) * (t2 - t1)
+    entries = sum(int(x) for x in wl.n_entries)
+    step_s = idx_layers * (t1 - t0) * entries / n + len(wl.layers) * wl.B * (t2 - t1)
     return {"value": wl.B / step_s, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": (f"one index layer (MXFP4 scan + top-{wl.K}) over {n} of {n_full} entries and one attention "
-                       f"({t1 - t0:.2f} s + {t2 - t1:.2f} s), scaled to the {len(wl.layers)}-layer step: scans and "
-                       f"top-k x{frac} x{idx_layers} layers, attention x{len(wl.layers)}")}
+            "sample": (f"one index layer (MXFP4 scan + top-{wl.K}) over {n} entries and one {wl.H}-head attention "
+                       f"({t1 - t0:.2f} s + {t2 - t1:.2f} s), scaled to the step: scans and top-k x{entries / n:g} "
+                       f"entries x{idx_layers} index layers, attention x{len(wl.layers)} layers x{wl.B} sequences")}
 
 
 def main():
@@ -104,75 +173,103 @@ def main():
     st = Step(wl, dev)
     st.build_cache()
     torch.cuda.synchronize()
+    R = args.replicas if args.replicas > 0 else 1 + math.ceil(2 * MALL_BYTES / st.cache.nbytes())
+    R = max(1, min(R, 16))
+    steps = [st] + [st.replica() for _ in range(R - 1)]
+    torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()  # every kernel of the step runs on this stream
-    ev_pairs = []
-
-    def timed_hook(phase, name):
-        if name != "index_score":
-            return
-        e = torch.cuda.Event(enable_timing=True)
-        e.record(stream)
-        if phase == "start":
-            ev_pairs.append([e, None])
-        else:
-            ev_pairs[-1][1] = e
-
     with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            st.run()
-    torch.cuda.synchronize()
-
-    graph = None
+        for s in steps:
+            s.run()  # one eager step per copy (the Full layer rewrites its newest entry)
+    stream.synchronize()
+    graphs = None
     if args.graph:
+        graphs = []
+        for s in steps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                s.run()
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def one_step(i, r):
+        if graphs is not None:
+            graphs[r].replay()
+        else:
+            steps[r].run()
+
+    def timed(n, rotate):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
         with torch.cuda.stream(stream):
-            st.run()  # one more eager step on the capture stream
-        stream.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            st.run()
+            for i in range(n):
+                one_step(i, i % R if rotate else 0)
         torch.cuda.synchronize()
-        for _ in range(2):
-            graph.replay()
-        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
 
-    # ---- timed region: K whole steps
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     with torch.cuda.stream(stream):
-        for _ in range(args.steps):
-            if graph is not None:
-                graph.replay()
-            else:
-                st.run()
+        for i in range(args.warmup):
+            one_step(i, i % R)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # ---- timed region: K whole steps, cold (rotating cache copies), then warm
+    ms_per_step = timed(args.steps, rotate=True)
+    warm_ms = timed(args.steps, rotate=False)
 
-    # ---- dominant kernel: index_score launches timed with events on their stream
-    with torch.cuda.stream(stream):
-        for _ in range(args.steps):
-            st.run(hook=timed_hook)
-    torch.cuda.synchronize()
-    durs = [a.elapsed_time(b) for a, b in ev_pairs]
-    idx_ms = sum(durs) / len(durs)
+    # ---- the scan kernel alone: back-to-back launches over the same inputs as the
+    # step (every index layer, every cache copy), timed with HIP events on the stream
     if wl.kind == "decode":
+        idx_calls = [(s.cache, L["q_idx"], L["w"], s.n_visible, s.block_table, s.scores, None)
+                     for s in steps for L in s.layers if L["mode"] in ("full", "reindex")]
         idx_bytes = sum(int(x) for x in wl.n_entries) * IDX_ENTRY_BYTES
-        step_bytes = fp4_bytes_per_step(wl)
         tokens = wl.B
     else:
+        idx_calls = [(s.cache, s.q_idx, s.w, s.n_visible, s.block_table2d, s.scores, s.seq_of_query) for s in steps]
         idx_bytes = int(wl.n_visible().astype("int64").sum()) * IDX_ENTRY_BYTES
-        step_bytes = idx_bytes + wl.chunk * wl.K * MAIN_ENTRY_BYTES
         tokens = wl.chunk
+
+    def scan_burst():
+        for c, qi, w, nv, bt, sc, soq in idx_calls:
+            lib.index_score(c, qi, w, nv, bt, sc, seq_of_query=soq)
+
+    reps = max(2, math.ceil(60 / len(idx_calls)))
+    with torch.cuda.stream(stream):
+        scan_burst()
+    stream.synchronize()
+    burst_graph = None
+    if args.graph:
+        burst_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(burst_graph, stream=stream):
+            scan_burst()
+        torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            if burst_graph is not None:
+                burst_graph.replay()
+            else:
+                scan_burst()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    idx_ms = e0.elapsed_time(e1) / (reps * len(idx_calls))
     achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
-    traffic = None
-    prof = os.path.join(ROOT, "profiles", f"index_score_traffic_{wl.name}.json")
-    if os.path.exists(prof):
-        with open(prof) as f:
-            traffic = json.load(f).get("traffic_bytes_per_launch")
+    traffic = stored_traffic(wl.name)
+    step_bytes = fp4_bytes_per_step(wl)
+
+    if args.copy_probe_mib > 0:
+        # a plain copy kernel of known size (read N, write N) for counter calibration
+        n = args.copy_probe_mib << 18
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     res = {
-        "metric": "decode tokens/sec & achieved HBM GB/s (FP4 cache) at 1M ctx, top-K 2048",
+        "metric": METRIC,
         "value": tokens / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -186,15 +283,23 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16 latents/keys/queries/window, U(0,1) head weights)",
         "config": {"workload": wl.name, "context_tokens": int(wl.ctx[0]) if wl.B == 1 else list(wl.ctx),
                    "entries_per_seq": [int(x) for x in wl.n_entries][:4], "batch": wl.B, "heads": wl.H,
-                   "index_heads": wl.Hi, "topk": wl.K, "window": wl.W, "layers": ",".join(wl.layers),
-                   "hip_graph": bool(args.graph)},
+                   "index_heads": wl.Hi, "topk": wl.K, "window": wl.W,
+                   "layers": ",".join(wl.layers) if wl.kind == "decode" else f"prefill chunk {wl.chunk}",
+                   "hip_graph": bool(args.graph), "cache_copies_rotated": R},
+        "warm_ms_per_step": warm_ms,
+        "warm_tokens_per_s": tokens / (warm_ms * 1e-3),
         "fp4_bytes_per_step": step_bytes,
         "fp4_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "fp4_frac_of_hbm_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {"kernel": "index_score", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "bytes_per_launch": idx_bytes, "avg_launch_ms": idx_ms, "launches_timed": len(durs)},
+                     "bytes_per_launch": idx_bytes, "avg_launch_ms": idx_ms,
+                     "launches_timed": reps * len(idx_calls)},
     }
+    if wl.kind == "prefill":
+        flop = int(wl.n_visible().astype("int64").sum()) * wl.Hi * 128 * 2
+        res["roofline_mfma_fp4"] = {"kernel": "index_score", "achieved": flop / (idx_ms * 1e-3) / 1e12,
+                                    "peak": MFMA_FP4_PEAK_TFLOPS, "unit": "TFLOP/s"}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(res), flush=True)

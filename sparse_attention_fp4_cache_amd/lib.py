@@ -145,6 +145,16 @@ class Cache:
     def nbytes(self) -> int:
         return self.num_slots * (256 + 32 + 64 + 4)
 
+    def clone(self) -> "Cache":
+        """A second cache in fresh device memory holding the same bytes."""
+        c = Cache.__new__(Cache)
+        c.num_slots = self.num_slots
+        for name in ("main_codes", "main_scales", "idx_codes", "idx_scales"):
+            setattr(c, name, getattr(self, name).clone())
+        c._s = _CacheStruct(c.main_codes.data_ptr(), c.main_scales.data_ptr(), c.idx_codes.data_ptr(),
+                            c.idx_scales.data_ptr(), c.num_slots, PAGE_SIZE)
+        return c
+
 
 def fp4_cache_write(cache: Cache, latent: torch.Tensor, idx_key: torch.Tensor, slot: torch.Tensor, stream=None):
     n = slot.shape[0]

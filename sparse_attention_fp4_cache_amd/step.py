@@ -14,6 +14,8 @@ in the HIP kernels behind ``lib``.
 """
 from __future__ import annotations
 
+import copy
+
 import numpy as np
 import torch
 
@@ -88,6 +90,13 @@ class DecodeStep:
         self.new_key = to_device_bits(np.stack(last_key), self.device)
         self.new_slot = torch.from_numpy(np.array(last_slot, np.int64)).to(self.device)
 
+    def replica(self) -> "DecodeStep":
+        """The same step over a copy of the cache in other device memory (query
+        inputs, outputs and workspaces are shared; run replicas one at a time)."""
+        r = copy.copy(self)
+        r.cache = self.cache.clone()
+        return r
+
     # -------------------------------------------------------------- step --
     def run(self, keep_scores: bool = False, hook=None):
         """One decode step over the layer schedule (enqueued on the current stream).
@@ -159,6 +168,12 @@ class PrefillStep:
         self.chunk_latent = to_device_bits(lat[n:n + nc], self.device)
         self.chunk_key = to_device_bits(key[n:n + nc], self.device)
         self.chunk_slot = torch.from_numpy(slots[n:n + nc]).to(self.device)
+
+    def replica(self) -> "PrefillStep":
+        """The same chunk step over a copy of the cache (other buffers shared)."""
+        r = copy.copy(self)
+        r.cache = self.cache.clone()
+        return r
 
     def run(self, hook=None):
         wl = self.wl

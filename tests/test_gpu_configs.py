@@ -1,0 +1,179 @@
+"""Whole-step GPU parity at the five workload configurations, at their full sizes.
+
+Each case builds the seeded synthetic inputs once, runs the step through the C ABI
+(the same calls and launch configurations the benchmark times), and compares with
+the CPU oracle run on the very same host arrays:
+  * cache bytes, indexer scores and top-k indices bit-exact;
+  * attention within 2e-3 absolute and 1e-2 of the largest reference magnitude.
+Where the oracle would take too long (the 4096-query prefill chunk), sampled
+queries are checked one by one and every query is checked for properties that
+hold at any size.  The oracle never sees a GPU result.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_fp4_cache_amd import lib
+from sparse_attention_fp4_cache_amd.step import DecodeStep, PrefillStep
+from sparse_attention_fp4_cache_amd.workloads import WORKLOADS
+from _helpers import attn_close, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    lib.load()
+
+
+def oracle_cache(wl):
+    """The oracle's own cache, written from the same seeded rows as the GPU cache."""
+    o = oracle.Cache(wl.num_slots)
+    for b in range(wl.B):
+        n = int(wl.n_entries[b]) + (wl.n_chunk_entries if wl.kind == "prefill" else 0)
+        lat, key = wl.cache_rows(b, 0, n)
+        oracle.fp4_cache_write(o, lat, key, wl.slots(b, 0, n))
+    return o
+
+
+def cache_equal(st, o, label):
+    for name in ("main_codes", "main_scales", "idx_codes", "idx_scales"):
+        a = getattr(st.cache, name).cpu().numpy()
+        b = getattr(o, name)
+        nbad = int(np.count_nonzero(a != b))
+        assert nbad == 0, f"{label}: {name} differs in {nbad} bytes"
+
+
+def scores_equal(got, ref, nvis, label):
+    for r in range(ref.shape[0]):
+        n = int(nvis[r])
+        g = np.ascontiguousarray(got[r, :n]).view(np.int32)
+        e = np.ascontiguousarray(ref[r, :n]).view(np.int32)
+        bad = np.flatnonzero(g != e)
+        assert len(bad) == 0, (f"{label}: row {r}: {len(bad)} scores differ, first entry {bad[0]}: "
+                               f"{got[r, bad[0]]!r} vs {ref[r, bad[0]]!r}")
+
+
+def topk_equal(got, ref, label):
+    bad = np.argwhere(got != ref)
+    assert len(bad) == 0, f"{label}: {len(bad)} top-k slots differ, first {bad[:4].tolist()}"
+
+
+def run_decode_case(name, attn_rows=None):
+    wl = WORKLOADS[name]
+    say(f"case: {name} (B={wl.B}, entries {int(wl.n_entries.min())}..{int(wl.n_entries.max())}, "
+        f"H={wl.H}, K={wl.K}, layers {','.join(wl.layers)})")
+    st = DecodeStep(wl, "cuda")
+    st.build_cache()
+    st.run(keep_scores=True)
+    torch.cuda.synchronize()
+    o = oracle_cache(wl)
+    cache_equal(st, o, name)
+    say("  cache bytes equal")
+    bt = wl.block_table()
+    nv = wl.n_visible()
+    latest = None
+    for li, L in enumerate(st.layers):
+        d = wl.layer_inputs(li)
+        if L["mode"] in ("full", "reindex"):
+            ref_s, not_fp32, _ = oracle.index_score(o, d["q_idx"], d["w"], nv, bt, ld=st.ld)
+            assert not_fp32 == 0
+            scores_equal(L["scores"].cpu().numpy(), ref_s, nv, f"{name} layer {li} scores")
+            latest = oracle.topk_select(ref_s, nv, wl.K)
+            topk_equal(L["topk"].cpu().numpy(), latest, f"{name} layer {li} top-k")
+            say(f"  layer {li} ({L['mode']}): scores and top-k bit-exact")
+        rows = np.arange(wl.B) if attn_rows is None else np.asarray(attn_rows)
+        ro, rl = oracle.sparse_attn_decode(o, d["q"][rows], latest[rows], bt[rows], d["swa"][rows],
+                                           d["swa_len"][rows], st.scale)
+        attn_close(L["out"].cpu().numpy()[rows], ro, L["lse"].cpu().numpy()[rows], rl,
+                   f"{name} layer {li} ({L['mode']}) attention")
+    return st
+
+
+def test_config_tiny_decode():
+    run_decode_case("tiny_decode")
+
+
+@pytest.mark.timeout(600)
+def test_config_decode_131k_outliers():
+    run_decode_case("decode_131k")
+
+
+@pytest.mark.timeout(900)
+def test_config_ragged_decode_32_paged():
+    # scores and top-k for all 32 sequences; attention for 8 of them (every 4th)
+    run_decode_case("ragged_decode_32", attn_rows=np.arange(0, 32, 4))
+
+
+@pytest.mark.timeout(1200)
+def test_config_decode_1m_10layer_and_graph_replay():
+    st = run_decode_case("decode_1m_10layer")
+    # the benchmark replays the step as one HIP graph: every replay must equal the
+    # eager step bit for bit, with eager work and synchronisations in between
+    ref = [(L["out"].clone(), L["lse"].clone(), None if "topk" not in L else L["topk"].clone()) for L in st.layers]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        st.run()
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        st.run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for L in st.layers:
+            L["out"].zero_()
+            L["lse"].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for li, (L, (o, l, t)) in enumerate(zip(st.layers, ref)):
+            assert torch.equal(L["out"].view(torch.int32), o.view(torch.int32)), f"replay {rep} layer {li} out"
+            assert torch.equal(L["lse"].view(torch.int32), l.view(torch.int32)), f"replay {rep} layer {li} lse"
+            if t is not None:
+                assert torch.equal(L["topk"], t), f"replay {rep} layer {li} top-k"
+        st.run()  # eager work between replays
+        torch.cuda.synchronize()
+    say("  graph replays equal the eager step")
+
+
+@pytest.mark.timeout(1200)
+def test_config_prefill_chunk_4096():
+    wl = WORKLOADS["prefill_chunk_4096"]
+    T, K = wl.chunk, wl.K
+    say(f"case: prefill_chunk_4096 (prefix {int(wl.n_entries[0])} entries + {wl.n_chunk_entries} in-chunk, "
+        f"T={T}, K={K})")
+    st = PrefillStep(wl, "cuda")
+    st.build_cache()
+    st.run()
+    torch.cuda.synchronize()
+    o = oracle_cache(wl)
+    cache_equal(st, o, "prefill")
+    say("  cache bytes equal (prefix + chunk entries)")
+    nv = wl.n_visible()
+    topk = st.topk.cpu().numpy()
+    # properties over every query: K distinct indices below n_visible, ascending
+    assert topk.shape == (T, K)
+    assert np.all(topk >= 0) and np.all(topk < nv[:, None]), "index out of the causal range"
+    assert np.all(np.diff(topk, axis=1) > 0), "indices not strictly ascending"
+    lse = st.lse.cpu().numpy()
+    assert np.all(np.isfinite(lse)), "non-finite lse"
+    say("  all queries: top-k causal, distinct, ascending; lse finite")
+    # sampled queries, one by one: first, around the odd/even boundary, middle, last
+    which = np.array([0, 1, 2, 2047, 2048, T - 2, T - 1], np.int32)
+    d = wl.layer_inputs(0)
+    bt = wl.block_table()
+    ld = st.ld
+    ref_s, not_fp32, _ = oracle.index_score(o, d["q_idx"][which], d["w"][which], nv[which], bt,
+                                            seq_of_query=np.zeros(len(which), np.int32), ld=ld)
+    assert not_fp32 == 0
+    got_s = st.scores[torch.from_numpy(which.astype(np.int64)).cuda()].cpu().numpy()
+    scores_equal(got_s, ref_s, nv[which], "prefill sampled scores")
+    ref_k = oracle.topk_select(ref_s, nv[which], K)
+    topk_equal(topk[which], ref_k, "prefill sampled top-k")
+    say(f"  queries {which.tolist()}: scores and top-k bit-exact")
+    idx_full = np.full((T, K), -1, np.int32)
+    idx_full[which] = ref_k
+    ro, rl = oracle.sparse_attn_prefill_chunk(o, d["q"], idx_full, bt[0], d["swa"], d["swa_first_valid"], wl.W,
+                                              st.scale, which=which)
+    attn_close(st.out.cpu().numpy()[which], ro[which], lse[which], rl[which], "prefill sampled attention")

@@ -42,10 +42,15 @@ def build() -> str:
 def lib():
     global _lib
     if _lib is None:
-        src = os.path.join(_HERE, "oracle.c")
-        if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(src):
-            build()
-        L = ctypes.CDLL(_SO)
+        # CSA2_ORACLE_LIB names another build of oracle.c (the mutation tests load
+        # copies with planted mistakes to show that the pins catch them)
+        path = os.environ.get("CSA2_ORACLE_LIB")
+        if path is None:
+            path = _SO
+            src = os.path.join(_HERE, "oracle.c")
+            if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(src):
+                build()
+        L = ctypes.CDLL(path)
         for name in ("oracle_bf16_value", "oracle_e2m1_value", "oracle_e4m3_value", "oracle_e8m0_value"):
             getattr(L, name).restype = ctypes.c_double
         L.oracle_bf16_value.argtypes = [ctypes.c_uint16]

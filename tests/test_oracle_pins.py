@@ -262,6 +262,28 @@ def _small_cache(rng, n, outlier=False):
     return c
 
 
+def test_cache_layout_low_nibble_first_at_its_slot():
+    # storage convention: channel 2k in bits 0-3 and 2k+1 in bits 4-7 of byte k (the
+    # element order of OCP MX packed FP4, and of the gfx950 FP4 MFMA operands); the
+    # scale bytes follow the block order; row i lands at slot[i] and nowhere else
+    rng = np.random.default_rng(41)
+    lat = to_bf16_bits(rng.standard_normal((3, 512)).astype(np.float32))
+    key = to_bf16_bits(rng.standard_normal((3, 128)).astype(np.float32))
+    slots = np.array([5, 0, 9])
+    c = oracle.Cache(64)
+    oracle.fp4_cache_write(c, lat, key, slots)
+    mc, ms = oracle.quant_nv16(lat.reshape(3, 32, 16))
+    kc, ks = oracle.quant_mx32(key.reshape(3, 4, 32))
+    mc = mc.reshape(3, 512).astype(np.int64)
+    kc = kc.reshape(3, 128).astype(np.int64)
+    for i, s in enumerate(slots):
+        assert [int(b) for b in c.main_codes[s]] == [int(mc[i, 2 * k] + 16 * mc[i, 2 * k + 1]) for k in range(256)]
+        assert [int(b) for b in c.idx_codes[s]] == [int(kc[i, 2 * k] + 16 * kc[i, 2 * k + 1]) for k in range(64)]
+        assert np.array_equal(c.main_scales[s], ms[i]) and np.array_equal(c.idx_scales[s], ks[i])
+    untouched = np.setdiff1d(np.arange(64), slots)
+    assert not c.main_codes[untouched].any() and not c.idx_scales[untouched].any()
+
+
 def _deq_idx_rows(c, slots):
     codes = np.stack([c.idx_codes[slots] & 15, c.idx_codes[slots] >> 4], axis=-1).reshape(len(slots), 128)
     sc = 2.0 ** (np.repeat(c.idx_scales[slots].astype(np.float64), 32, axis=1) - 127)

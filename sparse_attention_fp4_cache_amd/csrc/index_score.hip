@@ -34,7 +34,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kMaxSpread = 12;   // exponent-sum span accepted on the MFMA path
 constexpr int kMinExpSum = 130;  // keeps every nonzero dot >= 2^-126 (fp32 normal)
 constexpr int kMaxExpSum = 360;  // keeps every dot far below fp32 overflow
-constexpr int kMaxPagesPerWave = 16;  // pages (of 64 entries) one wavefront scans
+constexpr int kMaxPagesPerWave = 4;  // pages (of 64 entries) one wavefront scans, all prefetched
+constexpr int kWaves = 8;             // wavefronts per workgroup (they share one query staging)
+constexpr int kThreads = 64 * kWaves;
 
 // per-query staging record in LDS, for Hi = 16*MT heads
 template <int MT>
@@ -42,11 +44,9 @@ struct QStage {
   uint4 codes[MT][64];            // A operand of M-tile mt for lane l
   uint32_t scale[(MT + 3) / 4][64];  // byte (mt%4) of word mt/4: E8M0 of lane l in tile mt
   uint8_t u[16 * MT][4];          // E8M0 of head h, block b (plain order, exact path)
-  float w[16 * MT];
+  uint32_t stat[MT];  // heads of M-tile mt: largest block-exponent span | min u << 8 | max u << 16
   int row;
   int nvis;
-  int ok_spread;  // largest per-head block-exponent span of the query
-  int umin, umax;  // smallest / largest block exponent of the query
 };
 
 // Head held by row rho of M-tile mt: lane group rho/4 owns heads [(rho/4)*4MT, +4MT).
@@ -58,15 +58,21 @@ CSA2_DEV int head_of(int mt, int rho) { return (rho >> 2) * 4 * MT + 4 * mt + (r
 // round-to-nearest-even(x / X) with saturation and a copied sign bit, which is the
 // element rule exactly (checked on gfx950 against every bf16 value); blocks whose
 // shared exponent is near the ends of the range take the compare-based rule.
-CSA2_DEV void mx32_block(const uint16_t* __restrict__ src, uint4& out, uint32_t& u_out) {
+struct QRaw {
+  uint4 v[4];  // 32 bf16 values of one block
+};
+CSA2_DEV void mx32_load(const uint16_t* __restrict__ src, QRaw& r) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.v[i] = reinterpret_cast<const uint4*>(src)[i];
+}
+CSA2_DEV void mx32_block(const QRaw& r, uint4& out, uint32_t& u_out) {
   uint32_t raw[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint4 t = reinterpret_cast<const uint4*>(src)[i];
-    raw[4 * i] = t.x;
-    raw[4 * i + 1] = t.y;
-    raw[4 * i + 2] = t.z;
-    raw[4 * i + 3] = t.w;
+    raw[4 * i] = r.v[i].x;
+    raw[4 * i + 1] = r.v[i].y;
+    raw[4 * i + 2] = r.v[i].z;
+    raw[4 * i + 3] = r.v[i].w;
   }
   uint32_t amax_bits = 0;  // |x| as bf16 bits orders like the value
 #pragma unroll
@@ -77,18 +83,24 @@ CSA2_DEV void mx32_block(const uint16_t* __restrict__ src, uint4& out, uint32_t&
   const uint32_t u = mx_exponent(bf16_to_f32(amax_bits));
   const float X = ldexpf(1.0f, (int)u - 127);
   uint32_t word[4] = {0u, 0u, 0u, 0u};
-  if (u >= 4u && u <= 250u) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {  // element pair (2i, 2i+1) -> byte i
-      const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, bf16_to_f32(raw[i] & 0xFFFFu),
-                                                                   __uint_as_float(raw[i] & 0xFFFF0000u), X, 0);
-      word[i >> 2] |= (c & 0xFFu) << (8 * (i & 3));
-    }
-  } else {
+  for (int i = 0; i < 16; ++i) {  // element pair (2i, 2i+1) -> byte i
+    const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, bf16_to_f32(raw[i] & 0xFFFFu),
+                                                                 __uint_as_float(raw[i] & 0xFFFF0000u), X, 0);
+    word[i >> 2] |= (c & 0xFFu) << (8 * (i & 3));
+  }
+  const bool edge = u < 4u || u > 250u;
+  // a real (wave-uniform) branch: the compare-based rule only runs when some lane
+  // of the wavefront has a block exponent near the ends of the range
+  if (__builtin_amdgcn_ballot_w64(edge) != 0ull) {
+    if (edge) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      uint32_t c = e2m1_code(bf16_to_f32(raw[i] & 0xFFFFu), X) | (e2m1_code(bf16_to_f32(raw[i] >> 16), X) << 4);
-      word[i >> 2] |= c << (8 * (i & 3));
+      for (int k = 0; k < 4; ++k) word[k] = 0u;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        uint32_t c = e2m1_code(bf16_to_f32(raw[i] & 0xFFFFu), X) | (e2m1_code(bf16_to_f32(raw[i] >> 16), X) << 4);
+        word[i >> 2] |= c << (8 * (i & 3));
+      }
     }
   }
   out = make_uint4(word[0], word[1], word[2], word[3]);
@@ -142,159 +154,264 @@ struct KeyTile {
   uint32_t own;     // the 4 E8M0 bytes of entry `lane` of the page
 };
 
+// One page of keys: a wavefront-uniform page base plus fixed 32-bit lane offsets,
+// so every load takes the scalar-base + vector-offset form.
 CSA2_DEV void load_keys(KeyTile& t, const uint8_t* __restrict__ idx_codes, const uint8_t* __restrict__ idx_scales,
-                        int64_t slot0, int lane) {
-  const int g = lane >> 4, n = lane & 15;
+                        int page, int lane) {
+  const int64_t slot0 = (int64_t)__builtin_amdgcn_readfirstlane(page) * kPage;  // uniform
+  const uint32_t g = (uint32_t)lane >> 4, n = (uint32_t)lane & 15u;
+  const uint8_t* __restrict__ cb = idx_codes + slot0 * kIdxRowBytes;
+  const uint8_t* __restrict__ sb = idx_scales + slot0 * kIdxScaleBytes;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int64_t s = slot0 + 16 * nt + n;
-    t.codes[nt] = *reinterpret_cast<const uint4*>(idx_codes + s * kIdxRowBytes + 16 * g);
-    t.sc[nt] = idx_scales[s * kIdxScaleBytes + g];
+  for (uint32_t nt = 0; nt < 4; ++nt) {
+    const uint32_t e = 16u * nt + n;
+    t.codes[nt] = *reinterpret_cast<const uint4*>(cb + (e * (uint32_t)kIdxRowBytes + 16u * g));
+    t.sc[nt] = sb[e * (uint32_t)kIdxScaleBytes + g];
   }
-  t.own = *reinterpret_cast<const uint32_t*>(idx_scales + (slot0 + lane) * kIdxScaleBytes);
+  t.own = *reinterpret_cast<const uint32_t*>(sb + (uint32_t)lane * kIdxScaleBytes);
+  // issue order = use order: the tile is waited for as a unit, oldest first
+  __builtin_amdgcn_sched_barrier(0);
 }
 
+// Scores of one page for one query of the tile: 64 entries starting at logical entry
+// G * 64 of the query's sequence, whose keys are in `cur` (physical first slot slot0).
+// Returns whether this lane's entry lies outside the window where the MFMA result is
+// exact; the caller then recomputes it with exact_entry() after the page loop.
 template <int MT>
-__global__ __launch_bounds__(256) void index_score_kernel(const uint8_t* __restrict__ idx_codes,
+CSA2_DEV bool score_page(const QStage<MT>& s, const KeyTile& cur, int G, const float* __restrict__ wq,
+                         float* __restrict__ srow, int lane) {
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  int q_span = 0, q_umin = 255, q_umax = 0;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const uint32_t sv = s.stat[mt];
+    q_span = max(q_span, (int)(sv & 0xFFu));
+    q_umin = min(q_umin, (int)((sv >> 8) & 0xFFu));
+    q_umax = max(q_umax, (int)((sv >> 16) & 0xFFu));
+  }
+  // 16x16 complete dots per MFMA: d[mt][nt][r] = d(head(mt, 4*(lane/16)+r), entry 16nt + lane%16)
+  float d[MT][4][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const uint4 qa = s.codes[mt][lane];
+    const v8i a = {(int)qa.x, (int)qa.y, (int)qa.z, (int)qa.w, 0, 0, 0, 0};
+    const int asc = (int)s.scale[mt >> 2][lane];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const v8i b = {(int)cur.codes[nt].x, (int)cur.codes[nt].y, (int)cur.codes[nt].z, (int)cur.codes[nt].w,
+                     0, 0, 0, 0};
+      v4f acc;
+      switch (mt & 3) {
+        case 0: acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, 0, asc, 0, (int)cur.sc[nt]); break;
+        case 1: acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, 1, asc, 0, (int)cur.sc[nt]); break;
+        case 2: acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, 2, asc, 0, (int)cur.sc[nt]); break;
+        default: acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, 3, asc, 0, (int)cur.sc[nt]); break;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) d[mt][nt][r] = acc[r];
+    }
+  }
+  // lane L <- entry L of the page, register (b, mt, r) <- head b*4MT + 4mt + r
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) transpose4(d[mt][0][r], d[mt][1][r], d[mt][2][r], d[mt][3][r]);
+
+  const int j = G * kPage + lane;
+  const uint32_t own = cur.own;
+  int kmin = 255, kmax = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int u = (int)((own >> (8 * b)) & 0xFFu);
+    kmin = u < kmin ? u : kmin;
+    kmax = u > kmax ? u : kmax;
+  }
+  const bool visible = j < s.nvis;
+  const bool exact_needed = visible & (((kmax - kmin) + q_span > kMaxSpread) | (q_umin + kmin < kMinExpSum) |
+                                       (q_umax + kmax > kMaxExpSum));
+  float acc = 0.0f;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc = fmaf(wq[b * 4 * MT + 4 * mt + r], relu(d[mt][b][r]), acc);
+  if (visible) srow[j] = acc;
+  return exact_needed;
+}
+
+// The definition itself for one entry (integer block sums, one rounding per head,
+// the fma chain), for the rare entries flagged by score_page.
+template <int MT>
+CSA2_DEV void exact_entry(const QStage<MT>& s, const uint8_t* __restrict__ idx_codes,
+                          const uint8_t* __restrict__ idx_scales, int64_t slot, const float* __restrict__ wq,
+                          float* __restrict__ dst) {
+  constexpr int HI = 16 * MT;
+  const uint8_t* krow = idx_codes + slot * kIdxRowBytes;
+  const uint32_t own = *reinterpret_cast<const uint32_t*>(idx_scales + slot * kIdxScaleBytes);
+  float acc = 0.0f;
+  for (int h = 0; h < HI; ++h) acc = fmaf(wq[h], relu(exact_dot<MT>(s, h, krow, own)), acc);
+  *dst = acc;
+}
+
+template <int MT, int QT>
+__global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __restrict__ idx_codes,
                                                           const uint8_t* __restrict__ idx_scales,
                                                           const uint16_t* __restrict__ q_idx,
                                                           const float* __restrict__ w,
                                                           const int32_t* __restrict__ seq_of_query,
                                                           const int32_t* __restrict__ n_visible,
                                                           const int32_t* __restrict__ block_table, int max_pages,
-                                                          int nq, float* __restrict__ scores, int64_t ld, int qt,
+                                                          int nq, float* __restrict__ scores, int64_t ld,
                                                           int groups_per_wave, int total_groups) {
+  constexpr int qt = QT;  // queries per workgroup
   constexpr int HI = 16 * MT;
   extern __shared__ __align__(16) unsigned char smem[];
   QStage<MT>* st = reinterpret_cast<QStage<MT>*>(smem);
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wavefront
   const int q0 = blockIdx.y * qt;
-  const int gfirst = (blockIdx.x * 4 + wid) * groups_per_wave;
+  const int gfirst = (blockIdx.x * kWaves + wid) * groups_per_wave;
   const int gend = min(gfirst + groups_per_wave, total_groups);
   const int first_row = (q0 < nq) ? (seq_of_query ? seq_of_query[q0] : q0) : 0;
 
-  // ---- physical pages of this wavefront (one table read), and the first two pages
-  // of keys in flight while the queries are staged
-  int pages[kMaxPagesPerWave];
-#pragma unroll
-  for (int i = 0; i < kMaxPagesPerWave; ++i)
-    pages[i] = (gfirst + i < gend) ? block_table[(int64_t)first_row * max_pages + gfirst + i] : 0;
-  KeyTile t0, t1, t2;
-  int cur_row = first_row;
-  if (gfirst < gend) load_keys(t0, idx_codes, idx_scales, (int64_t)pages[0] * kPage, lane);
-  if (gfirst + 1 < gend) load_keys(t1, idx_codes, idx_scales, (int64_t)pages[1] * kPage, lane);
-
-  // ---- stage the tile's queries: MXFP4 operands, scales, weights
-  for (int item = tid; item < qt * MT * 64; item += 256) {
+  // ---- physical pages of this wavefront (uniform table reads), the raw query
+  // blocks this thread stages, then the first two pages of keys: all in flight
+  // together before any of them is used
+  const int items = qt * MT * 64;
+  // the staging item of this thread, (query, M-tile, lane) -> source block
+  auto item_src = [&](int item, const uint16_t*& src) {
     const int qi = item / (MT * 64), rem = item % (MT * 64), mt = rem >> 6, l = rem & 63;
-    const int g = l >> 4, rho = l & 15, h = head_of<MT>(mt, rho), q = q0 + qi;
+    const int q = q0 + qi;
+    src = q_idx + ((int64_t)q * HI + head_of<MT>(mt, l & 15)) * kIndexDim + 32 * (l >> 4);
+    return item < items && q < nq;
+  };
+  // per-query row and visible count (threads tid < qt)
+  int my_row = 0, my_nvis = 0;
+  if (tid < qt && q0 + tid < nq) {
+    my_row = seq_of_query ? seq_of_query[q0 + tid] : q0 + tid;
+    my_nvis = n_visible[q0 + tid];
+  }
+  QRaw qraw;  // the first round of staging loads goes out before the key loads
+  {
+    const uint16_t* src;
+    const bool ok = item_src(tid, src);
+    mx32_load(ok ? src : q_idx, qraw);  // unconditional (a spare thread reads block 0)
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the key loads
+  // physical page of the wavefront's k-th page (a uniform scalar read each time:
+  // an indexed register array would make every later wait conservative)
+  const int32_t* __restrict__ bt_row = block_table + (int64_t)first_row * max_pages + gfirst;
+  const int npg_all = max(min(gend - gfirst, kMaxPagesPerWave), 1);
+  auto page_of = [&](int k) { return gfirst < gend ? bt_row[min(k, npg_all - 1)] : 0; };
+
+  // the wavefront's first four pages, unconditionally (past its last page -- or
+  // with no page at all -- it re-reads a valid page and ignores the data)
+  KeyTile t0, t1, t2, t3;
+  // the four page numbers are read now.  Wavefronts that stage query blocks request
+  // their pages after the staging, so the staging's query loads do not queue behind
+  // the key burst; the others request theirs at once.
+  const int pg0 = page_of(0), pg1 = page_of(1), pg2 = page_of(2), pg3 = page_of(3);
+  const bool stager = wid * 64 < items;  // uniform
+  auto request_pages = [&]() {
+    load_keys(t0, idx_codes, idx_scales, pg0, lane);
+    load_keys(t1, idx_codes, idx_scales, pg1, lane);
+    load_keys(t2, idx_codes, idx_scales, pg2, lane);
+    load_keys(t3, idx_codes, idx_scales, pg3, lane);
+  };
+  if (!stager) request_pages();
+
+  // ---- stage the tile's queries: MXFP4 operands and scales.  Item = (query,
+  // M-tile, lane); the 64 items of one (query, M-tile) are one wavefront, whose lanes
+  // l, l^16, l^32, l^48 hold the four blocks of one head.
+  for (int item0 = 0; item0 < items; item0 += kThreads) {
+    const int item = item0 + tid;
+    const int qi = item / (MT * 64), rem = item % (MT * 64), mt = rem >> 6, l = rem & 63;
+    const int g = l >> 4, rho = l & 15, h = head_of<MT>(mt, rho);
     uint4 codes = make_uint4(0, 0, 0, 0);
     uint32_t u = 127;
-    if (q < nq) mx32_block(q_idx + ((int64_t)q * HI + h) * kIndexDim + 32 * g, codes, u);
-    st[qi].codes[mt][l] = codes;
-    st[qi].u[h][g] = (uint8_t)u;
-    reinterpret_cast<uint8_t*>(&st[qi].scale[mt >> 2][l])[mt & 3] = (uint8_t)u;
-  }
-  for (int item = tid; item < qt * HI; item += 256) {
-    const int qi = item / HI, h = item % HI, q = q0 + qi;
-    st[qi].w[h] = (q < nq) ? w[(int64_t)q * HI + h] : 0.0f;
+    const uint16_t* src;
+    if (item_src(item, src)) {
+      if (item0 > 0) mx32_load(src, qraw);
+      mx32_block(qraw, codes, u);
+    }
+    int lo = (int)u, hi = (int)u;  // over the head's four blocks
+    lo = min(lo, __shfl_xor(lo, 16));
+    hi = max(hi, __shfl_xor(hi, 16));
+    lo = min(lo, __shfl_xor(lo, 32));
+    hi = max(hi, __shfl_xor(hi, 32));
+    int span = hi - lo;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {  // over the wavefront's 16 heads
+      span = max(span, __shfl_xor(span, o));
+      lo = min(lo, __shfl_xor(lo, o));
+      hi = max(hi, __shfl_xor(hi, o));
+    }
+    if (item < items) {
+      st[qi].codes[mt][l] = codes;
+      st[qi].u[h][g] = (uint8_t)u;
+      reinterpret_cast<uint8_t*>(&st[qi].scale[mt >> 2][l])[mt & 3] = (uint8_t)u;
+      if (l == 0) st[qi].stat[mt] = (uint32_t)span | ((uint32_t)lo << 8) | ((uint32_t)hi << 16);
+    }
   }
   if (tid < qt) {
-    const int q = q0 + tid;
-    st[tid].row = (q < nq) ? (seq_of_query ? seq_of_query[q] : q) : 0;
-    st[tid].nvis = (q < nq) ? n_visible[q] : 0;
-    st[tid].ok_spread = 0;  // largest per-head span until the reduction below is done
-    st[tid].umin = 255;
-    st[tid].umax = 0;
+    st[tid].row = my_row;
+    st[tid].nvis = my_nvis;
   }
-  lds_barrier();
-  for (int item = tid; item < qt * HI; item += 256) {  // per-head block-exponent span
-    const int qi = item / HI, h = item % HI;
-    int lo = 255, hi = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int u = st[qi].u[h][b];
-      lo = u < lo ? u : lo;
-      hi = u > hi ? u : hi;
-    }
-    atomicMax(&st[qi].ok_spread, hi - lo);
-    atomicMin(&st[qi].umin, lo);
-    atomicMax(&st[qi].umax, hi);
-  }
+  if (stager) request_pages();
   lds_barrier();
   if (gfirst >= gend) return;
-  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int npg = gend - gfirst;
+  bool same_row = true;  // every query of the tile reads the first query's sequence
+  for (int qi = 1; qi < qt; ++qi) same_row &= (q0 + qi >= nq) || (st[qi].row == first_row);
 
-#pragma unroll 1
-  for (int i = 0; gfirst + i < gend; ++i) {
+  // entries needing the exact path: bit (i * qt + qi) for page i, query qi
+  unsigned long long exact_bits = 0ull;
+  // all queries of the tile on one page whose keys are in t
+  auto page_all = [&](const KeyTile& t, int i) {
     const int G = gfirst + i;
-    if (G + 2 < gend)  // two pages ahead stay in flight
-      load_keys(t2, idx_codes, idx_scales, (int64_t)pages[(i + 2) & (kMaxPagesPerWave - 1)] * kPage, lane);
-    KeyTile& cur = t0;
+#pragma unroll 1
     for (int qi = 0; qi < qt; ++qi) {
-      const QStage<MT>& s = st[qi];
-      if (G * kPage >= s.nvis) continue;  // uniform
-      if (s.row != cur_row) {  // a query of another sequence in this tile: load its page
-        load_keys(cur, idx_codes, idx_scales, (int64_t)block_table[(int64_t)s.row * max_pages + G] * kPage, lane);
-        cur_row = s.row;
-      }
-      // 16x16 complete dots per MFMA: d[mt][nt][r] = d(head(mt, 4*(lane/16)+r), entry 16nt + lane%16)
-      float d[MT][4][4];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const uint4 qa = s.codes[mt][lane];
-        const v8i a = {(int)qa.x, (int)qa.y, (int)qa.z, (int)qa.w, 0, 0, 0, 0};
-        const int asc = (int)s.scale[mt >> 2][lane];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const v8i b = {(int)cur.codes[nt].x, (int)cur.codes[nt].y, (int)cur.codes[nt].z, (int)cur.codes[nt].w,
-                         0, 0, 0, 0};
-          v4f acc;
-          switch (mt & 3) {
-            case 0: acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, 0, asc, 0, (int)cur.sc[nt]); break;
-            case 1: acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, 1, asc, 0, (int)cur.sc[nt]); break;
-            case 2: acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, 2, asc, 0, (int)cur.sc[nt]); break;
-            default: acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, 3, asc, 0, (int)cur.sc[nt]); break;
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) d[mt][nt][r] = acc[r];
-        }
-      }
-      // lane L <- entry L of the page, register (b, mt, r) <- head b*4MT + 4mt + r
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) transpose4(d[mt][0][r], d[mt][1][r], d[mt][2][r], d[mt][3][r]);
-
-      const int j = G * kPage + lane;
-      const uint32_t own = cur.own;
-      int kmin = 255, kmax = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int u = (int)((own >> (8 * b)) & 0xFFu);
-        kmin = u < kmin ? u : kmin;
-        kmax = u > kmax ? u : kmax;
-      }
-      const bool exact_needed = (j < s.nvis) & (((kmax - kmin) + s.ok_spread > kMaxSpread) |
-                                                (s.umin + kmin < kMinExpSum) | (s.umax + kmax > kMaxExpSum));
-      float acc = 0.0f;
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc = fmaf(s.w[b * 4 * MT + 4 * mt + r], relu(d[mt][b][r]), acc);
-      if (exact_needed) {  // rare: recompute this entry exactly
-        const int64_t slot = (int64_t)block_table[(int64_t)s.row * max_pages + G] * kPage + lane;
-        const uint8_t* krow = idx_codes + slot * kIdxRowBytes;
-        acc = 0.0f;
-        for (int h = 0; h < HI; ++h) acc = fmaf(s.w[h], relu(exact_dot<MT>(s, h, krow, own)), acc);
-      }
-      if (j < s.nvis) scores[(int64_t)(q0 + qi) * ld + j] = acc;
+      const QStage<MT>& sq = st[qi];
+      if (G * kPage >= sq.nvis) continue;  // uniform
+      const bool ex = score_page<MT>(sq, t, G, w + (int64_t)(q0 + qi) * HI, scores + (int64_t)(q0 + qi) * ld,
+                                     lane);
+      exact_bits |= (unsigned long long)ex << (i * qt + qi);
     }
-    t0 = t1;  // t1 and t2 always hold this wavefront's own (first-row) pages
-    t1 = t2;
-    cur_row = first_row;
+  };
+
+  if (same_row) {
+    // the wavefront's (at most four) pages, all requested in the prologue, in
+    // straight-line code: the wait for page k leaves pages k+1.. in flight (a loop
+    // here would make the compiler wait for every outstanding load at its head)
+    page_all(t0, 0);
+    if (npg > 1) page_all(t1, 1);
+    if (npg > 2) page_all(t2, 2);
+    if (npg > 3) page_all(t3, 3);
+    // rare: entries whose blocks fall outside the exact window of the MFMA
+    while (exact_bits != 0ull) {
+      const int b = __builtin_ctzll(exact_bits);
+      exact_bits &= exact_bits - 1;
+      const int i = b / qt, qi = b % qt;
+      exact_entry<MT>(st[qi], idx_codes, idx_scales, (int64_t)page_of(i) * kPage + lane, w + (int64_t)(q0 + qi) * HI,
+                      scores + (int64_t)(q0 + qi) * ld + (int64_t)(gfirst + i) * kPage + lane);
+    }
+  } else {
+    // queries of several sequences share the tile: each query reads its own pages
+    for (int i = 0; i < npg; ++i) {
+      const int G = gfirst + i;
+      for (int qi = 0; qi < qt; ++qi) {
+        const QStage<MT>& sq = st[qi];
+        if (G * kPage >= sq.nvis) continue;  // uniform
+        const int page = block_table[(int64_t)sq.row * max_pages + G];
+        const int64_t slot0 = (int64_t)page * kPage;
+        KeyTile t;
+        load_keys(t, idx_codes, idx_scales, page, lane);
+        if (score_page<MT>(sq, t, G, w + (int64_t)(q0 + qi) * HI, scores + (int64_t)(q0 + qi) * ld, lane))
+          exact_entry<MT>(sq, idx_codes, idx_scales, slot0 + lane, w + (int64_t)(q0 + qi) * HI,
+                          scores + (int64_t)(q0 + qi) * ld + (int64_t)G * kPage + lane);
+      }
+    }
   }
 }
 
@@ -304,19 +421,28 @@ static int launch_mt(const csa2_fp4_cache* c, const uint16_t* q_idx, const float
                      hipStream_t stream) {
   const int total_groups = (int)ceil_div(ld, kPage);
   if (total_groups == 0 || nq == 0) return CSA2_OK;
-  // queries per workgroup: share each loaded page among several queries when there are many
-  int qt = nq >= 64 ? 8 : 1;
-  while (qt > 1 && sizeof(QStage<MT>) * qt > 48 * 1024) qt >>= 1;
+  // queries per workgroup: several queries of one sequence share each loaded page
+  // (queries without a sequence map each read their own pages)
+  // (queries without a sequence map each read their own pages); the staged queries
+  // stay within 64 KB of LDS
+  const int qt = (soq == nullptr || nq < 64) ? 1 : (sizeof(QStage<MT>) * 8 <= 64 * 1024 ? 8 : 4);
   // pages per wavefront: enough wavefronts to cover the chip about twice
   const long long qtiles = ceil_div(nq, qt);
   const long long want_waves = qtiles >= 512 ? 4 * qtiles : 2048;
   int gpw = (int)ceil_div(total_groups * qtiles, want_waves);
   if (gpw < 1) gpw = 1;
   if (gpw > kMaxPagesPerWave) gpw = kMaxPagesPerWave;
-  const unsigned gx = ceil_div(total_groups, 4LL * gpw);
+  const unsigned gx = ceil_div(total_groups, (long long)kWaves * gpw);
   const size_t lds = sizeof(QStage<MT>) * qt;
-  hipLaunchKernelGGL(index_score_kernel<MT>, dim3(gx, (unsigned)qtiles), dim3(256), lds, stream, c->idx_codes,
-                     c->idx_scales, q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, qt, gpw, total_groups);
+  if (qt == 8)
+    hipLaunchKernelGGL((index_score_kernel<MT, 8>), dim3(gx, (unsigned)qtiles), dim3(kThreads), lds, stream, c->idx_codes,
+                       c->idx_scales, q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups);
+  else if (qt == 4)
+    hipLaunchKernelGGL((index_score_kernel<MT, 4>), dim3(gx, (unsigned)qtiles), dim3(kThreads), lds, stream, c->idx_codes,
+                       c->idx_scales, q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups);
+  else
+    hipLaunchKernelGGL((index_score_kernel<MT, 1>), dim3(gx, (unsigned)qtiles), dim3(kThreads), lds, stream, c->idx_codes,
+                       c->idx_scales, q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups);
   return launch_status();
 }
 

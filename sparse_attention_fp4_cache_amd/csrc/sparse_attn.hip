@@ -8,9 +8,10 @@
 // mean of the values); "La lignée DeepSeek" (one latent vector shared by all heads,
 // so every entry and window row is both key and value for all heads).
 //
-// Work decomposition.  A workgroup (4 wavefronts) owns one query, 16 heads and a
-// contiguous range of candidate rows (selected entries first, then window rows),
-// which it walks in tiles of 32 rows with an online softmax:
+// Work decomposition.  A workgroup (8 wavefronts, two halves of 4) owns one query,
+// 16 heads and a contiguous range of candidate rows (selected entries first, then
+// window rows).  The two halves walk alternate tiles of 32 rows at the same time,
+// each with its own LDS tile and online softmax, and combine their states at the end:
 //   gather   : 256 threads dequantise the tile into LDS twice, row-major X[32][512]
 //              and transposed XT[512][32] (bf16; E2M1 x E4M3 has at most 6
 //              significant bits in [2^-10, 2688], so the bf16 value is exact).  The
@@ -27,6 +28,8 @@
 //              part and a bf16 remainder so P keeps ~16 significant bits.
 // With several row ranges per query the unnormalised partial (O, m, l) goes to the
 // workspace and a merge kernel combines the ranges with their log-sum-exp weights.
+// Both halves run the same number of tile steps (a half past the end of the range
+// computes an empty tile), so every workgroup barrier is reached by all wavefronts.
 #include "common.hpp"
 #include "host_common.hpp"
 
@@ -66,13 +69,20 @@ struct AttnArgs {
 };
 
 constexpr int kSeg = 512;  // rows whose sources are resolved into LDS at a time
+constexpr int kThreads = 512;  // two halves of 4 wavefronts
 
-struct __align__(16) AttnSmem {
+struct __align__(16) HalfSmem {
   uint16_t x[kRT * kXStride];    // X[row][ch]
   uint16_t xt[512 * kXTStride];  // XT[ch][row]
   float red[4][2][4][64];        // partial logits [wave][mtile][r][lane]
-  int src[kSeg];                 // row source: slot >= 0, window row -2-r, or -1 (none)
 };
+struct __align__(16) AttnSmem {
+  HalfSmem h[2];
+  int src[kSeg];  // row source: slot >= 0, window row -2-r, or -1 (none)
+};
+static_assert(sizeof(AttnSmem) <= 160 * 1024, "attention LDS exceeds 160 KB");
+// the second half's tile area holds its softmax state for the final combine
+static_assert(sizeof(float4) * 4 * 8 * 64 + sizeof(float) * 2 * 4 * 64 <= sizeof(HalfSmem), "combine area");
 
 CSA2_DEV uint32_t pack_bf16_hi(float lo, float hi) {  // exact values only (low 16 bits zero)
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
@@ -95,13 +105,13 @@ struct TileRegs {
   uint32_t wmask[8];  // all ones for a window row
 };
 
-CSA2_DEV void issue_tile(const AttnArgs& a, const AttnSmem& sm, int tile_row0, int r_local_end, TileRegs& t) {
-  const int tid = threadIdx.x;
+CSA2_DEV void issue_tile(const AttnArgs& a, const int* src_rows, int tid, int tile_row0, int r_local_end,
+                         TileRegs& t) {
   const int rg = tid & 3, cb = tid >> 2;
 #pragma unroll
   for (int rr = 0; rr < 8; ++rr) {
     const int rl = tile_row0 + 8 * rg + rr;  // row index local to this segment
-    const int src = (rl < r_local_end) ? sm.src[rl] : -1;
+    const int src = (rl < r_local_end) ? src_rows[rl] : -1;
     t.mmask[rr] = src >= 0 ? ~0u : 0u;
     t.wmask[rr] = src <= -2 ? ~0u : 0u;
     const int64_t slot = src >= 0 ? src : 0;
@@ -112,7 +122,7 @@ CSA2_DEV void issue_tile(const AttnArgs& a, const AttnSmem& sm, int tile_row0, i
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
       const int rl = tile_row0 + 8 * rg + rr;
-      const int src = (rl < r_local_end) ? sm.src[rl] : -1;
+      const int src = (rl < r_local_end) ? src_rows[rl] : -1;
       const int64_t wrow = src <= -2 ? (int64_t)(-2 - src) : 0;
       t.win[rr] = *reinterpret_cast<const uint4*>(a.swa + wrow * kLatentDim + 8 * cb);
     }
@@ -126,8 +136,7 @@ CSA2_DEV void issue_tile(const AttnArgs& a, const AttnSmem& sm, int tile_row0, i
 // Branch-free: E4M3 scale via V_CVT_F32_FP8 (OCP E4M3FN on gfx950), E2M1 pairs via
 // V_CVT_SCALEF32_PK_F32_FP4 with a unit scale, product exact in fp32 and in bf16.
 // XT rows are written as 16-byte runs of 8 consecutive tile rows.
-CSA2_DEV void store_tile(AttnSmem& sm, const TileRegs& t) {
-  const int tid = threadIdx.x;
+CSA2_DEV void store_tile(HalfSmem& sm, int tid, const TileRegs& t) {
   const int rg = tid & 3, cb = tid >> 2;
   uint32_t w[8][4];
 #pragma unroll
@@ -168,9 +177,11 @@ CSA2_DEV bf16x8 as_bf16x8(uint4 v) {
   return r;
 }
 
-__global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
-  __shared__ AttnSmem sm;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+__global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a) {
+  __shared__ AttnSmem smem;
+  const int half = threadIdx.x >> 8;
+  const int tid = threadIdx.x & 255, lane = tid & 63, wid = tid >> 6;  // within the half
+  HalfSmem& sm = smem.h[half];
   const int g = lane >> 4, n16 = lane & 15;
   const int hg = blockIdx.y;          // head group of 16
   const int qrow = blockIdx.z;        // query
@@ -198,7 +209,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
   const int seg_n = min(kSeg, nrows - seg0);
   lds_barrier();  // the previous segment's sources are no longer read
   // where every row of this segment comes from (one round of index loads)
-  for (int rl = tid; rl < seg_n; rl += 256) {
+  for (int rl = (int)threadIdx.x; rl < seg_n; rl += kThreads) {
     const int r = r_begin + seg0 + rl;
     int src = -1;
     if (r < a.k) {
@@ -212,15 +223,16 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
         src = -2 - (qrow * a.window + wr);
       }
     }
-    sm.src[rl] = src;
+    smem.src[rl] = src;
   }
   lds_barrier();
   TileRegs cur;
-  issue_tile(a, sm, 0, seg_n, cur);
-  for (int row0 = 0; row0 < seg_n; row0 += kRT) {
+  issue_tile(a, smem.src, tid, half * kRT, seg_n, cur);
+  for (int pair0 = 0; pair0 < seg_n; pair0 += 2 * kRT) {
+    const int row0 = pair0 + half * kRT;  // may lie past seg_n: an empty tile
     lds_barrier();  // previous tile fully consumed
-    store_tile(sm, cur);
-    if (row0 + kRT < seg_n) issue_tile(a, sm, row0 + kRT, seg_n, cur);  // next tile in flight
+    store_tile(sm, tid, cur);
+    if (row0 + 2 * kRT < seg_n) issue_tile(a, smem.src, tid, row0 + 2 * kRT, seg_n, cur);  // next tile in flight
     lds_barrier();
     // ---- partial logits over this wavefront's 128 channels, two 16-row M-tiles
     v4f s[2];
@@ -248,7 +260,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
       for (int r = 0; r < 4; ++r) {
         const float v = ((sm.red[0][t][r][lane] + sm.red[1][t][r][lane]) + sm.red[2][t][r][lane]) + sm.red[3][t][r][lane];
         const int rl = row0 + 8 * g + 4 * t + r;
-        const bool valid = (rl < seg_n) & (sm.src[rl & (kSeg - 1)] != -1);  // no short-circuit branch
+        const bool valid = (rl < seg_n) & (smem.src[rl & (kSeg - 1)] != -1);  // no short-circuit branch
         z[t][r] = valid ? v * a.scale_log2 : -INFINITY;
         tmax = fmaxf(tmax, z[t][r]);
       }
@@ -295,6 +307,34 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
 
   }  // segments
 
+  // ---- combine the halves: the second half parks (O, m, l) in its tile area, the
+  // first half rescales both to the larger running maximum and adds them
+  lds_barrier();  // every tile consumed
+  float4* park = reinterpret_cast<float4*>(smem.h[1].x);  // [wid][mt][lane]
+  float* park_ml = reinterpret_cast<float*>(park + 4 * 8 * 64);  // [2][wid][lane]
+  if (half == 1) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+      park[(wid * 8 + mt) * 64 + lane] = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+    park_ml[wid * 64 + lane] = m_run;
+    park_ml[256 + wid * 64 + lane] = l_run;
+  }
+  lds_barrier();
+  if (half == 1) return;
+  {
+    const float m1 = park_ml[wid * 64 + lane], l1 = park_ml[256 + wid * 64 + lane];
+    const float M = fmaxf(m_run, m1);
+    const float a0 = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - M);
+    const float a1 = (m1 == -INFINITY) ? 0.0f : exp2f(m1 - M);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const float4 o1 = park[(wid * 8 + mt) * 64 + lane];
+      acc[mt] = acc[mt] * a0 + v4f{o1.x, o1.y, o1.z, o1.w} * a1;
+    }
+    l_run = l_run * a0 + l1 * a1;
+    m_run = M;
+  }
+
   // ---- write: lane holds head `head`, channels 128*wid + 16*mt + 4*g + r
   if (a.nsplit == 1) {
     const float inv = (l_run > 0.0f) ? 1.0f / l_run : 0.0f;
@@ -319,9 +359,11 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(AttnArgs a) {
 }
 
 // Combine the row ranges of one (query, head): out = sum_s 2^(m_s-M) O_s / L.
-// 512 threads: four groups of 128 each sum a quarter of the ranges (all their loads
-// issued together), then the groups are added in a fixed order.
+// 512 threads: four groups of 128 each sum a quarter of the ranges in a fixed order,
+// then the groups are added in a fixed order.  The first batch of O_s loads is issued
+// before the weights are known, so the two rounds of loads overlap.
 constexpr int kMergeMaxSplits = 256;
+constexpr int kMergeBatch = 8;  // ranges per group per round of loads
 __global__ __launch_bounds__(512) void attn_merge_kernel(AttnArgs a) {
   __shared__ float wgt[kMergeMaxSplits];
   __shared__ float4 part[3][128];
@@ -329,6 +371,13 @@ __global__ __launch_bounds__(512) void attn_merge_kernel(AttnArgs a) {
   const int head = blockIdx.x, qrow = blockIdx.y, tid = threadIdx.x;
   const int grp = tid >> 7, t = tid & 127;
   const int64_t base = (int64_t)qrow * a.nsplit * a.H + head;  // + s * H
+  const float4* po = reinterpret_cast<const float4*>(a.part_o);
+  float4 v[kMergeBatch];
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u) {  // ranges grp, grp + 4, ... of the first round
+    const int s = grp + 4 * u;
+    v[u] = (s < a.nsplit) ? po[(base + (int64_t)s * a.H) * (kLatentDim / 4) + t] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   if (tid < 64) {
     float M = -INFINITY;
     for (int s = tid; s < a.nsplit; s += 64) M = fmaxf(M, a.part_ml[2 * (base + (int64_t)s * a.H)]);
@@ -349,22 +398,22 @@ __global__ __launch_bounds__(512) void attn_merge_kernel(AttnArgs a) {
   }
   __syncthreads();
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = grp; s0 < a.nsplit; s0 += 32) {
-    float4 v[8];
+  for (int s0 = grp;; s0 += 4 * kMergeBatch) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int s = s0 + 4 * u;
-      v[u] = (s < a.nsplit) ? reinterpret_cast<const float4*>(a.part_o + (base + (int64_t)s * a.H) * kLatentDim)[t]
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kMergeBatch; ++u) {
       const int s = s0 + 4 * u;
       const float w = (s < a.nsplit) ? wgt[s] : 0.0f;
       o.x += v[u].x * w;
       o.y += v[u].y * w;
       o.z += v[u].z * w;
       o.w += v[u].w * w;
+    }
+    const int s1 = s0 + 4 * kMergeBatch;
+    if (s1 >= a.nsplit) break;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int s = s1 + 4 * u;
+      v[u] = (s < a.nsplit) ? po[(base + (int64_t)s * a.H) * (kLatentDim / 4) + t] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
   if (grp > 0) part[grp - 1][t] = o;
@@ -391,7 +440,7 @@ static void plan_splits(int nq, int H, int k, int window, int* nsplit, int* rows
   const int total = k + window;
   const int tiles = (total + kRT - 1) / kRT;
   const long long groups = (long long)nq * (H / 16);
-  int want = (int)((512 + groups - 1) / groups);
+  int want = (int)((256 + groups - 1) / groups);  // one 512-thread workgroup per CU
   if (want < 1) want = 1;
   int tiles_per = (tiles + want - 1) / want;
   if (tiles_per < 2 && tiles >= 2) tiles_per = 2;
@@ -413,7 +462,7 @@ static int run_attention(AttnArgs a, void* ws, size_t ws_bytes, hipStream_t stre
     a.part_ml = a.part_o + (size_t)a.nq * a.nsplit * a.H * kLatentDim;
   }
   const dim3 grid((unsigned)a.nsplit, (unsigned)(a.H / 16), (unsigned)a.nq);
-  hipLaunchKernelGGL(sparse_attn_kernel, grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(sparse_attn_kernel, grid, dim3(kThreads), 0, stream, a);
   if (a.nsplit > 1)
     hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)a.H, (unsigned)a.nq), dim3(512), 0, stream, a);
   return launch_status();

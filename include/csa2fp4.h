@@ -124,13 +124,29 @@ int index_score(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float*
  *                          ascending index order, then -1 padding.
  *   ws, ws_bytes          : device workspace of at least
  *                          topk_select_workspace_size(nq, ld, k) bytes.  It must be
- *                          zero-filled before its first use; every call leaves it
- *                          zero-filled again (in stream order).  Calls sharing one
- *                          workspace must be stream-ordered.
+ *                          zero-filled before its first use; every call returns its
+ *                          counters and histograms to zero (in stream order), so the
+ *                          next call needs no clearing.  The rest of it is scratch
+ *                          that each call overwrites before reading.  Calls sharing
+ *                          one workspace must be stream-ordered.
  * Bit-exact and deterministic. */
 size_t topk_select_workspace_size(int32_t nq, int64_t ld, int32_t k);
 int topk_select(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq, int32_t k,
                 int32_t* topk_idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* index_topk -- index_score followed by topk_select on the same scores, as one call:
+ * the indexer stage of a Full or Reindex layer.
+ * Source: as for index_score and topk_select ("DeepSeek-V4.1-Flash, expliqué pas à
+ * pas", CSA2 section: the indexer scores every entry, then keeps the best ones).
+ * Arguments as for the two calls; ws / ws_bytes as for topk_select (same size, same
+ * zero-fill contract).  scores and topk_idx are bit-identical to calling index_score
+ * and then topk_select.  When every query reads its own sequence (seq_of_query NULL,
+ * or fewer than 64 queries) the selection's first counting pass is folded into the
+ * scoring pass, which saves one launch. */
+int index_topk(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
+               const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* block_table, int32_t max_pages,
+               int32_t nq, float* scores, int64_t ld, int32_t k, int32_t* topk_idx, void* ws, size_t ws_bytes,
+               hipStream_t stream);
 
 /* sparse_attn_decode -- one softmax over the selected cache entries and the window.
  * Source: "DeepSeek-V4.1-Flash, expliqué pas à pas", CSA2 section (the main query

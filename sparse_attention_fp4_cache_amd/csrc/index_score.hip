@@ -25,6 +25,7 @@
 // all Hi heads in ascending order, and the fma chain runs with all 64 lanes busy.
 #include "common.hpp"
 #include "host_common.hpp"
+#include "topk_internal.hpp"
 
 namespace csa2 {
 
@@ -177,9 +178,12 @@ CSA2_DEV void load_keys(KeyTile& t, const uint8_t* __restrict__ idx_codes, const
 // G * 64 of the query's sequence, whose keys are in `cur` (physical first slot slot0).
 // Returns whether this lane's entry lies outside the window where the MFMA result is
 // exact; the caller then recomputes it with exact_entry() after the page loop.
+// With lh (uniform), every score written (except those left to the exact path) is
+// also counted in the workgroup's digit-1 histogram lh of the selection that follows.
 template <int MT>
-CSA2_DEV bool score_page(const QStage<MT>& s, const KeyTile& cur, int G, const float* __restrict__ wq,
-                         float* __restrict__ srow, int lane) {
+__device__ __attribute__((always_inline)) inline bool score_page(const QStage<MT>& s, const KeyTile& cur, int G,
+                                                                 const float* __restrict__ wq,
+                                                                 float* __restrict__ srow, int lane, uint32_t* lh) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   int q_span = 0, q_umin = 255, q_umax = 0;
 #pragma unroll
@@ -237,24 +241,28 @@ CSA2_DEV bool score_page(const QStage<MT>& s, const KeyTile& cur, int G, const f
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc = fmaf(wq[b * 4 * MT + 4 * mt + r], relu(d[mt][b][r]), acc);
   if (visible) srow[j] = acc;
+  if (lh != nullptr && visible && !exact_needed) atomicAdd(&lh[score_key(acc) >> kTopkBinShift], 1u);
   return exact_needed;
 }
 
 // The definition itself for one entry (integer block sums, one rounding per head,
 // the fma chain), for the rare entries flagged by score_page.
 template <int MT>
-CSA2_DEV void exact_entry(const QStage<MT>& s, const uint8_t* __restrict__ idx_codes,
-                          const uint8_t* __restrict__ idx_scales, int64_t slot, const float* __restrict__ wq,
-                          float* __restrict__ dst) {
+CSA2_DEV float exact_entry(const QStage<MT>& s, const uint8_t* __restrict__ idx_codes,
+                           const uint8_t* __restrict__ idx_scales, int64_t slot, const float* __restrict__ wq,
+                           float* __restrict__ dst) {
   constexpr int HI = 16 * MT;
   const uint8_t* krow = idx_codes + slot * kIdxRowBytes;
   const uint32_t own = *reinterpret_cast<const uint32_t*>(idx_scales + slot * kIdxScaleBytes);
   float acc = 0.0f;
   for (int h = 0; h < HI; ++h) acc = fmaf(wq[h], relu(exact_dot<MT>(s, h, krow, own)), acc);
   *dst = acc;
+  return acc;
 }
 
-template <int MT, int QT>
+// HIST (one query per workgroup only): also fill the query's digit-1 histogram
+// hist[q][kTopkBins] of the selection that follows, when n_visible[q] > k.
+template <int MT, int QT, bool HIST>
 __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __restrict__ idx_codes,
                                                           const uint8_t* __restrict__ idx_scales,
                                                           const uint16_t* __restrict__ q_idx,
@@ -263,7 +271,9 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
                                                           const int32_t* __restrict__ n_visible,
                                                           const int32_t* __restrict__ block_table, int max_pages,
                                                           int nq, float* __restrict__ scores, int64_t ld,
-                                                          int groups_per_wave, int total_groups) {
+                                                          int groups_per_wave, int total_groups,
+                                                          uint32_t* __restrict__ hist, int k) {
+  static_assert(!HIST || QT == 1, "the fused histogram serves one query per workgroup");
   constexpr int qt = QT;  // queries per workgroup
   constexpr int HI = 16 * MT;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -358,9 +368,14 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
     st[tid].row = my_row;
     st[tid].nvis = my_nvis;
   }
+  uint32_t* lh = reinterpret_cast<uint32_t*>(smem + sizeof(QStage<MT>) * qt);  // HIST only
+  if (HIST)
+#pragma unroll
+    for (int i = 0; i < kTopkBins / kThreads; ++i) lh[tid + i * kThreads] = 0u;
   if (stager) request_pages();
   lds_barrier();
-  if (gfirst >= gend) return;
+  const bool hist_on = HIST && q0 < nq && st[0].nvis > k;  // uniform (rows with n <= k need none)
+  if (gfirst < gend) {
   const int npg = gend - gfirst;
   bool same_row = true;  // every query of the tile reads the first query's sequence
   for (int qi = 1; qi < qt; ++qi) same_row &= (q0 + qi >= nq) || (st[qi].row == first_row);
@@ -375,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
       const QStage<MT>& sq = st[qi];
       if (G * kPage >= sq.nvis) continue;  // uniform
       const bool ex = score_page<MT>(sq, t, G, w + (int64_t)(q0 + qi) * HI, scores + (int64_t)(q0 + qi) * ld,
-                                     lane);
+                                     lane, hist_on ? lh : nullptr);
       exact_bits |= (unsigned long long)ex << (i * qt + qi);
     }
   };
@@ -393,8 +408,10 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
       const int b = __builtin_ctzll(exact_bits);
       exact_bits &= exact_bits - 1;
       const int i = b / qt, qi = b % qt;
-      exact_entry<MT>(st[qi], idx_codes, idx_scales, (int64_t)page_of(i) * kPage + lane, w + (int64_t)(q0 + qi) * HI,
-                      scores + (int64_t)(q0 + qi) * ld + (int64_t)(gfirst + i) * kPage + lane);
+      const float e = exact_entry<MT>(st[qi], idx_codes, idx_scales, (int64_t)page_of(i) * kPage + lane,
+                                      w + (int64_t)(q0 + qi) * HI,
+                                      scores + (int64_t)(q0 + qi) * ld + (int64_t)(gfirst + i) * kPage + lane);
+      if (HIST && hist_on) atomicAdd(&lh[score_key(e) >> kTopkBinShift], 1u);
     }
   } else {
     // queries of several sequences share the tile: each query reads its own pages
@@ -407,25 +424,40 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
         const int64_t slot0 = (int64_t)page * kPage;
         KeyTile t;
         load_keys(t, idx_codes, idx_scales, page, lane);
-        if (score_page<MT>(sq, t, G, w + (int64_t)(q0 + qi) * HI, scores + (int64_t)(q0 + qi) * ld, lane))
+        if (score_page<MT>(sq, t, G, w + (int64_t)(q0 + qi) * HI, scores + (int64_t)(q0 + qi) * ld, lane,
+                           nullptr))
           exact_entry<MT>(sq, idx_codes, idx_scales, slot0 + lane, w + (int64_t)(q0 + qi) * HI,
                           scores + (int64_t)(q0 + qi) * ld + (int64_t)G * kPage + lane);
       }
     }
   }
+  }  // gfirst < gend
+  if (HIST && hist_on) {  // every wavefront is done: add the workgroup's counts
+    __syncthreads();
+    uint32_t* gh = hist + (size_t)q0 * kTopkBins;
+#pragma unroll
+    for (int i = 0; i < kTopkBins / kThreads; ++i) {
+      const uint32_t c = lh[tid + i * kThreads];
+      if (c) atomicAdd(&gh[tid + i * kThreads], c);
+    }
+  }
+}
+
+// Queries per workgroup of the scan (1 when every query reads its own sequence).
+static int query_tile(const int32_t* soq, int32_t nq, size_t stage_bytes) {
+  return (soq == nullptr || nq < 64) ? 1 : (stage_bytes * 8 <= 64 * 1024 ? 8 : 4);
 }
 
 template <int MT>
 static int launch_mt(const csa2_fp4_cache* c, const uint16_t* q_idx, const float* w, const int32_t* soq,
                      const int32_t* nvis, const int32_t* bt, int32_t max_pages, int32_t nq, float* scores, int64_t ld,
-                     hipStream_t stream) {
+                     uint32_t* hist, int k, hipStream_t stream) {
   const int total_groups = (int)ceil_div(ld, kPage);
   if (total_groups == 0 || nq == 0) return CSA2_OK;
   // queries per workgroup: several queries of one sequence share each loaded page
-  // (queries without a sequence map each read their own pages)
   // (queries without a sequence map each read their own pages); the staged queries
   // stay within 64 KB of LDS
-  const int qt = (soq == nullptr || nq < 64) ? 1 : (sizeof(QStage<MT>) * 8 <= 64 * 1024 ? 8 : 4);
+  const int qt = query_tile(soq, nq, sizeof(QStage<MT>));
   // pages per wavefront: enough wavefronts to cover the chip about twice
   const long long qtiles = ceil_div(nq, qt);
   const long long want_waves = qtiles >= 512 ? 4 * qtiles : 2048;
@@ -433,17 +465,58 @@ static int launch_mt(const csa2_fp4_cache* c, const uint16_t* q_idx, const float
   if (gpw < 1) gpw = 1;
   if (gpw > kMaxPagesPerWave) gpw = kMaxPagesPerWave;
   const unsigned gx = ceil_div(total_groups, (long long)kWaves * gpw);
+  const dim3 grid(gx, (unsigned)qtiles), block(kThreads);
   const size_t lds = sizeof(QStage<MT>) * qt;
-  if (qt == 8)
-    hipLaunchKernelGGL((index_score_kernel<MT, 8>), dim3(gx, (unsigned)qtiles), dim3(kThreads), lds, stream, c->idx_codes,
-                       c->idx_scales, q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups);
-  else if (qt == 4)
-    hipLaunchKernelGGL((index_score_kernel<MT, 4>), dim3(gx, (unsigned)qtiles), dim3(kThreads), lds, stream, c->idx_codes,
-                       c->idx_scales, q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups);
-  else
-    hipLaunchKernelGGL((index_score_kernel<MT, 1>), dim3(gx, (unsigned)qtiles), dim3(kThreads), lds, stream, c->idx_codes,
-                       c->idx_scales, q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups);
+  if (hist != nullptr) {  // one query per workgroup (the caller checked)
+    hipLaunchKernelGGL((index_score_kernel<MT, 1, true>), grid, block, lds + kTopkBins * sizeof(uint32_t), stream,
+                       c->idx_codes, c->idx_scales, q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw,
+                       total_groups, hist, k);
+  } else if (qt == 8) {
+    hipLaunchKernelGGL((index_score_kernel<MT, 8, false>), grid, block, lds, stream, c->idx_codes, c->idx_scales,
+                       q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k);
+  } else if (qt == 4) {
+    hipLaunchKernelGGL((index_score_kernel<MT, 4, false>), grid, block, lds, stream, c->idx_codes, c->idx_scales,
+                       q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k);
+  } else {
+    hipLaunchKernelGGL((index_score_kernel<MT, 1, false>), grid, block, lds, stream, c->idx_codes, c->idx_scales,
+                       q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k);
+  }
   return launch_status();
+}
+
+static int launch_hi(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
+                     const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* block_table,
+                     int32_t max_pages, int32_t nq, float* scores, int64_t ld, uint32_t* hist, int k,
+                     hipStream_t stream) {
+  switch (Hi / 16) {
+#define CSA2_MT(m) \
+  case m:          \
+    return launch_mt<m>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, hist, k, \
+                        stream);
+    CSA2_MT(1)
+    CSA2_MT(2)
+    CSA2_MT(3)
+    CSA2_MT(4)
+    CSA2_MT(5)
+    CSA2_MT(6)
+    CSA2_MT(7)
+    default: return launch_mt<8>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld,
+                                 hist, k, stream);
+#undef CSA2_MT
+  }
+}
+
+static int check_args(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
+                      const int32_t* n_visible, const int32_t* block_table, int32_t max_pages, int32_t nq,
+                      float* scores, int64_t ld) {
+  if (!cache_ok(cache)) return CSA2_ERR_NULL;
+  if (!cache_shape_ok(cache) || nq < 0 || ld < 0 || max_pages < 0) return CSA2_ERR_SHAPE;
+  if (Hi < 16 || Hi > 128 || Hi % 16 != 0) return CSA2_ERR_SHAPE;
+  if (nq == 0 || ld == 0) return CSA2_OK;
+  if (!q_idx || !w || !n_visible || !block_table || !scores) return CSA2_ERR_NULL;
+  if (max_pages < (ld + CSA2_PAGE_SIZE - 1) / CSA2_PAGE_SIZE) return CSA2_ERR_SHAPE;
+  if (ld > (int64_t)1 << 30) return CSA2_ERR_SHAPE;
+  return CSA2_OK;
 }
 
 }  // namespace csa2
@@ -453,21 +526,29 @@ using namespace csa2;
 extern "C" int index_score(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
                            const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* block_table,
                            int32_t max_pages, int32_t nq, float* scores, int64_t ld, hipStream_t stream) {
-  if (!cache_ok(cache)) return CSA2_ERR_NULL;
-  if (!cache_shape_ok(cache) || nq < 0 || ld < 0 || max_pages < 0) return CSA2_ERR_SHAPE;
-  if (Hi < 16 || Hi > 128 || Hi % 16 != 0) return CSA2_ERR_SHAPE;
-  if (nq == 0 || ld == 0) return CSA2_OK;
-  if (!q_idx || !w || !n_visible || !block_table || !scores) return CSA2_ERR_NULL;
-  if (max_pages < (ld + CSA2_PAGE_SIZE - 1) / CSA2_PAGE_SIZE) return CSA2_ERR_SHAPE;
-  if (ld > (int64_t)1 << 30) return CSA2_ERR_SHAPE;
-  switch (Hi / 16) {
-    case 1: return launch_mt<1>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
-    case 2: return launch_mt<2>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
-    case 3: return launch_mt<3>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
-    case 4: return launch_mt<4>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
-    case 5: return launch_mt<5>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
-    case 6: return launch_mt<6>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
-    case 7: return launch_mt<7>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
-    default: return launch_mt<8>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
+  const int st = check_args(cache, q_idx, w, Hi, n_visible, block_table, max_pages, nq, scores, ld);
+  if (st != CSA2_OK || nq == 0 || ld == 0) return st;
+  return launch_hi(cache, q_idx, w, Hi, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, nullptr, 0,
+                   stream);
+}
+
+extern "C" int index_topk(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
+                          const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* block_table,
+                          int32_t max_pages, int32_t nq, float* scores, int64_t ld, int32_t k, int32_t* topk_idx,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_args(cache, q_idx, w, Hi, n_visible, block_table, max_pages, nq, scores, ld);
+  if (st != CSA2_OK) return st;
+  if (k < 1 || k > CSA2_MAX_K || ld >= ((int64_t)1 << 31)) return CSA2_ERR_SHAPE;
+  if (nq == 0) return CSA2_OK;
+  if (!topk_idx) return CSA2_ERR_NULL;
+  if (!ws || ws_bytes < topk_select_workspace_size(nq, ld, k)) return CSA2_ERR_WORKSPACE;
+  // the counting pass folds into the scan when every workgroup serves one query
+  const bool fuse = ld > 0 && query_tile(seq_of_query, nq, 0) == 1;
+  if (ld > 0) {
+    uint32_t* hist = fuse ? topk_digit1_hist(ws, nq, ld) : nullptr;
+    st = launch_hi(cache, q_idx, w, Hi, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, hist, k,
+                   stream);
+    if (st != CSA2_OK) return st;
   }
+  return topk_enqueue(scores, ld, n_visible, nq, k, topk_idx, ws, stream, fuse);
 }

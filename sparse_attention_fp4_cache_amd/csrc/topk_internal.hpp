@@ -1,0 +1,22 @@
+// topk_internal.hpp -- the selection's pieces that the fused indexer stage shares
+// (not part of the C ABI).
+#pragma once
+#include <cstddef>
+#include <cstdint>
+#include <hip/hip_runtime.h>
+
+namespace csa2 {
+
+constexpr int kTopkBins = 4096;      // digit-1 bins: the top 12 bits of the score key
+constexpr int kTopkBinShift = 20;
+
+// Per-query digit-1 histograms ([nq][kTopkBins] u32) inside a top-k workspace.
+uint32_t* topk_digit1_hist(void* ws, int32_t nq, int64_t ld);
+
+// Enqueue the selection; with hist_done the digit-1 histograms are already filled
+// (by the scoring pass) and the counting launch is skipped.  Arguments were
+// validated by the caller.
+int topk_enqueue(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq, int32_t k,
+                 int32_t* topk_idx, void* ws, hipStream_t stream, bool hist_done);
+
+}  // namespace csa2

@@ -9,7 +9,8 @@
 // distinct, so the answer is unique.  Two launches over a grid of
 // (chunks of 4096 consecutive scores) x (queries):
 //   1. hist   : 4096-bin histogram of the top 12 key bits (digit 1), added to a
-//               per-query global histogram.
+//               per-query global histogram (index_topk folds this pass into the
+//               scoring pass).
 //   2. select : every workgroup finds the threshold bin b* of digit 1 (where the
 //               running count from the top reaches k), writes the composites of its
 //               entries in bins >= b* -- in index order -- to its own fixed region
@@ -29,11 +30,12 @@
 // with the arrival atomic, so no cache-wide write-back or invalidate is needed.
 #include "common.hpp"
 #include "host_common.hpp"
+#include "topk_internal.hpp"
 
 namespace csa2 {
 
-constexpr int kBins = 4096;  // 12-bit digits
-constexpr int kBinShift = 20;
+constexpr int kBins = kTopkBins;  // 12-bit digits
+constexpr int kBinShift = kTopkBinShift;
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kPer = 8;  // consecutive scores per thread
@@ -468,6 +470,29 @@ extern "C" size_t topk_select_workspace_size(int32_t nq, int64_t ld, int32_t k) 
   return ws_bytes_for(nq, nchunk);
 }
 
+namespace csa2 {
+
+uint32_t* topk_digit1_hist(void* ws, int32_t nq, int64_t ld) {
+  const long long nchunk = ld > 0 ? (ld + kChunk - 1) / kChunk : 1;
+  return carve(ws, nq, nchunk).hist;
+}
+
+int topk_enqueue(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq, int32_t k,
+                 int32_t* topk_idx, void* ws, hipStream_t stream, bool hist_done) {
+  const long long nchunk = ld > 0 ? (ld + kChunk - 1) / kChunk : 1;
+  const long long kchunk = (k + kChunk - 1) / kChunk;  // the n <= k path writes k outputs
+  const long long grid_x = nchunk > kchunk ? nchunk : kchunk;
+  const TopkWs w = carve(ws, nq, nchunk);
+  const dim3 grid((unsigned)grid_x, (unsigned)nq);
+  if (ld > 0 && !hist_done)
+    hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kThreads), 0, stream, scores, ld, n_visible, k, w);
+  hipLaunchKernelGGL(topk_select_kernel, grid, dim3(kThreads), 0, stream, scores, ld, n_visible, k, topk_idx, w,
+                     (int)nchunk);
+  return launch_status();
+}
+
+}  // namespace csa2
+
 extern "C" int topk_select(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq, int32_t k,
                            int32_t* topk_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (nq < 0 || ld < 0 || k < 1 || k > CSA2_MAX_K) return CSA2_ERR_SHAPE;
@@ -475,13 +500,5 @@ extern "C" int topk_select(const float* scores, int64_t ld, const int32_t* n_vis
   if (nq == 0) return CSA2_OK;
   if (!n_visible || !topk_idx || (ld > 0 && !scores)) return CSA2_ERR_NULL;
   if (!ws || ws_bytes < topk_select_workspace_size(nq, ld, k)) return CSA2_ERR_WORKSPACE;
-  const long long nchunk = ld > 0 ? (ld + kChunk - 1) / kChunk : 1;
-  const long long kchunk = (k + kChunk - 1) / kChunk;  // the n <= k path writes k outputs
-  const long long grid_x = nchunk > kchunk ? nchunk : kchunk;
-  const TopkWs w = carve(ws, nq, nchunk);
-  const dim3 grid((unsigned)grid_x, (unsigned)nq);
-  if (ld > 0) hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kThreads), 0, stream, scores, ld, n_visible, k, w);
-  hipLaunchKernelGGL(topk_select_kernel, grid, dim3(kThreads), 0, stream, scores, ld, n_visible, k, topk_idx, w,
-                     (int)nchunk);
-  return launch_status();
+  return topk_enqueue(scores, ld, n_visible, nq, k, topk_idx, ws, stream, false);
 }

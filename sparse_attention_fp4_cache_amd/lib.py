@@ -28,6 +28,7 @@ EXPORTS = (
     "index_score",
     "topk_select_workspace_size",
     "topk_select",
+    "index_topk",
     "sparse_attn_decode_workspace_size",
     "sparse_attn_decode",
     "sparse_attn_prefill_chunk_workspace_size",
@@ -73,6 +74,8 @@ def load() -> ctypes.CDLL:
         L.topk_select_workspace_size.argtypes = [_I32, _I64, _I32]
         L.topk_select_workspace_size.restype = _SZ
         L.topk_select.argtypes = [_P, _I64, _P, _I32, _I32, _P, _P, _SZ, _P]
+        L.index_topk.argtypes = [ctypes.POINTER(_CacheStruct), _P, _P, _I32, _P, _P, _P, _I32, _I32, _P, _I64, _I32,
+                                 _P, _P, _SZ, _P]
         L.sparse_attn_decode_workspace_size.argtypes = [_I32, _I32, _I32, _I32]
         L.sparse_attn_decode_workspace_size.restype = _SZ
         L.sparse_attn_decode.argtypes = [ctypes.POINTER(_CacheStruct), _P, _I32, _P, _I32, _P, _I32, _P, _P, _I32,
@@ -192,6 +195,24 @@ def topk_select(scores: torch.Tensor, n_visible: torch.Tensor, k: int, topk_idx:
                                              _ptr(n_visible, torch.int32, "n_visible"), nq, k,
                                              _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(ws, torch.uint8, "ws"),
                                              ws.numel(), _stream(stream)))
+
+
+def index_topk(cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, n_visible: torch.Tensor,
+               block_table: torch.Tensor, scores: torch.Tensor, k: int, topk_idx: torch.Tensor, ws: torch.Tensor,
+               seq_of_query: torch.Tensor | None = None, stream=None):
+    """index_score then topk_select on the same scores, as one call (same results)."""
+    nq, Hi, d = q_idx.shape
+    if d != INDEX_DIM or w.shape != (nq, Hi) or n_visible.shape != (nq,) or scores.dim() != 2 or scores.shape[0] != nq:
+        raise ValueError("shape mismatch in index_topk arguments")
+    if topk_idx.shape != (nq, k):
+        raise ValueError("topk_idx must be [nq, k]")
+    _check("index_topk", load().index_topk(cache.struct, _bits16(q_idx, "q_idx"), _ptr(w, torch.float32, "w"), Hi,
+                                           _ptr(seq_of_query, torch.int32, "seq_of_query"),
+                                           _ptr(n_visible, torch.int32, "n_visible"),
+                                           _ptr(block_table, torch.int32, "block_table"), block_table.shape[1], nq,
+                                           _ptr(scores, torch.float32, "scores"), scores.shape[1], k,
+                                           _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(ws, torch.uint8, "ws"),
+                                           ws.numel(), _stream(stream)))
 
 
 def sparse_attn_decode_workspace_size(B: int, H: int, k: int, window: int) -> int:

@@ -37,9 +37,12 @@ class DecodeStep:
     attend with the latest indices.
     """
 
-    def __init__(self, wl: Workload, device="cuda", softmax_scale: float | None = None):
+    def __init__(self, wl: Workload, device="cuda", softmax_scale: float | None = None, fused_index: bool = True):
+        """fused_index: run each indexer stage as one index_topk call (same results
+        as index_score followed by topk_select, one launch fewer)."""
         assert wl.kind == "decode"
         self.wl = wl
+        self.fused_index = fused_index
         self.device = device
         self.scale = lib.default_softmax_scale() if softmax_scale is None else softmax_scale
         B, K, W = wl.B, wl.K, wl.W
@@ -109,12 +112,18 @@ class DecodeStep:
                 call("fp4_cache_write", lib.fp4_cache_write, self.cache, self.new_latent, self.new_key,
                      self.new_slot)
             if mode in ("full", "reindex"):
-                call("index_score", lib.index_score, self.cache, L["q_idx"], L["w"], self.n_visible,
-                     self.block_table, self.scores)
-                if keep_scores:
-                    L["scores"] = self.scores.clone()
-                call("topk_select", lib.topk_select, self.scores, self.n_visible, self.wl.K, L["topk"],
-                     self.ws_topk)
+                if self.fused_index:
+                    call("index_topk", lib.index_topk, self.cache, L["q_idx"], L["w"], self.n_visible,
+                         self.block_table, self.scores, self.wl.K, L["topk"], self.ws_topk)
+                    if keep_scores:
+                        L["scores"] = self.scores.clone()
+                else:
+                    call("index_score", lib.index_score, self.cache, L["q_idx"], L["w"], self.n_visible,
+                         self.block_table, self.scores)
+                    if keep_scores:
+                        L["scores"] = self.scores.clone()
+                    call("topk_select", lib.topk_select, self.scores, self.n_visible, self.wl.K, L["topk"],
+                         self.ws_topk)
                 latest = L["topk"]
             if latest is None:
                 raise ValueError("a reuse layer needs an earlier full or reindex layer")

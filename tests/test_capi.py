@@ -98,6 +98,23 @@ def test_topk_validation(L):
     assert L.topk_select_workspace_size(4, 10000, 64) > ws
 
 
+def test_index_topk_validation(L):
+    ws = L.topk_select_workspace_size(1, 4096, 64)
+    args = lambda **kw: dict(dict(cache=_cache(), q=FAKE, w=FAKE, Hi=64, soq=None, nv=FAKE, bt=FAKE, mp=64, nq=1,
+                                  sc=FAKE, ld=4096, k=64, idx=FAKE, ws=FAKE, wsb=ws), **kw)
+    call = lambda a: L.index_topk(a["cache"], a["q"], a["w"], a["Hi"], a["soq"], a["nv"], a["bt"], a["mp"], a["nq"],
+                                  a["sc"], a["ld"], a["k"], a["idx"], a["ws"], a["wsb"], None)
+    assert call(args(cache=_cache(null=True))) == -1
+    assert call(args(Hi=40)) == -2
+    assert call(args(k=0)) == -2
+    assert call(args(k=4097)) == -2
+    assert call(args(idx=None)) == -1
+    assert call(args(ws=None)) == -4
+    assert call(args(wsb=ws - 1)) == -4
+    assert call(args(mp=10)) == -2
+    assert call(args(nq=0)) == 0
+
+
 def test_attention_validation(L):
     c = _cache()
     ws = L.sparse_attn_decode_workspace_size(1, 64, 2048, 128)

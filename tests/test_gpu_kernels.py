@@ -377,3 +377,77 @@ def test_index_score_reveals_query_quantisation():
     got = scores.cpu().numpy()
     bad = np.argwhere(got.view(np.int32) != ref.view(np.int32))
     assert len(bad) == 0, f"{len(bad)} differ, first {bad[:5].tolist()}: {got[tuple(bad[0])]} vs {ref[tuple(bad[0])]}"
+
+
+def _fused_vs_separate(rng, n_per_seq, Hi, k, key_fn=None, seq_of_query=None, reps=2):
+    """index_topk against index_score followed by topk_select (bit for bit), on a
+    paged cache; called `reps` times on one workspace (it must be left clean)."""
+    B = len(n_per_seq)
+    pages = [(n + 63) // 64 for n in n_per_seq]
+    phys = rng.permutation(sum(pages))
+    bt = np.zeros((B, max(pages)), np.int32)
+    off, lat, key, slots = 0, [], [], []
+    for b, n in enumerate(n_per_seq):
+        bt[b, :pages[b]] = phys[off:off + pages[b]]
+        off += pages[b]
+        j = np.arange(n)
+        slots.append(bt[b, j // 64].astype(np.int64) * 64 + j % 64)
+        kk = rng.standard_normal((n, 128)).astype(np.float32)
+        key.append(bits(key_fn(kk) if key_fn else kk))
+        lat.append(bits(np.zeros((n, 512), np.float32)))
+    g = lib.Cache(sum(pages) * 64)
+    lib.fp4_cache_write(g, dev_bits(np.concatenate(lat)), dev_bits(np.concatenate(key)), dev(np.concatenate(slots)))
+    if seq_of_query is None:
+        nq, soq, nvis = B, None, np.array(n_per_seq, np.int32)
+    else:
+        soq = np.asarray(seq_of_query, np.int32)
+        nq = len(soq)
+        nvis = np.array([max(1, n_per_seq[s] - 7 * i % 50) for i, s in enumerate(soq)], np.int32)
+    ld = ((int(nvis.max()) + 63) // 64) * 64
+    q = bits(rng.standard_normal((nq, Hi, 128)).astype(np.float32))
+    w = rng.random((nq, Hi), dtype=np.float32)
+    dq, dw, dnv, dbt = dev_bits(q), dev(w), dev(nvis), dev(bt)
+    dsoq = None if soq is None else dev(soq)
+    ws = torch.zeros(lib.topk_select_workspace_size(nq, ld, k), dtype=torch.uint8, device="cuda")
+    s_sep = torch.full((nq, ld), float("nan"), device="cuda")
+    i_sep = torch.full((nq, k), -7, dtype=torch.int32, device="cuda")
+    lib.index_score(g, dq, dw, dnv, dbt, s_sep, seq_of_query=dsoq)
+    lib.topk_select(s_sep, dnv, k, i_sep, ws)
+    for rep in range(reps):
+        s_f = torch.full((nq, ld), float("nan"), device="cuda")
+        i_f = torch.full((nq, k), -7, dtype=torch.int32, device="cuda")
+        lib.index_topk(g, dq, dw, dnv, dbt, s_f, k, i_f, ws, seq_of_query=dsoq)
+        torch.cuda.synchronize()
+        a, b = s_f.cpu().numpy(), s_sep.cpu().numpy()
+        for r in range(nq):
+            assert same_bits_f32(a[r, :nvis[r]], b[r, :nvis[r]]), f"rep {rep} row {r}: scores differ"
+        assert torch.equal(i_f, i_sep), f"rep {rep}: top-k differs"
+    # the workspace needs no clearing between calls: a separate selection after the
+    # fused calls still matches
+    i_again = torch.full((nq, k), -7, dtype=torch.int32, device="cuda")
+    lib.topk_select(s_sep, dnv, k, i_again, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(i_again, i_sep), "selection after fused calls differs"
+
+
+def test_index_topk_fused_equals_separate_calls():
+    rng = np.random.default_rng(300)
+    say("case: index_topk fused (3 ragged sequences, one with n <= k), twice on one workspace")
+    _fused_vs_separate(rng, [20000, 200, 9000], 64, 256)
+    say("case: index_topk fused, one long row (many chunks)")
+    _fused_vs_separate(rng, [70000], 64, 2048)
+
+
+def test_index_topk_fused_exact_path_entries():
+    def keys(k):
+        k[:, 0:32] *= 2.0 ** -12
+        k[:, 64:96] *= 2.0 ** 6
+        return k
+
+    say("case: index_topk fused with exact-path entries (wide exponent spread)")
+    _fused_vs_separate(np.random.default_rng(301), [6000], 16, 512, key_fn=keys)
+
+
+def test_index_topk_query_tiles_fall_back():
+    say("case: index_topk with a sequence map and 70 queries (tiles of queries, separate counting pass)")
+    _fused_vs_separate(np.random.default_rng(302), [5000, 3000], 32, 128, seq_of_query=[0] * 40 + [1] * 30)

@@ -13,11 +13,13 @@ its cache out of the MALL.  Warm mode (one copy, replayed) is reported beside it
 Prints ONE JSON line: tokens/s (sequences / step time), the FP4 cache bytes read
 per step and their rate, a roofline record for the indexer scan (the kernel that
 carries the FP4 bytes), timed with HIP events on its own stream over graph
-replays of back-to-back launches, and the CPU oracle on a bounded sample.
+replays of back-to-back launches, the same timing for each library call of the
+step, and the CPU oracle on a bounded sample.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 import argparse
+import functools
 import hashlib
 import json
 import math
@@ -216,44 +218,60 @@ def main():
     ms_per_step = timed(args.steps, rotate=True)
     warm_ms = timed(args.steps, rotate=False)
 
-    # ---- the scan kernel alone: back-to-back launches over the same inputs as the
-    # step (every index layer, every cache copy), timed with HIP events on the stream
+    # ---- each library call alone: back-to-back launches over the same inputs as the
+    # step (every layer, every cache copy), captured in a graph and timed with HIP
+    # events on the stream; the scan (index_score) is the roofline kernel
+    def burst_ms(calls, target=60):
+        reps = max(2, math.ceil(target / len(calls)))
+
+        def run_all():
+            for fn in calls:
+                fn()
+
+        with torch.cuda.stream(stream):
+            run_all()
+        stream.synchronize()
+        g = None
+        if args.graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                run_all()
+            torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(reps):
+                if g is not None:
+                    g.replay()
+                else:
+                    run_all()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * len(calls)), reps * len(calls)
+
+    calls_us = {}
     if wl.kind == "decode":
-        idx_calls = [(s.cache, L["q_idx"], L["w"], s.n_visible, s.block_table, s.scores, None)
-                     for s in steps for L in s.layers if L["mode"] in ("full", "reindex")]
+        idx_layers = [L for L in st.layers if L["mode"] in ("full", "reindex")]
+        scan = [functools.partial(lib.index_score, s.cache, L["q_idx"], L["w"], s.n_visible, s.block_table, s.scores)
+                for s in steps for L in idx_layers]
+        calls_us["index_topk"] = burst_ms([functools.partial(lib.index_topk, s.cache, L["q_idx"], L["w"], s.n_visible,
+                                                             s.block_table, s.scores, wl.K, L["topk"], s.ws_topk)
+                                           for s in steps for L in idx_layers])[0] * 1e3
+        calls_us["topk_select"] = burst_ms([functools.partial(lib.topk_select, st.scores, st.n_visible, wl.K,
+                                                              L["topk"], st.ws_topk) for L in idx_layers])[0] * 1e3
+        calls_us["sparse_attn_decode"] = burst_ms([functools.partial(
+            lib.sparse_attn_decode, s.cache, L["q"], st.layers[0]["topk"], s.block_table, L["swa"], L["swa_len"],
+            st.scale, L["out"], L["lse"], s.ws_attn) for s in steps for L in st.layers])[0] * 1e3
         idx_bytes = sum(int(x) for x in wl.n_entries) * IDX_ENTRY_BYTES
         tokens = wl.B
     else:
-        idx_calls = [(s.cache, s.q_idx, s.w, s.n_visible, s.block_table2d, s.scores, s.seq_of_query) for s in steps]
+        scan = [functools.partial(lib.index_score, s.cache, s.q_idx, s.w, s.n_visible, s.block_table2d, s.scores,
+                                  seq_of_query=s.seq_of_query) for s in steps]
         idx_bytes = int(wl.n_visible().astype("int64").sum()) * IDX_ENTRY_BYTES
         tokens = wl.chunk
-
-    def scan_burst():
-        for c, qi, w, nv, bt, sc, soq in idx_calls:
-            lib.index_score(c, qi, w, nv, bt, sc, seq_of_query=soq)
-
-    reps = max(2, math.ceil(60 / len(idx_calls)))
-    with torch.cuda.stream(stream):
-        scan_burst()
-    stream.synchronize()
-    burst_graph = None
-    if args.graph:
-        burst_graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(burst_graph, stream=stream):
-            scan_burst()
-        torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        for _ in range(reps):
-            if burst_graph is not None:
-                burst_graph.replay()
-            else:
-                scan_burst()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    idx_ms = e0.elapsed_time(e1) / (reps * len(idx_calls))
+    idx_ms, idx_launches = burst_ms(scan)
+    calls_us["index_score"] = idx_ms * 1e3
     achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
     traffic = stored_traffic(wl.name)
     step_bytes = fp4_bytes_per_step(wl)
@@ -294,7 +312,8 @@ def main():
         "roofline": {"kernel": "index_score", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "bytes_per_launch": idx_bytes, "avg_launch_ms": idx_ms,
-                     "launches_timed": reps * len(idx_calls)},
+                     "launches_timed": idx_launches},
+        "calls_us": calls_us,
     }
     if wl.kind == "prefill":
         flop = int(wl.n_visible().astype("int64").sum()) * wl.Hi * 128 * 2

@@ -12,20 +12,23 @@
 // 16 heads and a contiguous range of candidate rows (selected entries first, then
 // window rows).  The two halves walk alternate tiles of 32 rows at the same time,
 // each with its own LDS tile and online softmax, and combine their states at the end:
-//   gather   : 256 threads dequantise the tile into LDS twice, row-major X[32][512]
-//              and transposed XT[512][32] (bf16; E2M1 x E4M3 has at most 6
-//              significant bits in [2^-10, 2688], so the bf16 value is exact).  The
-//              bytes of the next tile are loaded into registers while the current
-//              tile is computed.
+//   gather   : a thread loads 64 channels of one tile row with 16-byte loads (only
+//              the kinds of row the tile holds: FP4 entry or bf16 window row) and
+//              dequantises them into LDS as row-major X[32][512] (bf16; E2M1 x E4M3
+//              has at most 6 significant bits in [2^-10, 2688], so the bf16 value is
+//              exact).  16-byte chunks are XOR-swizzled per row block against bank
+//              conflicts.  The bytes of the next tile are loaded into registers while
+//              the current tile is computed.
 //   logits   : S^T = X Q^T with V_MFMA_F32_16X16X32_BF16; each wavefront covers a
 //              quarter of the 512 channels and the four partial tiles are summed in
 //              LDS in a fixed order.  The rows are permuted across the two 16-row
 //              M-tiles so that lane group g holds rows 8g .. 8g+7.
 //   softmax  : per head, running max / sum in fp32 (exp2 of log2e-scaled logits).
-//   values   : O^T += XT P^T; each wavefront owns 128 output channels.  The P
-//              operand comes straight from the logits accumulator registers (the
-//              K index of the MFMA is permuted to match), split into a bf16 high
-//              part and a bf16 remainder so P keeps ~16 significant bits.
+//   values   : O^T += X^T P^T; each wavefront owns 128 output channels.  The X^T
+//              operand is read from row-major X with DS_READ_B64_TR_B16 (a transposing
+//              LDS read), the P operand comes straight from the logits accumulator
+//              registers (the K index of the MFMA is permuted to match), split into a
+//              bf16 high part and a bf16 remainder so P keeps ~16 significant bits.
 // With several row ranges per query the unnormalised partial (O, m, l) goes to the
 // workspace and a merge kernel combines the ranges with their log-sum-exp weights.
 // Both halves run the same number of tile steps (a half past the end of the range
@@ -36,12 +39,13 @@
 namespace csa2 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int kRT = 32;              // rows per tile
 constexpr int kXStride = 512 + 8;    // bf16 elements per row of X in LDS (padding vs bank conflicts)
-constexpr int kXTStride = kRT + 4;   // bf16 elements per channel of XT in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnArgs {
@@ -72,13 +76,12 @@ constexpr int kSeg = 512;  // rows whose sources are resolved into LDS at a time
 constexpr int kThreads = 512;  // two halves of 4 wavefronts
 
 struct __align__(16) HalfSmem {
-  uint16_t x[kRT * kXStride];    // X[row][ch]
-  uint16_t xt[512 * kXTStride];  // XT[ch][row]
+  uint16_t x[kRT * kXStride];    // X[row][ch], 16-byte chunks swizzled by xchunk()
   float red[4][2][4][64];        // partial logits [wave][mtile][r][lane]
 };
 struct __align__(16) AttnSmem {
   HalfSmem h[2];
-  int src[kSeg];  // row source: slot >= 0, window row -2-r, or -1 (none)
+  int src[kSeg];  // row source: slot >= 0, window row -2-r, or -1 (none, also the padding)
 };
 static_assert(sizeof(AttnSmem) <= 160 * 1024, "attention LDS exceeds 160 KB");
 // the second half's tile area holds its softmax state for the final combine
@@ -88,86 +91,103 @@ CSA2_DEV uint32_t pack_bf16_hi(float lo, float hi) {  // exact values only (low 
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
 }
 
+// Max / sum over the lanes l, l^16, l^32, l^48 with the VALU lane swaps of gfx950:
+// permlane16_swap(v, v) leaves the values of 16-lane rows 2i and 2i+1 in the two
+// results, in that order, in every lane of both rows; permlane32_swap(v, v) does the
+// same for the two halves.  Every lane combines the same operands in the same order.
+CSA2_DEV float max_rows(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+CSA2_DEV float sum_rows(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 CSA2_DEV uint32_t bf16_rne_bits(float f) {  // fp32 -> bf16 bits, round to nearest even (finite f)
   uint32_t u = __float_as_uint(f);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Raw bytes of this thread's 8 rows x 8 channels of one tile, as loaded from HBM.
-// Thread t: rows 8*(t%4) .. +7, channels 8*(t/4) .. +7.  Every row issues the same
-// loads whatever its kind (addresses of missing kinds are clamped to row 0), so the
-// compiler keeps all of them in flight together instead of waiting per branch.
+// Physical 16-byte chunk of logical chunk c (8 channels) within a row of X: chunk
+// c of the 8-chunk block c/8 is moved to (c % 8) ^ (c / 8), so the eight threads that
+// write one row block per instruction hit different banks.
+CSA2_DEV int xchunk(int c) { return c ^ ((c >> 3) & 7); }
+
+// Raw bytes of this thread's share of one tile, as loaded from HBM.  Thread t of a
+// half owns tile row t/8 and channels 64*(t%8) .. +63.  Only the kinds of row the
+// tile can hold are loaded (a uniform branch); an address of a missing row is
+// clamped to row 0 and its value masked out.
 struct TileRegs {
-  uint32_t code[8];   // main row: 4 code bytes (8 channels)
-  uint32_t sc[8];     // main row: E4M3 scale byte
-  uint4 win[8];       // window row: 8 bf16
-  uint32_t mmask[8];  // all ones for a main row
-  uint32_t wmask[8];  // all ones for a window row
+  uint4 code[2];  // FP4 entry: 32 code bytes (64 channels)
+  uint32_t sc;    // FP4 entry: the E4M3 scale bytes of channels 16j .. 16j+15, j = 0..3
+  uint4 win[8];   // window row: 64 bf16
+  int kind;       // 1: FP4 entry, 2: window row, 0: no row
 };
 
-CSA2_DEV void issue_tile(const AttnArgs& a, const int* src_rows, int tid, int tile_row0, int r_local_end,
+CSA2_DEV void issue_tile(const AttnArgs& a, const int* src_rows, int tid, int tile_row0, bool has_main, bool has_win,
                          TileRegs& t) {
-  const int rg = tid & 3, cb = tid >> 2;
-#pragma unroll
-  for (int rr = 0; rr < 8; ++rr) {
-    const int rl = tile_row0 + 8 * rg + rr;  // row index local to this segment
-    const int src = (rl < r_local_end) ? src_rows[rl] : -1;
-    t.mmask[rr] = src >= 0 ? ~0u : 0u;
-    t.wmask[rr] = src <= -2 ? ~0u : 0u;
+  const int row = tid >> 3, c8 = tid & 7;
+  const int src = src_rows[tile_row0 + row];
+  t.kind = src >= 0 ? 1 : (src <= -2 ? 2 : 0);
+  if (has_main) {
     const int64_t slot = src >= 0 ? src : 0;
-    t.code[rr] = *reinterpret_cast<const uint32_t*>(a.main_codes + slot * kMainRowBytes + 4 * cb);
-    t.sc[rr] = a.main_scales[slot * kMainScaleBytes + (cb >> 1)];
+    const uint4* cp = reinterpret_cast<const uint4*>(a.main_codes + slot * kMainRowBytes) + 2 * c8;
+    t.code[0] = cp[0];
+    t.code[1] = cp[1];
+    t.sc = reinterpret_cast<const uint32_t*>(a.main_scales + slot * kMainScaleBytes)[c8];
+  } else {
+    t.code[0] = t.code[1] = make_uint4(0u, 0u, 0u, 0u);
+    t.sc = 0u;
   }
-  if (a.window > 0) {
+  if (has_win) {
+    const int64_t wrow = src <= -2 ? (int64_t)(-2 - src) : 0;
+    const uint4* wp = reinterpret_cast<const uint4*>(a.swa + wrow * kLatentDim) + 8 * c8;
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      const int rl = tile_row0 + 8 * rg + rr;
-      const int src = (rl < r_local_end) ? src_rows[rl] : -1;
-      const int64_t wrow = src <= -2 ? (int64_t)(-2 - src) : 0;
-      t.win[rr] = *reinterpret_cast<const uint4*>(a.swa + wrow * kLatentDim + 8 * cb);
-    }
+    for (int i = 0; i < 8; ++i) t.win[i] = wp[i];
   } else {
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) t.win[rr] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < 8; ++i) t.win[i] = make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
-// Dequantise the loaded bytes into X (row-major) and XT (transposed) in LDS.
-// Branch-free: E4M3 scale via V_CVT_F32_FP8 (OCP E4M3FN on gfx950), E2M1 pairs via
-// V_CVT_SCALEF32_PK_F32_FP4 with a unit scale, product exact in fp32 and in bf16.
-// XT rows are written as 16-byte runs of 8 consecutive tile rows.
-CSA2_DEV void store_tile(HalfSmem& sm, int tid, const TileRegs& t) {
-  const int rg = tid & 3, cb = tid >> 2;
-  uint32_t w[8][4];
+CSA2_DEV uint4 and4(uint4 v, uint32_t m) { return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m); }
+CSA2_DEV uint4 or4(uint4 a, uint4 b) { return make_uint4(a.x | b.x, a.y | b.y, a.z | b.z, a.w | b.w); }
+
+// E2M1 x E4M3 of 8 channels (one code dword) as 8 bf16, exact.
+CSA2_DEV uint4 dequant8(uint32_t c, float s) {
+  const v2f d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+  const v2f d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+  const v2f d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
+  const v2f d3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+  return make_uint4(pack_bf16_hi(d0[0] * s, d0[1] * s), pack_bf16_hi(d1[0] * s, d1[1] * s),
+                    pack_bf16_hi(d2[0] * s, d2[1] * s), pack_bf16_hi(d3[0] * s, d3[1] * s));
+}
+
+// Dequantise the loaded bytes into X (row-major, swizzled chunks) in LDS.
+// Branch-free within a tile: E4M3 scale via V_CVT_F32_FP8 (OCP E4M3FN on gfx950),
+// E2M1 pairs via V_CVT_SCALEF32_PK_F32_FP4 with a unit scale, product exact in
+// fp32 and in bf16.
+CSA2_DEV void store_tile(HalfSmem& sm, int tid, const TileRegs& t, bool has_main) {
+  const int row = tid >> 3, c8 = tid & 7;
+  uint4* xr = reinterpret_cast<uint4*>(sm.x + row * kXStride);
+  const uint32_t wmask = t.kind == 2 ? ~0u : 0u;
+  if (has_main) {
+    const uint32_t mmask = t.kind == 1 ? ~0u : 0u;
+    const uint32_t cw[8] = {t.code[0].x, t.code[0].y, t.code[0].z, t.code[0].w,
+                            t.code[1].x, t.code[1].y, t.code[1].z, t.code[1].w};
+    const float sc[4] = {__builtin_amdgcn_cvt_f32_fp8((int)t.sc, 0), __builtin_amdgcn_cvt_f32_fp8((int)t.sc, 1),
+                         __builtin_amdgcn_cvt_f32_fp8((int)t.sc, 2), __builtin_amdgcn_cvt_f32_fp8((int)t.sc, 3)};
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr) {
-    const float s = __builtin_amdgcn_cvt_f32_fp8((int)t.sc[rr], 0);
-    const v2f d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.code[rr], 1.0f, 0);
-    const v2f d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.code[rr], 1.0f, 1);
-    const v2f d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.code[rr], 1.0f, 2);
-    const v2f d3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.code[rr], 1.0f, 3);
-    const uint32_t m[4] = {pack_bf16_hi(d0[0] * s, d0[1] * s), pack_bf16_hi(d1[0] * s, d1[1] * s),
-                           pack_bf16_hi(d2[0] * s, d2[1] * s), pack_bf16_hi(d3[0] * s, d3[1] * s)};
-    const uint32_t wv[4] = {t.win[rr].x, t.win[rr].y, t.win[rr].z, t.win[rr].w};
+    for (int i = 0; i < 8; ++i)  // chunk i (8 channels) of this thread's 64 uses scale byte i / 2
+      xr[xchunk(8 * c8 + i)] = or4(and4(dequant8(cw[i], sc[i >> 1]), mmask), and4(t.win[i], wmask));
+  } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[rr][i] = (m[i] & t.mmask[rr]) | (wv[i] & t.wmask[rr]);
-    *reinterpret_cast<uint4*>(sm.x + (8 * rg + rr) * kXStride + 8 * cb) =
-        make_uint4(w[rr][0], w[rr][1], w[rr][2], w[rr][3]);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {  // channels 8cb + 2i (low halves) and 8cb + 2i + 1 (high halves)
-    uint32_t lo[4], hi[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      lo[p] = __builtin_amdgcn_perm(w[2 * p + 1][i], w[2 * p][i], 0x05040100u);
-      hi[p] = __builtin_amdgcn_perm(w[2 * p + 1][i], w[2 * p][i], 0x07060302u);
-    }
-    uint2* dst0 = reinterpret_cast<uint2*>(sm.xt + (8 * cb + 2 * i) * kXTStride + 8 * rg);
-    uint2* dst1 = reinterpret_cast<uint2*>(sm.xt + (8 * cb + 2 * i + 1) * kXTStride + 8 * rg);
-    dst0[0] = make_uint2(lo[0], lo[1]);
-    dst0[1] = make_uint2(lo[2], lo[3]);
-    dst1[0] = make_uint2(hi[0], hi[1]);
-    dst1[1] = make_uint2(hi[2], hi[3]);
+    for (int i = 0; i < 8; ++i) xr[xchunk(8 * c8 + i)] = and4(t.win[i], wmask);
   }
 }
 
@@ -208,11 +228,14 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a) {
   for (int seg0 = 0; seg0 < nrows; seg0 += kSeg) {
   const int seg_n = min(kSeg, nrows - seg0);
   lds_barrier();  // the previous segment's sources are no longer read
-  // where every row of this segment comes from (one round of index loads)
-  for (int rl = (int)threadIdx.x; rl < seg_n; rl += kThreads) {
+  // where every row of this segment comes from (one round of index loads); rows
+  // past the segment up to the next tile pair are padding (-1)
+  const int seg_pad = (seg_n + 2 * kRT - 1) / (2 * kRT) * (2 * kRT);
+  for (int rl = (int)threadIdx.x; rl < seg_pad; rl += kThreads) {
     const int r = r_begin + seg0 + rl;
     int src = -1;
-    if (r < a.k) {
+    if (rl >= seg_n) {
+    } else if (r < a.k) {
       const int j = a.topk_idx[(int64_t)qrow * a.k + r];
       if (j >= 0) src = a.block_table[(int64_t)bt_row * a.max_pages + (j >> 6)] * kPage + (j & 63);
     } else {
@@ -226,13 +249,17 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a) {
     smem.src[rl] = src;
   }
   lds_barrier();
+  // kinds of row in the tile at segment row rl0: FP4 entries below k, window rows above
+  auto has_main = [&](int rl0) { return r_begin + seg0 + rl0 < a.k; };
+  auto has_win = [&](int rl0) { return a.window > 0 && r_begin + seg0 + rl0 + kRT > a.k; };
   TileRegs cur;
-  issue_tile(a, smem.src, tid, half * kRT, seg_n, cur);
+  issue_tile(a, smem.src, tid, half * kRT, has_main(half * kRT), has_win(half * kRT), cur);
   for (int pair0 = 0; pair0 < seg_n; pair0 += 2 * kRT) {
     const int row0 = pair0 + half * kRT;  // may lie past seg_n: an empty tile
     lds_barrier();  // previous tile fully consumed
-    store_tile(sm, tid, cur);
-    if (row0 + 2 * kRT < seg_n) issue_tile(a, smem.src, tid, row0 + 2 * kRT, seg_n, cur);  // next tile in flight
+    store_tile(sm, tid, cur, has_main(row0));
+    const int next0 = row0 + 2 * kRT;  // inside the padded sources whenever another pair follows
+    if (pair0 + 2 * kRT < seg_n) issue_tile(a, smem.src, tid, next0, has_main(next0), has_win(next0), cur);
     lds_barrier();
     // ---- partial logits over this wavefront's 128 channels, two 16-row M-tiles
     v4f s[2];
@@ -244,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a) {
         // M row n16 of tile t is tile row 8*(n16/4) + 4t + n16%4, so that lane group g
         // ends up holding the logits of rows 8g .. 8g+7
         const int xrow = 8 * (n16 >> 2) + 4 * t + (n16 & 3);
-        const uint4 xa = *reinterpret_cast<const uint4*>(sm.x + xrow * kXStride + 128 * wid + 32 * ks + 8 * g);
+        const uint4 xa = reinterpret_cast<const uint4*>(sm.x + xrow * kXStride)[xchunk(16 * wid + 4 * ks + g)];
         s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(qop[ks]), s[t], 0, 0, 0);
       }
 #pragma unroll
@@ -264,8 +291,7 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a) {
         z[t][r] = valid ? v * a.scale_log2 : -INFINITY;
         tmax = fmaxf(tmax, z[t][r]);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = max_rows(tmax);
     const float m_new = fmaxf(m_run, tmax);
     const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
     float p[2][4];
@@ -277,8 +303,7 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a) {
         p[t][r] = exp2f(z[t][r] - (m_new == -INFINITY ? 0.0f : m_new));  // exp2(-inf) = 0
         psum += p[t][r];
       }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
+    psum = sum_rows(psum);
     l_run = l_run * alpha + psum;
     m_run = m_new;
     // P^T operand: K slot 8g+i <-> tile row 8g+i = this lane's p[i/4][i%4]
@@ -293,13 +318,18 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a) {
     }
     const bf16x8 Bhi = as_bf16x8(make_uint4(phi[0], phi[1], phi[2], phi[3]));
     const bf16x8 Blo = as_bf16x8(make_uint4(plo[0], plo[1], plo[2], plo[3]));
+    // X^T operand of M-tile mt: lane (n16, g) needs channel 128*wid + 16*mt + n16 of
+    // tile rows 8g .. 8g+7.  In a transposing read, lane 4r + c of each 16-lane group
+    // addresses channels 4c .. 4c+3 of row r and receives channel n16 of rows 0..3.
+    const int tr_c = n16 & 3;
+    const uint16_t* tr_row = sm.x + (8 * g + (n16 >> 2)) * kXStride + 4 * (tr_c & 1);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
       acc[mt] *= alpha;
-      const int ch = 128 * wid + 16 * mt + n16;
-      const uint2 lo4 = *reinterpret_cast<const uint2*>(sm.xt + ch * kXTStride + 8 * g);
-      const uint2 hi4 = *reinterpret_cast<const uint2*>(sm.xt + ch * kXTStride + 8 * g + 4);
-      const bf16x8 A = as_bf16x8(make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+      const uint16_t* tp = tr_row + 8 * xchunk(16 * wid + 2 * mt + (tr_c >> 1));
+      const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)tp);
+      const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tp + 4 * kXStride));
+      const bf16x8 A = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bhi, acc[mt], 0, 0, 0);
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Blo, acc[mt], 0, 0, 0);
     }

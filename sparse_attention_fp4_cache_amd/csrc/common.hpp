@@ -87,4 +87,65 @@ CSA2_DEV void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+
+// ---- cross-lane helpers (one wavefront of 64 lanes) --------------------------
+
+// Max / sum over the lanes l, l^16, l^32, l^48 with the VALU lane swaps of gfx950:
+// permlane16_swap(v, v) leaves the values of 16-lane rows 2i and 2i+1 in the two
+// results, in that order, in every lane of both rows; permlane32_swap(v, v) does the
+// same for the two halves.  Every lane combines the same operands in the same order.
+CSA2_DEV float max_rows(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+CSA2_DEV float sum_rows(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// DPP lane exchanges within 16-lane rows (quad_perm [1,0,3,2], [2,3,0,1],
+// row_half_mirror, row_mirror): after the four steps every lane of a row holds the
+// row's max / sum, combined in the same order in every lane.
+template <int kCtrl>
+CSA2_DEV float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, true));
+}
+CSA2_DEV float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return max_rows(v);
+}
+CSA2_DEV float wave_sum(float v) {
+  v = v + dpp_f<0xB1>(v);
+  v = v + dpp_f<0x4E>(v);
+  v = v + dpp_f<0x141>(v);
+  v = v + dpp_f<0x140>(v);
+  return sum_rows(v);
+}
+
+// DPP row shift / row broadcast of a u32 (0 where the source lane is outside the
+// row, or the lane's row is masked off).
+template <int kCtrl, int kRowMask = 0xF>
+CSA2_DEV uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 within each 16-lane
+// row, then lane 15 of rows 0 / 2 into rows 1 / 3 and lane 31 into rows 2 and 3.
+CSA2_DEV uint32_t wave_incl_scan(uint32_t v) {
+  v += dpp_u32<0x111>(v);
+  v += dpp_u32<0x112>(v);
+  v += dpp_u32<0x114>(v);
+  v += dpp_u32<0x118>(v);
+  v += dpp_u32<0x142, 0xA>(v);
+  v += dpp_u32<0x143, 0xC>(v);
+  return v;
+}
+
 }  // namespace csa2

@@ -261,7 +261,8 @@ CSA2_DEV float exact_entry(const QStage<MT>& s, const uint8_t* __restrict__ idx_
 }
 
 // HIST (one query per workgroup only): also fill the query's digit-1 histogram
-// hist[q][kTopkBins] of the selection that follows, when n_visible[q] > k.
+// (copy blockIdx.x % kTopkHistCopies of hist[q]) of the selection that follows, when
+// n_visible[q] > k.
 template <int MT, int QT, bool HIST>
 __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __restrict__ idx_codes,
                                                           const uint8_t* __restrict__ idx_scales,
@@ -434,7 +435,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
   }  // gfirst < gend
   if (HIST && hist_on) {  // every wavefront is done: add the workgroup's counts
     __syncthreads();
-    uint32_t* gh = hist + (size_t)q0 * kTopkBins;
+    uint32_t* gh = hist + ((size_t)q0 * kTopkHistCopies + blockIdx.x % kTopkHistCopies) * kTopkBins;
 #pragma unroll
     for (int i = 0; i < kTopkBins / kThreads; ++i) {
       const uint32_t c = lh[tid + i * kThreads];

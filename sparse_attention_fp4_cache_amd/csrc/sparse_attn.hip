@@ -91,23 +91,6 @@ CSA2_DEV uint32_t pack_bf16_hi(float lo, float hi) {  // exact values only (low 
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
 }
 
-// Max / sum over the lanes l, l^16, l^32, l^48 with the VALU lane swaps of gfx950:
-// permlane16_swap(v, v) leaves the values of 16-lane rows 2i and 2i+1 in the two
-// results, in that order, in every lane of both rows; permlane32_swap(v, v) does the
-// same for the two halves.  Every lane combines the same operands in the same order.
-CSA2_DEV float max_rows(float v) {
-  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-  p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-CSA2_DEV float sum_rows(float v) {
-  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-  p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-
 CSA2_DEV uint32_t bf16_rne_bits(float f) {  // fp32 -> bf16 bits, round to nearest even (finite f)
   uint32_t u = __float_as_uint(f);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
@@ -389,79 +372,71 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a) {
 }
 
 // Combine the row ranges of one (query, head): out = sum_s 2^(m_s-M) O_s / L.
-// 512 threads: four groups of 128 each sum a quarter of the ranges in a fixed order,
-// then the groups are added in a fixed order.  The first batch of O_s loads is issued
-// before the weights are known, so the two rounds of loads overlap.
-constexpr int kMergeMaxSplits = 256;
-constexpr int kMergeBatch = 8;  // ranges per group per round of loads
-__global__ __launch_bounds__(512) void attn_merge_kernel(AttnArgs a) {
-  __shared__ float wgt[kMergeMaxSplits];
-  __shared__ float4 part[3][128];
-  __shared__ float Ms, Ls;
-  const int head = blockIdx.x, qrow = blockIdx.y, tid = threadIdx.x;
-  const int grp = tid >> 7, t = tid & 127;
-  const int64_t base = (int64_t)qrow * a.nsplit * a.H + head;  // + s * H
-  const float4* po = reinterpret_cast<const float4*>(a.part_o);
-  float4 v[kMergeBatch];
+// Four wavefronts per (query, head), each owning 128 channels (two per lane).  With
+// at most B <= 64 ranges a wavefront issues the loads of every range's O_s at once
+// (unconditional: addresses past the last range are clamped to it, weight 0)
+// together with lane s's (m_s, l_s), takes M and L with wave reductions, and sums
+// the ranges in index order with one fma chain per channel: one round of loads, no
+// LDS, no barrier.  More ranges take rounds of 64.
+constexpr int kMergeThreads = 256;
+template <int B>
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
+  const int head = blockIdx.x, qrow = blockIdx.y;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int ns = a.nsplit;
+  const int64_t base = (int64_t)qrow * ns * a.H + head;  // + s * H
+  const float2* po = reinterpret_cast<const float2*>(a.part_o) + 64 * wv + lane;  // + pidx * 256
+  auto ml_of = [&](int s) { return *reinterpret_cast<const float2*>(a.part_ml + 2 * (base + (int64_t)s * a.H)); };
+  float2 o = make_float2(0.f, 0.f);
+  float M, L = 0.0f;
+  auto accumulate = [&](const float2 (&v)[B], float w) {
 #pragma unroll
-  for (int u = 0; u < kMergeBatch; ++u) {  // ranges grp, grp + 4, ... of the first round
-    const int s = grp + 4 * u;
-    v[u] = (s < a.nsplit) ? po[(base + (int64_t)s * a.H) * (kLatentDim / 4) + t] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  if (tid < 64) {
-    float M = -INFINITY;
-    for (int s = tid; s < a.nsplit; s += 64) M = fmaxf(M, a.part_ml[2 * (base + (int64_t)s * a.H)]);
-    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    float L = 0.0f;
-    for (int s = tid; s < a.nsplit; s += 64) {
-      const int64_t pidx = base + (int64_t)s * a.H;
-      const float ms = a.part_ml[2 * pidx];
-      const float w = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
-      wgt[s] = w;
-      L += a.part_ml[2 * pidx + 1] * w;
+    for (int u = 0; u < B; ++u) {
+      const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
+      o.x = fmaf(v[u].x, wu, o.x);
+      o.y = fmaf(v[u].y, wu, o.y);
     }
-    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
-    if (tid == 0) {
-      Ms = M;
-      Ls = L;
-    }
-  }
-  __syncthreads();
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = grp;; s0 += 4 * kMergeBatch) {
+  };
+  if (ns <= B) {
+    float2 v[B];
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) {
-      const int s = s0 + 4 * u;
-      const float w = (s < a.nsplit) ? wgt[s] : 0.0f;
-      o.x += v[u].x * w;
-      o.y += v[u].y * w;
-      o.z += v[u].z * w;
-      o.w += v[u].w * w;
-    }
-    const int s1 = s0 + 4 * kMergeBatch;
-    if (s1 >= a.nsplit) break;
+    for (int u = 0; u < B; ++u) v[u] = po[(base + (int64_t)min(u, ns - 1) * a.H) * (kLatentDim / 2)];
+    const float2 ml = lane < ns ? ml_of(lane) : make_float2(-INFINITY, 0.0f);
+    M = wave_max(ml.x);
+    const float w = (ml.x == -INFINITY) ? 0.0f : exp2f(ml.x - M);
+    L = wave_sum(ml.y * w);
+    accumulate(v, w);
+  } else {
+    M = -INFINITY;
+    for (int s0 = 0; s0 < ns; s0 += 64)
+      if (s0 + lane < ns) M = fmaxf(M, ml_of(s0 + lane).x);
+    M = wave_max(M);
+    for (int s0 = 0; s0 < ns; s0 += B) {
+      float2 v[B];
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) {
-      const int s = s1 + 4 * u;
-      v[u] = (s < a.nsplit) ? po[(base + (int64_t)s * a.H) * (kLatentDim / 4) + t] : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int u = 0; u < B; ++u) v[u] = po[(base + (int64_t)min(s0 + u, ns - 1) * a.H) * (kLatentDim / 2)];
+      const float2 ml = (lane < B && s0 + lane < ns) ? ml_of(s0 + lane) : make_float2(-INFINITY, 0.0f);
+      const float w = (ml.x == -INFINITY) ? 0.0f : exp2f(ml.x - M);
+      L += wave_sum(ml.y * w);
+      accumulate(v, w);
     }
   }
-  if (grp > 0) part[grp - 1][t] = o;
-  __syncthreads();
-  if (grp == 0) {
-    for (int g2 = 0; g2 < 3; ++g2) {
-      const float4 p = part[g2][t];
-      o.x += p.x;
-      o.y += p.y;
-      o.z += p.z;
-      o.w += p.w;
-    }
-    const float L = Ls;
-    const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
-    reinterpret_cast<float4*>(a.out + ((int64_t)qrow * a.H + head) * kLatentDim)[t] =
-        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
-    if (t == 0) a.lse[(int64_t)qrow * a.H + head] = (L > 0.0f) ? (Ms + log2f(L)) / kLog2e : -INFINITY;
-  }
+  const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+  reinterpret_cast<float2*>(a.out + ((int64_t)qrow * a.H + head) * kLatentDim)[64 * wv + lane] =
+      make_float2(o.x * inv, o.y * inv);
+  if (threadIdx.x == 0) a.lse[(int64_t)qrow * a.H + head] = (L > 0.0f) ? (M + log2f(L)) / kLog2e : -INFINITY;
+}
+
+static void launch_merge(const AttnArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.H, (unsigned)a.nq), block(kMergeThreads);
+  const int ns = a.nsplit;
+  if (ns <= 8) hipLaunchKernelGGL(attn_merge_kernel<8>, grid, block, 0, stream, a);
+  else if (ns <= 16) hipLaunchKernelGGL(attn_merge_kernel<16>, grid, block, 0, stream, a);
+  else if (ns <= 24) hipLaunchKernelGGL(attn_merge_kernel<24>, grid, block, 0, stream, a);
+  else if (ns <= 32) hipLaunchKernelGGL(attn_merge_kernel<32>, grid, block, 0, stream, a);
+  else if (ns <= 40) hipLaunchKernelGGL(attn_merge_kernel<40>, grid, block, 0, stream, a);
+  else if (ns <= 48) hipLaunchKernelGGL(attn_merge_kernel<48>, grid, block, 0, stream, a);
+  else hipLaunchKernelGGL(attn_merge_kernel<64>, grid, block, 0, stream, a);
 }
 
 // Row ranges per query: enough workgroups to spread a small batch over the chip,
@@ -493,8 +468,7 @@ static int run_attention(AttnArgs a, void* ws, size_t ws_bytes, hipStream_t stre
   }
   const dim3 grid((unsigned)a.nsplit, (unsigned)(a.H / 16), (unsigned)a.nq);
   hipLaunchKernelGGL(sparse_attn_kernel, grid, dim3(kThreads), 0, stream, a);
-  if (a.nsplit > 1)
-    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)a.H, (unsigned)a.nq), dim3(512), 0, stream, a);
+  if (a.nsplit > 1) launch_merge(a, stream);
   return launch_status();
 }
 

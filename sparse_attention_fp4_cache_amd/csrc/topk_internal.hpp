@@ -9,8 +9,13 @@ namespace csa2 {
 
 constexpr int kTopkBins = 4096;      // digit-1 bins: the top 12 bits of the score key
 constexpr int kTopkBinShift = 20;
+// Copies of each query's digit-1 histogram: workgroup w adds its counts into copy
+// w % kTopkHistCopies and the selection sums the copies.  Hundreds of workgroups
+// adding into one copy serialise on the same few hot bins; four copies remove that.
+constexpr int kTopkHistCopies = 4;
 
-// Per-query digit-1 histograms ([nq][kTopkBins] u32) inside a top-k workspace.
+// Per-query digit-1 histograms ([nq][kTopkHistCopies][kTopkBins] u32) inside a
+// top-k workspace.
 uint32_t* topk_digit1_hist(void* ws, int32_t nq, int64_t ld);
 
 // Enqueue the selection; with hist_done the digit-1 histograms are already filled

@@ -8,9 +8,10 @@
 // largest 64-bit composites (key << 32) | (0xFFFFFFFF - index), which are all
 // distinct, so the answer is unique.  Two launches over a grid of
 // (chunks of 4096 consecutive scores) x (queries):
-//   1. hist   : 4096-bin histogram of the top 12 key bits (digit 1), added to a
-//               per-query global histogram (index_topk folds this pass into the
-//               scoring pass).
+//   1. hist   : 4096-bin histogram of the top 12 key bits (digit 1), added to one
+//               of four copies of a per-query global histogram (by workgroup
+//               index; the select pass sums them).  index_topk folds this pass into
+//               the scoring pass.
 //   2. select : every workgroup finds the threshold bin b* of digit 1 (where the
 //               running count from the top reaches k), writes the composites of its
 //               entries in bins >= b* -- in index order -- to its own fixed region
@@ -51,7 +52,7 @@ static_assert(sizeof(TopkCtl) == 64, "TopkCtl is 64 bytes");
 
 struct TopkWs {
   TopkCtl* ctl;              // [nq]
-  uint32_t* hist;            // [nq][kBins]: digit 1 (key bits 31..20)
+  uint32_t* hist;            // [nq][kTopkHistCopies][kBins]: digit 1 (key bits 31..20)
   uint32_t* hist2;           // [nq][kBins]: digit 2 (key bits 19..8) of the b* entries
   uint32_t* count;           // [nq][nchunk]: entries of the chunk in bins >= b*
   unsigned long long* list;  // [nq][kListCap]: chunk c's entries at c * (kListCap / nch)
@@ -60,7 +61,8 @@ struct TopkWs {
 __host__ __device__ inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 __host__ __device__ inline size_t ws_bytes_for(int nq, long long nchunk) {
-  return align_up(sizeof(TopkCtl) * (size_t)nq) + 2 * align_up(sizeof(uint32_t) * kBins * (size_t)nq) +
+  return align_up(sizeof(TopkCtl) * (size_t)nq) + align_up(sizeof(uint32_t) * kBins * kTopkHistCopies * (size_t)nq) +
+         align_up(sizeof(uint32_t) * kBins * (size_t)nq) +
          align_up(sizeof(uint32_t) * (size_t)nchunk * (size_t)nq) +
          align_up(sizeof(unsigned long long) * kListCap * (size_t)nq);
 }
@@ -71,7 +73,7 @@ __host__ __device__ inline TopkWs carve(void* base, int nq, long long nchunk) {
   w.ctl = (TopkCtl*)p;
   p += align_up(sizeof(TopkCtl) * (size_t)nq);
   w.hist = (uint32_t*)p;
-  p += align_up(sizeof(uint32_t) * kBins * (size_t)nq);
+  p += align_up(sizeof(uint32_t) * kBins * kTopkHistCopies * (size_t)nq);
   w.hist2 = (uint32_t*)p;
   p += align_up(sizeof(uint32_t) * kBins * (size_t)nq);
   w.count = (uint32_t*)p;
@@ -91,95 +93,109 @@ template <typename T>
 CSA2_DEV void st_agent(T* p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 template <typename T>
 CSA2_DEV T ld_agent(T* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+// 16 bytes at byte offset `off` of a buffer of `num_bytes` bytes, read with the sc1
+// cache policy (the coherence of the agent-scope accesses above).  A raw buffer
+// descriptor: dword 3 = 0x00020000 is the gfx9 format word for plain 32-bit data;
+// offsets at or past num_bytes read zeros instead of faulting.
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+constexpr int kCpolSc1 = 16;
+CSA2_DEV uint4 ld_agent16(const void* base, uint32_t num_bytes, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
+  const v4u32 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSc1);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 CSA2_DEV void wait_all_memory() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// This thread's kPer consecutive keys of a chunk, all loads in flight together.
+// This thread's kPer consecutive keys of a chunk, all loads in flight together:
+// two 16-byte loads when the row is 16-byte aligned and the chunk is whole.
 CSA2_DEV void load_keys(const float* __restrict__ row, int64_t base, int64_t n, uint32_t (&key)[kPer]) {
   float v[kPer];
+  const int64_t j0 = base + (int64_t)threadIdx.x * kPer;
+  if (((reinterpret_cast<uintptr_t>(row) & 15u) == 0) && base + kChunk <= n) {
+    const float4 a = reinterpret_cast<const float4*>(row + j0)[0], b = reinterpret_cast<const float4*>(row + j0)[1];
+    v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+  } else {
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int64_t j = base + (int64_t)threadIdx.x * kPer + i;
-    v[i] = (j < n) ? row[j] : 0.0f;
+    for (int i = 0; i < kPer; ++i) v[i] = (j0 + i < n) ? row[j0 + i] : 0.0f;
   }
 #pragma unroll
   for (int i = 0; i < kPer; ++i) key[i] = score_key(v[i]);
 }
 
-// Block-wide inclusive scan (kThreads threads) of one value per thread: wave scans
-// and one LDS exchange.  wsum: kWaves u32 of LDS.
+// Block-wide inclusive scan (kThreads threads) of one value per thread: DPP wave
+// scans and one LDS exchange behind one LDS-only barrier (loads, stores and atomics
+// in flight stay in flight).  wsum: kWaves u32 of LDS that no
+// thread may write again before every thread has passed the next barrier (callers
+// alternate between two such areas).
 CSA2_DEV uint32_t block_inclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
+  v = wave_incl_scan(v);
   if (lane == 63) wsum[wid] = v;
-  __syncthreads();
+  lds_barrier();
+  const uint4 w0 = reinterpret_cast<const uint4*>(wsum)[0], w1 = reinterpret_cast<const uint4*>(wsum)[1];
+  const uint32_t w[kWaves] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
   uint32_t before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const uint32_t s = wsum[w];
-    before += (w < wid) ? s : 0u;
-    all += s;
+  for (int i = 0; i < kWaves; ++i) {
+    before += (i < wid) ? w[i] : 0u;
+    all += w[i];
   }
-  __syncthreads();
   *total = all;
   return v + before;
 }
+static_assert(kWaves == 8, "block_inclusive_scan reads 8 wave sums");
 
-// Copy kBins counters into LDS with every load in flight before the first store
-// (a strided loop would wait for each load in turn).
-template <bool kCoherent>
-CSA2_DEV void load_bins(uint32_t* dst, uint32_t* src) {
-  constexpr int per = kBins / kThreads;
-  uint32_t v[per];
-#pragma unroll
-  for (int i = 0; i < per; ++i) {
-    uint32_t* p = src + threadIdx.x + i * kThreads;
-    v[i] = kCoherent ? ld_agent(p) : *p;
-  }
-#pragma unroll
-  for (int i = 0; i < per; ++i) dst[threadIdx.x + i * kThreads] = v[i];
-}
+constexpr int kPerBins = kBins / kThreads;  // bins per thread in a digit search
 
-// Histogram h[0..kBins) in LDS: digit D with count(digit > D) < need <= count(digit >= D).
-// Returns D; *above = count(digit > D).  Requires 1 <= need <= total count.
-CSA2_DEV int find_digit(const uint32_t* h, uint32_t need, uint32_t* wsum, int* dig_s, uint32_t* above_s,
-                        uint32_t* above) {
-  constexpr int per = kBins / kThreads;
-  const int t = threadIdx.x;
-  // thread t owns bins [kBins - per*(t+1), kBins - per*t): threads in order walk the
-  // bins from the top down
-  const int hi = kBins - per * t;
+// Thread t's bins of a digit search: [kBins - 8(t+1), kBins - 8t), so that threads in
+// order walk the bins from the top down.
+CSA2_DEV int bins_lo() { return kBins - kPerBins * ((int)threadIdx.x + 1); }
+
+struct Digit {
+  int d;           // the digit
+  uint32_t above;  // count in digits above it
+  uint32_t cnt;    // count in it
+};
+
+// Digit D with count(digit > D) < need <= count(digit >= D) of a histogram whose
+// bins [bins_lo(), bins_lo() + 8) this thread holds in h (ascending).  Requires
+// 1 <= need <= total count.  res: LDS slot written by one thread before the barrier
+// and read by all after it; wsum as for block_inclusive_scan.
+CSA2_DEV Digit find_digit(const uint32_t (&h)[kPerBins], uint32_t need, uint32_t* wsum, Digit* res) {
   uint32_t s = 0;
 #pragma unroll
-  for (int i = 1; i <= per; ++i) s += h[hi - i];
+  for (int i = 0; i < kPerBins; ++i) s += h[i];
   uint32_t total;
-  const uint32_t incl = block_inclusive_scan(s, wsum, &total);  // count in bins >= hi - per
-  const uint32_t excl = incl - s;                                // count in bins >= hi
+  const uint32_t incl = block_inclusive_scan(s, wsum, &total);  // count in bins >= bins_lo()
+  const uint32_t excl = incl - s;                                // count in bins above them
   if (excl < need && need <= incl) {
     uint32_t acc = excl;
-    for (int i = 1; i <= per; ++i) {
-      const uint32_t c = h[hi - i];
-      if (acc + c >= need) {
-        *dig_s = hi - i;
-        *above_s = acc;
-        break;
+    bool found = false;
+#pragma unroll
+    for (int i = kPerBins - 1; i >= 0; --i) {
+      if (!found && acc + h[i] >= need) {
+        *res = Digit{bins_lo() + i, acc, h[i]};
+        found = true;
       }
-      acc += c;
+      acc += h[i];
     }
   }
-  __syncthreads();
-  const int D = *dig_s;
-  *above = *above_s;
-  __syncthreads();
-  return D;
+  lds_barrier();
+  return *res;
 }
+
+// This thread's bins of an LDS histogram, for find_digit.
+CSA2_DEV void bins_from_lds(const uint32_t* h, uint32_t (&v)[kPerBins]) {
+  const uint4 a = reinterpret_cast<const uint4*>(h + bins_lo())[0], b = reinterpret_cast<const uint4*>(h + bins_lo())[1];
+  v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+}
+static_assert(kPerBins == 8, "digit searches hold 8 bins per thread");
 
 // ---------------------------------------------------------------- kernel 1 --
 __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __restrict__ scores, int64_t ld,
@@ -198,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __rest
   for (int i = 0; i < kPer; ++i)
     if (base + (int64_t)tid * kPer + i < n) atomicAdd(&lh[key[i] >> kBinShift], 1u);
   __syncthreads();
-  uint32_t* gh = ws.hist + (size_t)q * kBins;
+  uint32_t* gh = ws.hist + ((size_t)q * kTopkHistCopies + blockIdx.x % kTopkHistCopies) * kBins;
   for (int b = tid; b < kBins; b += kThreads) {
     const uint32_t c = lh[b];
     if (c) atomicAdd(&gh[b], c);
@@ -206,13 +222,15 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __rest
 }
 
 struct SelectSmem {
-  uint32_t h[kBins];
-  unsigned long long list[kListCap];
+  uint32_t h[kBins];                  // LDS histogram of the radix rounds (rare)
+  unsigned long long list[kListCap];  // the listed entries of a query, in index order
   uint32_t cpos[kMaxChunksFast + 1];  // chunk -> first position in the ordered list
-  uint32_t wsum[kWaves];
-  uint32_t above_s, ovf, more;
-  int dig_s, is_last;
-  unsigned long long min_s;
+  uint32_t wsum[4][kWaves];           // wave sums of block scans (used in rotation)
+  Digit dig[4];                       // digit-search results (used in rotation)
+  unsigned long long cand[64];        // the few candidates under the boundary prefix
+  uint32_t ncand, ovf, more;
+  int is_last;
+  unsigned long long min_s, bnd_s;
 };
 
 // Candidates of the boundary: the listed entries in LDS, or (slow path) the score row.
@@ -245,35 +263,57 @@ template <typename Src>
 CSA2_DEV unsigned long long select_boundary(const Src& src, uint32_t need, unsigned long long prefix, int hi,
                                             uint32_t cnt, SelectSmem& sm) {
   const int tid = threadIdx.x;
+  int parity = 0;
   while (true) {
     if (cnt == need || hi == 0) {  // all of them are in: the boundary is their minimum
       if (hi == 0) return prefix;
       if (tid == 0) sm.min_s = ~0ull;
-      __syncthreads();
+      lds_barrier();
       src.each([&](unsigned long long x) {
         if ((x >> hi) == prefix) atomicMin(&sm.min_s, x);
       });
-      __syncthreads();
+      lds_barrier();
       const unsigned long long m = sm.min_s;
-      __syncthreads();
+      lds_barrier();
       return m;
     }
     const int width = hi >= 12 ? 12 : hi;
     const int lo = hi - width;
     for (int b = tid; b < kBins; b += kThreads) sm.h[b] = 0;
-    __syncthreads();
+    lds_barrier();
     src.each([&](unsigned long long x) {
       if ((x >> hi) == prefix) atomicAdd(&sm.h[(int)((x >> lo) & ((1ull << width) - 1))], 1u);
     });
-    __syncthreads();
-    uint32_t above;
-    const int D = find_digit(sm.h, need, sm.wsum, &sm.dig_s, &sm.above_s, &above);
-    cnt = sm.h[D];
-    __syncthreads();
-    need -= above;
-    prefix = (prefix << width) | (unsigned long long)D;
+    lds_barrier();
+    uint32_t hv[kPerBins];
+    bins_from_lds(sm.h, hv);
+    const Digit D = find_digit(hv, need, sm.wsum[2 + parity], &sm.dig[2 + parity]);
+    parity ^= 1;
+    cnt = D.cnt;
+    need -= D.above;
+    prefix = (prefix << width) | (unsigned long long)D.d;
     hi = lo;
   }
+}
+
+// The need-th largest of the (at most 64) listed entries under a 24-bit key prefix:
+// they are gathered into LDS, and one wavefront ranks every one against the others.
+CSA2_DEV unsigned long long small_boundary(const unsigned long long* list, int total, unsigned long long prefix,
+                                           uint32_t need, SelectSmem& sm) {
+  for (int i = threadIdx.x; i < total; i += kThreads) {
+    const unsigned long long x = list[i];
+    if ((x >> 40) == prefix) sm.cand[atomicAdd(&sm.ncand, 1u)] = x;
+  }
+  lds_barrier();
+  if (threadIdx.x < 64) {
+    const int nc = (int)sm.ncand, lane = threadIdx.x;
+    const unsigned long long mine = lane < nc ? sm.cand[lane] : 0ull;
+    uint32_t rank = 0;  // candidates above this one
+    for (int j = 0; j < nc; ++j) rank += sm.cand[j] > mine ? 1u : 0u;
+    if (lane < nc && rank == need - 1) sm.bnd_s = mine;
+  }
+  lds_barrier();
+  return sm.bnd_s;
 }
 
 // Ordered compaction of the list entries >= boundary into out[0..k): every
@@ -296,7 +336,7 @@ CSA2_DEV void compact_list(const unsigned long long* list, int total, unsigned l
 #pragma unroll
   for (int j = 0; j < kIt; ++j) cnt += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(x[j] >= boundary));
   if (lane == 0) wsum[wid] = cnt;
-  __syncthreads();
+  lds_barrier();
   uint32_t pos = 0;
   for (int w = 0; w < wid; ++w) pos += wsum[w];
 #pragma unroll
@@ -307,7 +347,7 @@ CSA2_DEV void compact_list(const unsigned long long* list, int total, unsigned l
     if (keep && o < (uint32_t)k) out[o] = (int32_t)index_of(x[j]);
     pos += (uint32_t)__popcll(m);
   }
-  __syncthreads();  // wsum is reused by the caller
+  lds_barrier();  // wsum is reused by the caller
 }
 
 // ---------------------------------------------------------------- kernel 2 --
@@ -328,9 +368,9 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
   }
   if (base >= n) return;
   const int nch = (int)((n + kChunk - 1) / kChunk);
-  const int cap = kListCap / nch;  // region of each chunk in the list (0: always the slow path)
+  const int cap = (kListCap / nch) & ~1;  // region of each chunk in the list (0: always the slow path)
   TopkCtl* ctl = ws.ctl + q;
-  uint32_t* gh = ws.hist + (size_t)q * kBins;
+  uint32_t* gh = ws.hist + (size_t)q * kTopkHistCopies * kBins;  // its copies, kBins apart
   uint32_t* gh2 = ws.hist2 + (size_t)q * kBins;
   uint32_t* gcount = ws.count + (size_t)q * nchunk;
   unsigned long long* glist = ws.list + (size_t)q * kListCap;
@@ -338,11 +378,24 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
 
   uint32_t key[kPer];
   load_keys(row, base, n, key);
-  load_bins<false>(sm.h, gh);
-  if (tid == 0) sm.dig_s = 0;
-  __syncthreads();
-  uint32_t above_b;
-  const uint32_t bstar = (uint32_t)find_digit(sm.h, (uint32_t)k, sm.wsum, &sm.dig_s, &sm.above_s, &above_b);
+  uint32_t hb[kPerBins];
+  {
+    uint4 h[kTopkHistCopies][2];
+#pragma unroll
+    for (int r = 0; r < kTopkHistCopies; ++r) {
+      h[r][0] = reinterpret_cast<const uint4*>(gh + r * kBins + bins_lo())[0];
+      h[r][1] = reinterpret_cast<const uint4*>(gh + r * kBins + bins_lo())[1];
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint4 t = h[0][j];
+#pragma unroll
+      for (int r = 1; r < kTopkHistCopies; ++r) t = make_uint4(t.x + h[r][j].x, t.y + h[r][j].y, t.z + h[r][j].z, t.w + h[r][j].w);
+      hb[4 * j] = t.x, hb[4 * j + 1] = t.y, hb[4 * j + 2] = t.z, hb[4 * j + 3] = t.w;
+    }
+  }
+  const Digit d1 = find_digit(hb, (uint32_t)k, sm.wsum[0], &sm.dig[0]);
+  const uint32_t bstar = (uint32_t)d1.d, above_b = d1.above;
 
   // this chunk's entries in bins >= b*, in index order, into its region; its b*
   // entries also go into the digit-2 histogram
@@ -355,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
     if (vis && bin == bstar) atomicAdd(&gh2[(key[i] >> 8) & (kBins - 1)], 1u);
   }
   uint32_t tot;
-  const uint32_t off = block_inclusive_scan((uint32_t)__popc(m), sm.wsum, &tot) - (uint32_t)__popc(m);
+  const uint32_t off = block_inclusive_scan((uint32_t)__popc(m), sm.wsum[1], &tot) - (uint32_t)__popc(m);
   uint32_t p = off;
   unsigned long long* region = glist + (size_t)blockIdx.x * cap;
 #pragma unroll
@@ -374,69 +427,77 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
   // ---- last workgroup of this query: every region, count and histogram is in place
   const uint32_t need = (uint32_t)k - above_b;  // 1 <= need <= entries in b*
   // one round of device-coherent loads: the chunk counts, the digit-2 histogram and
-  // the first 64 slots of the regions of up to 16 chunks per wavefront (read before
-  // the counts say how many are filled; only the filled ones are kept)
-  constexpr int kG = 16;
+  // the first kSpec slots of the regions of the first kSpecChunks chunks (thread t:
+  // 8 slots of chunk t / 4), read before the counts say how many are filled; only
+  // the filled ones are kept.  Slots past the list read zeros.
+  constexpr int kSpec = 32;
+  constexpr int kSpecChunks = kThreads * 8 / kSpec;
   const bool one_pass = nch <= kThreads;  // rows up to 2M entries
   const uint32_t my_cnt = (one_pass && tid < nch) ? ld_agent(gcount + tid) : 0u;
-  uint32_t h2[kBins / kThreads];
+  uint32_t h2[kPerBins];
+  {
+    const uint4 a0 = ld_agent16(gh2, kBins * 4u, (uint32_t)bins_lo() * 4u);
+    const uint4 a1 = ld_agent16(gh2, kBins * 4u, (uint32_t)bins_lo() * 4u + 16u);
+    h2[0] = a0.x, h2[1] = a0.y, h2[2] = a0.z, h2[3] = a0.w, h2[4] = a1.x, h2[5] = a1.y, h2[6] = a1.z, h2[7] = a1.w;
+  }
+  const int spec_c = tid >> 2, spec_s0 = 8 * (tid & 3);
+  unsigned long long spec[8];
 #pragma unroll
-  for (int i = 0; i < kBins / kThreads; ++i) h2[i] = ld_agent(gh2 + tid + i * kThreads);
-  unsigned long long spec[kG];
-#pragma unroll
-  for (int u = 0; u < kG; ++u) {
-    const int c = wid + u * kWaves;
-    spec[u] = (c < nch && lane < cap) ? ld_agent(glist + (size_t)c * cap + lane) : 0ull;
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = ld_agent16(glist, kListCap * 8u, (uint32_t)(spec_c * cap + spec_s0 + 2 * i) * 8u);
+    spec[2 * i] = ((unsigned long long)v.y << 32) | v.x;
+    spec[2 * i + 1] = ((unsigned long long)v.w << 32) | v.z;
   }
   if (tid == 0) {
     sm.ovf = one_pass ? 0u : 1u;
-    sm.more = nch > kG * kWaves ? 1u : 0u;
+    sm.more = nch > kSpecChunks ? 1u : 0u;
+    sm.ncand = 0u;
   }
-#pragma unroll
-  for (int i = 0; i < kBins / kThreads; ++i) sm.h[tid + i * kThreads] = h2[i];
   uint32_t total = 0;
-  if (one_pass) {
+  if (one_pass) {  // uniform
     uint32_t t2;
-    const uint32_t incl = block_inclusive_scan(my_cnt, sm.wsum, &t2);
+    const uint32_t incl = block_inclusive_scan(my_cnt, sm.wsum[0], &t2);
     if (tid < nch) sm.cpos[tid] = incl - my_cnt;
     if (my_cnt > (uint32_t)cap) sm.ovf = 1u;
-    if (my_cnt > 64u) sm.more = 1u;
+    if (my_cnt > (uint32_t)kSpec) sm.more = 1u;
     total = t2;
     if (tid == 0) sm.cpos[nch] = total;
   }
-  __syncthreads();
+  lds_barrier();
   if (sm.ovf == 0u) {
-    // the regions, in chunk order, into LDS: one wavefront per chunk, lanes across
-    // the chunk's entries
+    // the filled slots, in chunk order, into LDS
+    if (spec_c < nch && spec_c < kSpecChunks) {
+      const uint32_t pos = sm.cpos[spec_c], cn = sm.cpos[spec_c + 1] - pos;
 #pragma unroll
-    for (int u = 0; u < kG; ++u) {
-      const int c = min(wid + u * kWaves, nch);  // clamped: chunks past the end are empty
-      const uint32_t pos = sm.cpos[c], cn = sm.cpos[min(c + 1, nch)] - pos;
-      if ((uint32_t)lane < cn) sm.list[pos + lane] = spec[u];
+      for (int j = 0; j < 8; ++j)
+        if ((uint32_t)(spec_s0 + j) < cn) sm.list[pos + spec_s0 + j] = spec[j];
     }
-    if (sm.more) {  // rare: more than 16 chunks per wavefront, or more than 64 entries in a region
+    if (sm.more) {  // rare: chunks past kSpecChunks, or more than kSpec entries in a region
       for (int c = wid; c < nch; c += kWaves) {
         const uint32_t pos = sm.cpos[c], cn = sm.cpos[c + 1] - pos;
-        const uint32_t from = c < kG * kWaves ? 64u : 0u;
+        const uint32_t from = c < kSpecChunks ? (uint32_t)kSpec : 0u;
         for (uint32_t j = from + lane; j < cn; j += 64) sm.list[pos + j] = ld_agent(glist + (size_t)c * cap + j);
       }
     }
-    __syncthreads();
     // digit 2 of the boundary from the histogram the workgroups built
-    uint32_t above2;
-    const int D2 = find_digit(sm.h, need, sm.wsum, &sm.dig_s, &sm.above_s, &above2);
-    const uint32_t cnt2 = sm.h[D2];
-    __syncthreads();
-    const unsigned long long prefix = ((unsigned long long)bstar << 12) | (unsigned long long)D2;  // key bits 31..8
-    const LdsCands src{sm.list, (int)total};
-    const unsigned long long boundary = select_boundary(src, need - above2, prefix, 40, cnt2, sm);
-    compact_list(sm.list, (int)total, boundary, k, out, sm.wsum);
+    const Digit d2 = find_digit(h2, need, sm.wsum[1], &sm.dig[1]);  // its barriers also publish the list
+    const unsigned long long prefix = ((unsigned long long)bstar << 12) | (unsigned long long)d2.d;  // key bits 31..8
+    const uint32_t need2 = need - d2.above;
+    unsigned long long boundary;
+    if (d2.cnt <= 64u) {
+      boundary = small_boundary(sm.list, (int)total, prefix, need2, sm);
+    } else {
+      const LdsCands src{sm.list, (int)total};
+      boundary = select_boundary(src, need2, prefix, 40, d2.cnt, sm);
+    }
+    compact_list(sm.list, (int)total, boundary, k, out, sm.wsum[0]);
   } else {
     // slow path (a region overflowed, or very long rows): boundary from the score
     // row, then an ordered scan of the row, kThreads entries per round
     const RowCands src{row, n, bstar};
     const unsigned long long boundary = select_boundary(src, need, (unsigned long long)bstar, 52, 0xFFFFFFFFu, sm);
     uint32_t written = 0;
+    int parity = 0;
     for (int64_t r0 = 0; r0 < n; r0 += kThreads) {
       const int64_t i = r0 + tid;
       bool keep = false;
@@ -446,14 +507,16 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
         keep = bin > bstar || (bin == bstar && composite(kk, (uint32_t)i) >= boundary);
       }
       uint32_t t2;
-      const uint32_t incl = block_inclusive_scan(keep ? 1u : 0u, sm.wsum, &t2);
+      const uint32_t incl = block_inclusive_scan(keep ? 1u : 0u, sm.wsum[parity], &t2);
+      parity ^= 1;
       if (keep && written + incl - 1 < (uint32_t)k) out[written + incl - 1] = (int32_t)i;
       written += t2;
     }
   }
   // leave the workspace clean for the next call
   for (int b = tid; b < kBins; b += kThreads) {
-    gh[b] = 0u;
+#pragma unroll
+    for (int r = 0; r < kTopkHistCopies; ++r) gh[r * kBins + b] = 0u;
     gh2[b] = 0u;
   }
   if (tid == 0) ctl->arrive = 0u;

@@ -47,6 +47,12 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 constexpr int kRT = 32;              // rows per tile
 constexpr int kXStride = 512 + 8;    // bf16 elements per row of X in LDS (padding vs bank conflicts)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 2^x with V_EXP_F32 alone: exact where the library exp2f is (results of normal
+// magnitude), it only skips the library's rescaling for results below 2^-126, which
+// weigh nothing here.
+CSA2_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 struct AttnArgs {
   const uint8_t* main_codes;
@@ -85,7 +91,11 @@ struct __align__(16) AttnSmem {
 };
 static_assert(sizeof(AttnSmem) <= 160 * 1024, "attention LDS exceeds 160 KB");
 // the second half's tile area holds its softmax state for the final combine
-static_assert(sizeof(float4) * 4 * 8 * 64 + sizeof(float) * 2 * 4 * 64 <= sizeof(HalfSmem), "combine area");
+// at the end each half's tile area holds its O as [16 heads][kOStride floats], and
+// the first half's logit area the (m, l) of both halves
+constexpr int kOStride = kLatentDim + 4;  // floats per head row (rows start 4 banks apart)
+static_assert(16 * kOStride * sizeof(float) <= sizeof(HalfSmem::x), "combine area");
+static_assert(2 * 16 * 2 * sizeof(float) <= sizeof(HalfSmem::red), "combine (m, l) area");
 
 CSA2_DEV uint32_t pack_bf16_hi(float lo, float hi) {  // exact values only (low 16 bits zero)
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
@@ -276,14 +286,14 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a) {
       }
     tmax = max_rows(tmax);
     const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
+    const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
     float p[2][4];
     float psum = 0.0f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[t][r] = exp2f(z[t][r] - (m_new == -INFINITY ? 0.0f : m_new));  // exp2(-inf) = 0
+        p[t][r] = fast_exp2(z[t][r] - (m_new == -INFINITY ? 0.0f : m_new));  // exp2(-inf) = 0
         psum += p[t][r];
       }
     psum = sum_rows(psum);
@@ -320,53 +330,59 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a) {
 
   }  // segments
 
-  // ---- combine the halves: the second half parks (O, m, l) in its tile area, the
-  // first half rescales both to the larger running maximum and adds them
+  // ---- combine the halves and write.  Each half leaves its O in its own tile area
+  // as [head][channel] and its (m, l) per head next to it; then all 512 threads
+  // rescale both halves to the larger running maximum, add them and write whole
+  // 2 KB rows of the output.
   lds_barrier();  // every tile consumed
-  float4* park = reinterpret_cast<float4*>(smem.h[1].x);  // [wid][mt][lane]
-  float* park_ml = reinterpret_cast<float*>(park + 4 * 8 * 64);  // [2][wid][lane]
-  if (half == 1) {
+  float* o_mine = reinterpret_cast<float*>(sm.x);
+  float* ml = reinterpret_cast<float*>(smem.h[0].red);  // [half][16 heads][m, l]
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-      park[(wid * 8 + mt) * 64 + lane] = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
-    park_ml[wid * 64 + lane] = m_run;
-    park_ml[256 + wid * 64 + lane] = l_run;
+  for (int mt = 0; mt < 8; ++mt)
+    *reinterpret_cast<float4*>(o_mine + n16 * kOStride + 128 * wid + 16 * mt + 4 * g) =
+        make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+  if (wid == 0 && g == 0) {
+    ml[(half * 16 + n16) * 2] = m_run;
+    ml[(half * 16 + n16) * 2 + 1] = l_run;
   }
   lds_barrier();
-  if (half == 1) return;
-  {
-    const float m1 = park_ml[wid * 64 + lane], l1 = park_ml[256 + wid * 64 + lane];
-    const float M = fmaxf(m_run, m1);
-    const float a0 = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - M);
-    const float a1 = (m1 == -INFINITY) ? 0.0f : exp2f(m1 - M);
+  const float* o0 = reinterpret_cast<const float*>(smem.h[0].x);
+  const float* o1 = reinterpret_cast<const float*>(smem.h[1].x);
+  // thread t: float4 c4 = t % 128 of heads hq, hq + 4, hq + 8, hq + 12 (hq = t / 128);
+  // every LDS read first, then the arithmetic and the stores
+  const int hq = (int)threadIdx.x >> 7, c4 = (int)threadIdx.x & 127;
+  float2 s0[4], s1[4];
+  float4 x0[4], x1[4];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const float4 o1 = park[(wid * 8 + mt) * 64 + lane];
-      acc[mt] = acc[mt] * a0 + v4f{o1.x, o1.y, o1.z, o1.w} * a1;
-    }
-    l_run = l_run * a0 + l1 * a1;
-    m_run = M;
+  for (int i = 0; i < 4; ++i) {
+    const int hh = hq + 4 * i;
+    s0[i] = *reinterpret_cast<const float2*>(ml + hh * 2);
+    s1[i] = *reinterpret_cast<const float2*>(ml + (16 + hh) * 2);
+    x0[i] = *reinterpret_cast<const float4*>(o0 + hh * kOStride + 4 * c4);
+    x1[i] = *reinterpret_cast<const float4*>(o1 + hh * kOStride + 4 * c4);
   }
-
-  // ---- write: lane holds head `head`, channels 128*wid + 16*mt + 4*g + r
-  if (a.nsplit == 1) {
-    const float inv = (l_run > 0.0f) ? 1.0f / l_run : 0.0f;
-    float* op = a.out + ((int64_t)qrow * a.H + head) * kLatentDim + 128 * wid + 4 * g;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-      *reinterpret_cast<float4*>(op + 16 * mt) =
-          make_float4(acc[mt][0] * inv, acc[mt][1] * inv, acc[mt][2] * inv, acc[mt][3] * inv);
-    if (wid == 0 && g == 0)
-      a.lse[(int64_t)qrow * a.H + head] = (l_run > 0.0f) ? (m_run + log2f(l_run)) / kLog2e : -INFINITY;
-  } else {
-    const int64_t pidx = ((int64_t)qrow * a.nsplit + split) * a.H + head;
-    float* op = a.part_o + pidx * kLatentDim + 128 * wid + 4 * g;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-      *reinterpret_cast<float4*>(op + 16 * mt) = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
-    if (wid == 0 && g == 0) {
-      a.part_ml[2 * pidx] = m_run;
-      a.part_ml[2 * pidx + 1] = l_run;
+  for (int i = 0; i < 4; ++i) {
+    const float m0 = s0[i].x, l0 = s0[i].y, m1 = s1[i].x, l1 = s1[i].y;
+    const float M = fmaxf(m0, m1);
+    const float a0 = (m0 == -INFINITY) ? 0.0f : fast_exp2(m0 - M);
+    const float a1 = (m1 == -INFINITY) ? 0.0f : fast_exp2(m1 - M);
+    const float L = l0 * a0 + l1 * a1;
+    const float4 o = make_float4(x0[i].x * a0 + x1[i].x * a1, x0[i].y * a0 + x1[i].y * a1,
+                                 x0[i].z * a0 + x1[i].z * a1, x0[i].w * a0 + x1[i].w * a1);
+    const int hd = hg * 16 + hq + 4 * i;
+    if (a.nsplit == 1) {
+      const float inv = (L > 0.0f) ? __builtin_amdgcn_rcpf(L) : 0.0f;
+      reinterpret_cast<float4*>(a.out + ((int64_t)qrow * a.H + hd) * kLatentDim)[c4] =
+          make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+      if (c4 == 0) a.lse[(int64_t)qrow * a.H + hd] = (L > 0.0f) ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
+    } else {
+      const int64_t pidx = ((int64_t)qrow * a.nsplit + split) * a.H + hd;
+      reinterpret_cast<float4*>(a.part_o + pidx * kLatentDim)[c4] = o;
+      if (c4 == 0) {
+        a.part_ml[2 * pidx] = M;
+        a.part_ml[2 * pidx + 1] = L;
+      }
     }
   }
 }
@@ -403,7 +419,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     for (int u = 0; u < B; ++u) v[u] = po[(base + (int64_t)min(u, ns - 1) * a.H) * (kLatentDim / 2)];
     const float2 ml = lane < ns ? ml_of(lane) : make_float2(-INFINITY, 0.0f);
     M = wave_max(ml.x);
-    const float w = (ml.x == -INFINITY) ? 0.0f : exp2f(ml.x - M);
+    const float w = (ml.x == -INFINITY) ? 0.0f : fast_exp2(ml.x - M);
     L = wave_sum(ml.y * w);
     accumulate(v, w);
   } else {
@@ -416,15 +432,15 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < B; ++u) v[u] = po[(base + (int64_t)min(s0 + u, ns - 1) * a.H) * (kLatentDim / 2)];
       const float2 ml = (lane < B && s0 + lane < ns) ? ml_of(s0 + lane) : make_float2(-INFINITY, 0.0f);
-      const float w = (ml.x == -INFINITY) ? 0.0f : exp2f(ml.x - M);
+      const float w = (ml.x == -INFINITY) ? 0.0f : fast_exp2(ml.x - M);
       L += wave_sum(ml.y * w);
       accumulate(v, w);
     }
   }
-  const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+  const float inv = (L > 0.0f) ? __builtin_amdgcn_rcpf(L) : 0.0f;
   reinterpret_cast<float2*>(a.out + ((int64_t)qrow * a.H + head) * kLatentDim)[64 * wv + lane] =
       make_float2(o.x * inv, o.y * inv);
-  if (threadIdx.x == 0) a.lse[(int64_t)qrow * a.H + head] = (L > 0.0f) ? (M + log2f(L)) / kLog2e : -INFINITY;
+  if (threadIdx.x == 0) a.lse[(int64_t)qrow * a.H + head] = (L > 0.0f) ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
 }
 
 static void launch_merge(const AttnArgs& a, hipStream_t stream) {

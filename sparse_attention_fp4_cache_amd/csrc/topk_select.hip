@@ -322,29 +322,22 @@ CSA2_DEV unsigned long long small_boundary(const unsigned long long* list, int t
 // exchange of the counts writes them at their positions.
 CSA2_DEV void compact_list(const unsigned long long* list, int total, unsigned long long boundary, int k,
                            int32_t* __restrict__ out, uint32_t* wsum) {
-  constexpr int kIt = kListCap / (64 * kWaves);
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int per_w = (((total + kWaves - 1) / kWaves) + 63) & ~63;
   const int s0 = wid * per_w, s1 = min(s0 + per_w, total);
-  unsigned long long x[kIt];
-#pragma unroll
-  for (int j = 0; j < kIt; ++j) {
-    const int e = s0 + 64 * j + lane;
-    x[j] = e < s1 ? list[e] : 0ull;  // 0 is below every boundary
-  }
+  auto entry = [&](int e) { return e < s1 ? list[e] : 0ull; };  // 0 is below every boundary
   uint32_t cnt = 0;
-#pragma unroll
-  for (int j = 0; j < kIt; ++j) cnt += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(x[j] >= boundary));
+  for (int e0 = s0; e0 < s1; e0 += 64) cnt += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(entry(e0 + lane) >= boundary));
   if (lane == 0) wsum[wid] = cnt;
   lds_barrier();
   uint32_t pos = 0;
   for (int w = 0; w < wid; ++w) pos += wsum[w];
-#pragma unroll
-  for (int j = 0; j < kIt; ++j) {
-    const bool keep = x[j] >= boundary;
+  for (int e0 = s0; e0 < s1; e0 += 64) {  // the segment again, from LDS
+    const unsigned long long x = entry(e0 + lane);
+    const bool keep = x >= boundary;
     const unsigned long long m = __builtin_amdgcn_ballot_w64(keep);
     const uint32_t o = pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-    if (keep && o < (uint32_t)k) out[o] = (int32_t)index_of(x[j]);
+    if (keep && o < (uint32_t)k) out[o] = (int32_t)index_of(x);
     pos += (uint32_t)__popcll(m);
   }
   lds_barrier();  // wsum is reused by the caller
@@ -379,6 +372,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
   uint32_t key[kPer];
   load_keys(row, base, n, key);
   uint32_t hb[kPerBins];
+  uint32_t nz1 = 0;  // bit r: one of this thread's bins of copy r is nonzero (cleared at the end)
   {
     uint4 h[kTopkHistCopies][2];
 #pragma unroll
@@ -386,6 +380,12 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
       h[r][0] = reinterpret_cast<const uint4*>(gh + r * kBins + bins_lo())[0];
       h[r][1] = reinterpret_cast<const uint4*>(gh + r * kBins + bins_lo())[1];
     }
+#pragma unroll
+    for (int r = 0; r < kTopkHistCopies; ++r)
+      nz1 |= ((h[r][0].x | h[r][0].y | h[r][0].z | h[r][0].w | h[r][1].x | h[r][1].y | h[r][1].z | h[r][1].w) != 0u
+                  ? 1u
+                  : 0u)
+             << r;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       uint4 t = h[0][j];
@@ -513,11 +513,17 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
       written += t2;
     }
   }
-  // leave the workspace clean for the next call
-  for (int b = tid; b < kBins; b += kThreads) {
+  // leave the workspace clean for the next call: only the runs of 8 bins seen nonzero
+  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-    for (int r = 0; r < kTopkHistCopies; ++r) gh[r * kBins + b] = 0u;
-    gh2[b] = 0u;
+  for (int r = 0; r < kTopkHistCopies; ++r)
+    if (nz1 & (1u << r)) {
+      reinterpret_cast<uint4*>(gh + r * kBins + bins_lo())[0] = z4;
+      reinterpret_cast<uint4*>(gh + r * kBins + bins_lo())[1] = z4;
+    }
+  if ((h2[0] | h2[1] | h2[2] | h2[3] | h2[4] | h2[5] | h2[6] | h2[7]) != 0u) {
+    reinterpret_cast<uint4*>(gh2 + bins_lo())[0] = z4;
+    reinterpret_cast<uint4*>(gh2 + bins_lo())[1] = z4;
   }
   if (tid == 0) ctl->arrive = 0u;
 }

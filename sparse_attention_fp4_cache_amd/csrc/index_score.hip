@@ -261,7 +261,7 @@ CSA2_DEV float exact_entry(const QStage<MT>& s, const uint8_t* __restrict__ idx_
 }
 
 // HIST (one query per workgroup only): also fill the query's digit-1 histogram
-// (copy blockIdx.x % kTopkHistCopies of hist[q]) of the selection that follows, when
+// (copy blockIdx.x % ncopies of hist[q]) of the selection that follows, when
 // n_visible[q] > k.
 template <int MT, int QT, bool HIST>
 __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __restrict__ idx_codes,
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
                                                           const int32_t* __restrict__ block_table, int max_pages,
                                                           int nq, float* __restrict__ scores, int64_t ld,
                                                           int groups_per_wave, int total_groups,
-                                                          uint32_t* __restrict__ hist, int k) {
+                                                          uint32_t* __restrict__ hist, int k, int ncopies) {
   static_assert(!HIST || QT == 1, "the fused histogram serves one query per workgroup");
   constexpr int qt = QT;  // queries per workgroup
   constexpr int HI = 16 * MT;
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
   }  // gfirst < gend
   if (HIST && hist_on) {  // every wavefront is done: add the workgroup's counts
     __syncthreads();
-    uint32_t* gh = hist + ((size_t)q0 * kTopkHistCopies + blockIdx.x % kTopkHistCopies) * kTopkBins;
+    uint32_t* gh = hist + ((size_t)q0 * kTopkHistCopies + blockIdx.x % ncopies) * kTopkBins;
 #pragma unroll
     for (int i = 0; i < kTopkBins / kThreads; ++i) {
       const uint32_t c = lh[tid + i * kThreads];
@@ -452,7 +452,7 @@ static int query_tile(const int32_t* soq, int32_t nq, size_t stage_bytes) {
 template <int MT>
 static int launch_mt(const csa2_fp4_cache* c, const uint16_t* q_idx, const float* w, const int32_t* soq,
                      const int32_t* nvis, const int32_t* bt, int32_t max_pages, int32_t nq, float* scores, int64_t ld,
-                     uint32_t* hist, int k, hipStream_t stream) {
+                     uint32_t* hist, int k, int* copies, hipStream_t stream) {
   const int total_groups = (int)ceil_div(ld, kPage);
   if (total_groups == 0 || nq == 0) return CSA2_OK;
   // queries per workgroup: several queries of one sequence share each loaded page
@@ -468,19 +468,21 @@ static int launch_mt(const csa2_fp4_cache* c, const uint16_t* q_idx, const float
   const unsigned gx = ceil_div(total_groups, (long long)kWaves * gpw);
   const dim3 grid(gx, (unsigned)qtiles), block(kThreads);
   const size_t lds = sizeof(QStage<MT>) * qt;
+  const int ncopies = topk_hist_copies(gx);
+  if (copies != nullptr) *copies = ncopies;
   if (hist != nullptr) {  // one query per workgroup (the caller checked)
     hipLaunchKernelGGL((index_score_kernel<MT, 1, true>), grid, block, lds + kTopkBins * sizeof(uint32_t), stream,
                        c->idx_codes, c->idx_scales, q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw,
-                       total_groups, hist, k);
+                       total_groups, hist, k, ncopies);
   } else if (qt == 8) {
     hipLaunchKernelGGL((index_score_kernel<MT, 8, false>), grid, block, lds, stream, c->idx_codes, c->idx_scales,
-                       q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k);
+                       q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k, ncopies);
   } else if (qt == 4) {
     hipLaunchKernelGGL((index_score_kernel<MT, 4, false>), grid, block, lds, stream, c->idx_codes, c->idx_scales,
-                       q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k);
+                       q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k, ncopies);
   } else {
     hipLaunchKernelGGL((index_score_kernel<MT, 1, false>), grid, block, lds, stream, c->idx_codes, c->idx_scales,
-                       q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k);
+                       q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k, ncopies);
   }
   return launch_status();
 }
@@ -488,12 +490,12 @@ static int launch_mt(const csa2_fp4_cache* c, const uint16_t* q_idx, const float
 static int launch_hi(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
                      const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* block_table,
                      int32_t max_pages, int32_t nq, float* scores, int64_t ld, uint32_t* hist, int k,
-                     hipStream_t stream) {
+                     int* copies, hipStream_t stream) {
   switch (Hi / 16) {
 #define CSA2_MT(m) \
   case m:          \
     return launch_mt<m>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, hist, k, \
-                        stream);
+                        copies, stream);
     CSA2_MT(1)
     CSA2_MT(2)
     CSA2_MT(3)
@@ -502,7 +504,7 @@ static int launch_hi(const csa2_fp4_cache* cache, const uint16_t* q_idx, const f
     CSA2_MT(6)
     CSA2_MT(7)
     default: return launch_mt<8>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld,
-                                 hist, k, stream);
+                                 hist, k, copies, stream);
 #undef CSA2_MT
   }
 }
@@ -530,7 +532,7 @@ extern "C" int index_score(const csa2_fp4_cache* cache, const uint16_t* q_idx, c
   const int st = check_args(cache, q_idx, w, Hi, n_visible, block_table, max_pages, nq, scores, ld);
   if (st != CSA2_OK || nq == 0 || ld == 0) return st;
   return launch_hi(cache, q_idx, w, Hi, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, nullptr, 0,
-                   stream);
+                   nullptr, stream);
 }
 
 extern "C" int index_topk(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
@@ -545,11 +547,12 @@ extern "C" int index_topk(const csa2_fp4_cache* cache, const uint16_t* q_idx, co
   if (!ws || ws_bytes < topk_select_workspace_size(nq, ld, k)) return CSA2_ERR_WORKSPACE;
   // the counting pass folds into the scan when every workgroup serves one query
   const bool fuse = ld > 0 && query_tile(seq_of_query, nq, 0) == 1;
+  int copies = 1;
   if (ld > 0) {
     uint32_t* hist = fuse ? topk_digit1_hist(ws, nq, ld) : nullptr;
     st = launch_hi(cache, q_idx, w, Hi, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, hist, k,
-                   stream);
+                   &copies, stream);
     if (st != CSA2_OK) return st;
   }
-  return topk_enqueue(scores, ld, n_visible, nq, k, topk_idx, ws, stream, fuse);
+  return topk_enqueue(scores, ld, n_visible, nq, k, topk_idx, ws, stream, fuse, copies);
 }

@@ -200,7 +200,7 @@ static_assert(kPerBins == 8, "digit searches hold 8 bins per thread");
 // ---------------------------------------------------------------- kernel 1 --
 __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __restrict__ scores, int64_t ld,
                                                              const int32_t* __restrict__ n_visible, int k,
-                                                             TopkWs ws) {
+                                                             TopkWs ws, int ncopies) {
   __shared__ uint32_t lh[kBins];
   const int q = blockIdx.y, tid = threadIdx.x;
   const int64_t n = n_visible[q];
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __rest
   for (int i = 0; i < kPer; ++i)
     if (base + (int64_t)tid * kPer + i < n) atomicAdd(&lh[key[i] >> kBinShift], 1u);
   __syncthreads();
-  uint32_t* gh = ws.hist + ((size_t)q * kTopkHistCopies + blockIdx.x % kTopkHistCopies) * kBins;
+  uint32_t* gh = ws.hist + ((size_t)q * kTopkHistCopies + blockIdx.x % ncopies) * kBins;
   for (int b = tid; b < kBins; b += kThreads) {
     const uint32_t c = lh[b];
     if (c) atomicAdd(&gh[b], c);
@@ -259,9 +259,9 @@ struct RowCands {
 // `prefix`: 12-bit digits of the composite below bit hi, stopping as soon as every
 // candidate left under the chosen prefix is selected.  `cnt` is the number of
 // candidates under `prefix` (they are all selected when cnt == need).
-template <typename Src>
+template <typename Src, typename Smem>
 CSA2_DEV unsigned long long select_boundary(const Src& src, uint32_t need, unsigned long long prefix, int hi,
-                                            uint32_t cnt, SelectSmem& sm) {
+                                            uint32_t cnt, Smem& sm) {
   const int tid = threadIdx.x;
   int parity = 0;
   while (true) {
@@ -298,12 +298,11 @@ CSA2_DEV unsigned long long select_boundary(const Src& src, uint32_t need, unsig
 
 // The need-th largest of the (at most 64) listed entries under a 24-bit key prefix:
 // they are gathered into LDS, and one wavefront ranks every one against the others.
-CSA2_DEV unsigned long long small_boundary(const unsigned long long* list, int total, unsigned long long prefix,
-                                           uint32_t need, SelectSmem& sm) {
-  for (int i = threadIdx.x; i < total; i += kThreads) {
-    const unsigned long long x = list[i];
+template <typename Src, typename Smem>
+CSA2_DEV unsigned long long small_boundary(const Src& src, unsigned long long prefix, uint32_t need, Smem& sm) {
+  src.each([&](unsigned long long x) {
     if ((x >> 40) == prefix) sm.cand[atomicAdd(&sm.ncand, 1u)] = x;
-  }
+  });
   lds_barrier();
   if (threadIdx.x < 64) {
     const int nc = (int)sm.ncand, lane = threadIdx.x;
@@ -347,7 +346,7 @@ CSA2_DEV void compact_list(const unsigned long long* list, int total, unsigned l
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __restrict__ scores, int64_t ld,
                                                                const int32_t* __restrict__ n_visible, int k,
                                                                int32_t* __restrict__ topk_idx, TopkWs ws,
-                                                               int nchunk) {
+                                                               int nchunk, int ncopies) {
   __shared__ SelectSmem sm;
   const int q = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t n = n_visible[q];
@@ -377,8 +376,12 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
     uint4 h[kTopkHistCopies][2];
 #pragma unroll
     for (int r = 0; r < kTopkHistCopies; ++r) {
-      h[r][0] = reinterpret_cast<const uint4*>(gh + r * kBins + bins_lo())[0];
-      h[r][1] = reinterpret_cast<const uint4*>(gh + r * kBins + bins_lo())[1];
+      if (r < ncopies) {  // uniform
+        h[r][0] = reinterpret_cast<const uint4*>(gh + r * kBins + bins_lo())[0];
+        h[r][1] = reinterpret_cast<const uint4*>(gh + r * kBins + bins_lo())[1];
+      } else {
+        h[r][0] = h[r][1] = make_uint4(0u, 0u, 0u, 0u);
+      }
     }
 #pragma unroll
     for (int r = 0; r < kTopkHistCopies; ++r)
@@ -485,7 +488,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
     const uint32_t need2 = need - d2.above;
     unsigned long long boundary;
     if (d2.cnt <= 64u) {
-      boundary = small_boundary(sm.list, (int)total, prefix, need2, sm);
+      boundary = small_boundary(LdsCands{sm.list, (int)total}, prefix, need2, sm);
     } else {
       const LdsCands src{sm.list, (int)total};
       boundary = select_boundary(src, need2, prefix, 40, d2.cnt, sm);
@@ -528,6 +531,196 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
   if (tid == 0) ctl->arrive = 0u;
 }
 
+// ------------------------------------------------------- one row per workgroup --
+// For many query rows (a prefill chunk): one workgroup selects one row.  The digit-1
+// histogram comes from the counting pass; each wavefront then walks its own
+// contiguous eighth of the row once, appending the entries in bins >= b* -- in index
+// order -- to its own LDS list (ballot-free: a DPP prefix sum of per-lane counts), and
+// counting the b* entries' next 12 key bits into an LDS digit-2 histogram.  The
+// eight lists, taken in wavefront order, are the row's candidates in index order;
+// the boundary and the ordered compaction follow as in the last workgroup above.
+constexpr int kRowCap = 1024;           // listed entries per wavefront segment
+constexpr int kRowSelectQueries = 128;  // rows from which this kernel is used
+struct RowSmem {
+  unsigned long long list[kWaves][kRowCap];
+  uint32_t h[kBins];  // digit-2 histogram of the b* entries, then radix-round scratch
+  uint32_t cnt[kWaves];
+  uint32_t wsum[4][kWaves];
+  Digit dig[4];
+  unsigned long long cand[64];
+  uint32_t ncand, ovf;
+  unsigned long long min_s, bnd_s;
+};
+struct RowLists {
+  const unsigned long long (*list)[kRowCap];
+  const uint32_t* cnt;
+  template <typename F>
+  CSA2_DEV void each(F&& f) const {
+    for (int w = 0; w < kWaves; ++w)
+      for (int i = threadIdx.x; i < (int)cnt[w]; i += kThreads) f(list[w][i]);
+  }
+};
+
+__global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restrict__ scores, int64_t ld,
+                                                            const int32_t* __restrict__ n_visible, int k,
+                                                            int32_t* __restrict__ topk_idx, uint32_t* __restrict__ hist,
+                                                            int ncopies) {
+  __shared__ RowSmem sm;
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int64_t n = n_visible[q];
+  int32_t* out = topk_idx + (int64_t)q * k;
+  if (n <= k) {  // everything visible is selected, then -1 padding
+    for (int i = tid; i < k; i += kThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  const float* row = scores + (int64_t)q * ld;
+  uint32_t* gh = hist + (size_t)q * kTopkHistCopies * kBins;
+  uint32_t hb[kPerBins] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  uint4 hc[kTopkHistCopies][2];
+#pragma unroll
+  for (int r = 0; r < kTopkHistCopies; ++r)
+    if (r < ncopies) {  // uniform
+      hc[r][0] = reinterpret_cast<const uint4*>(gh + r * kBins + bins_lo())[0];
+      hc[r][1] = reinterpret_cast<const uint4*>(gh + r * kBins + bins_lo())[1];
+    }
+#pragma unroll
+  for (int r = 0; r < kTopkHistCopies; ++r)
+    if (r < ncopies) {
+      const uint4 a0 = hc[r][0], a1 = hc[r][1];
+      hb[0] += a0.x, hb[1] += a0.y, hb[2] += a0.z, hb[3] += a0.w;
+      hb[4] += a1.x, hb[5] += a1.y, hb[6] += a1.z, hb[7] += a1.w;
+      // only this workgroup reads the row's histogram: return it to zero
+      if ((a0.x | a0.y | a0.z | a0.w | a1.x | a1.y | a1.z | a1.w) != 0u) {
+        reinterpret_cast<uint4*>(gh + r * kBins + bins_lo())[0] = make_uint4(0u, 0u, 0u, 0u);
+        reinterpret_cast<uint4*>(gh + r * kBins + bins_lo())[1] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+  for (int i = 0; i < kBins / kThreads; ++i) sm.h[tid + i * kThreads] = 0u;
+  if (tid == 0) {
+    sm.ovf = 0u;
+    sm.ncand = 0u;
+  }
+  const Digit d1 = find_digit(hb, (uint32_t)k, sm.wsum[0], &sm.dig[0]);  // its barriers publish the zeroing
+  const uint32_t bstar = (uint32_t)d1.d, above_b = d1.above;
+
+  // this wavefront's segment [s0, s1), U x 256 entries per step (thread: 4 consecutive
+  // entries per 256); order within a step: u, then lane, then the 4 entries
+  constexpr int U = 8;
+  const int64_t seg = (((n + kWaves - 1) / kWaves) + 255) & ~(int64_t)255;
+  const int64_t s0 = min(n, (int64_t)wid * seg), s1 = min(n, s0 + seg);
+  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+  uint32_t wcount = 0;  // entries listed by this wavefront so far (uniform)
+  for (int64_t e0 = s0; e0 < s1; e0 += 256 * U) {
+    uint32_t key[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = e0 + 256 * u + 4 * lane;
+      float v[4];
+      if (aligned && j + 4 <= s1) {
+        const float4 f = *reinterpret_cast<const float4*>(row + j);
+        v[0] = f.x, v[1] = f.y, v[2] = f.z, v[3] = f.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = j + i < s1 ? row[j + i] : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) key[u][i] = score_key(v[i]);
+    }
+    uint32_t keep = 0;  // bit 4u + i
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool valid = e0 + 256 * u + 4 * lane + i < s1;
+        const uint32_t bin = key[u][i] >> kBinShift;
+        if (valid && bin >= bstar) keep |= 1u << (4 * u + i);
+        if (valid && bin == bstar) atomicAdd(&sm.h[(key[u][i] >> 8) & (kBins - 1)], 1u);
+      }
+    // positions: a DPP prefix sum over the lanes of each u's counts, two u per scan
+    // (16-bit halves: at most 256 per half)
+    uint32_t before = wcount;
+#pragma unroll
+    for (int u = 0; u < U; u += 2) {
+      const uint32_t c0 = (uint32_t)__popc((keep >> (4 * u)) & 15u), c1 = (uint32_t)__popc((keep >> (4 * u + 4)) & 15u);
+      const uint32_t incl = wave_incl_scan(c0 | (c1 << 16));
+      const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+      const uint32_t ex0 = (incl & 0xFFFFu) - c0, ex1 = (incl >> 16) - c1;
+      uint32_t p0 = before + ex0, p1 = before + (tot & 0xFFFFu) + ex1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (keep & (1u << (4 * u + i))) {
+          if (p0 < (uint32_t)kRowCap) sm.list[wid][p0] = composite(key[u][i], (uint32_t)(e0 + 256 * u + 4 * lane + i));
+          ++p0;
+        }
+        if (keep & (1u << (4 * u + 4 + i))) {
+          if (p1 < (uint32_t)kRowCap)
+            sm.list[wid][p1] = composite(key[u + 1][i], (uint32_t)(e0 + 256 * (u + 1) + 4 * lane + i));
+          ++p1;
+        }
+      }
+      before += (tot & 0xFFFFu) + (tot >> 16);
+    }
+    wcount = before;
+  }
+  if (lane == 0) {
+    sm.cnt[wid] = min(wcount, (uint32_t)kRowCap);
+    if (wcount > (uint32_t)kRowCap) sm.ovf = 1u;
+  }
+  lds_barrier();
+  const uint32_t need = (uint32_t)k - above_b;  // 1 <= need <= entries in b*
+  if (sm.ovf == 0u) {
+    uint32_t hv[kPerBins];
+    bins_from_lds(sm.h, hv);
+    const Digit d2 = find_digit(hv, need, sm.wsum[1], &sm.dig[1]);
+    const unsigned long long prefix = ((unsigned long long)bstar << 12) | (unsigned long long)d2.d;  // key bits 31..8
+    const uint32_t need2 = need - d2.above;
+    const RowLists src{sm.list, sm.cnt};
+    const unsigned long long boundary = d2.cnt <= 64u ? small_boundary(src, prefix, need2, sm)
+                                                      : select_boundary(src, need2, prefix, 40, d2.cnt, sm);
+    // ordered compaction: wavefront wid's list after the kept entries of the lists before it
+    const int cn = (int)sm.cnt[wid];
+    uint32_t kept = 0;
+    for (int i0 = 0; i0 < cn; i0 += 64) {
+      const unsigned long long x = i0 + lane < cn ? sm.list[wid][i0 + lane] : 0ull;  // 0 is below every boundary
+      kept += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(x >= boundary));
+    }
+    if (lane == 0) sm.wsum[0][wid] = kept;
+    lds_barrier();
+    uint32_t pos = 0;
+    for (int w = 0; w < wid; ++w) pos += sm.wsum[0][w];
+    for (int i0 = 0; i0 < cn; i0 += 64) {
+      const unsigned long long x = i0 + lane < cn ? sm.list[wid][i0 + lane] : 0ull;
+      const bool kp = x >= boundary;
+      const unsigned long long m = __builtin_amdgcn_ballot_w64(kp);
+      const uint32_t o = pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (kp && o < (uint32_t)k) out[o] = (int32_t)index_of(x);
+      pos += (uint32_t)__popcll(m);
+    }
+  } else {
+    // a segment listed more than kRowCap entries: boundary from the row, then an
+    // ordered scan of the row, kThreads entries per round
+    const RowCands src{row, n, bstar};
+    const unsigned long long boundary = select_boundary(src, need, (unsigned long long)bstar, 52, 0xFFFFFFFFu, sm);
+    uint32_t written = 0;
+    int parity = 0;
+    for (int64_t r0 = 0; r0 < n; r0 += kThreads) {
+      const int64_t i = r0 + tid;
+      bool kp = false;
+      if (i < n) {
+        const uint32_t kk = score_key(row[i]);
+        const uint32_t bin = kk >> kBinShift;
+        kp = bin > bstar || (bin == bstar && composite(kk, (uint32_t)i) >= boundary);
+      }
+      uint32_t t2;
+      const uint32_t incl = block_inclusive_scan(kp ? 1u : 0u, sm.wsum[parity], &t2);
+      parity ^= 1;
+      if (kp && written + incl - 1 < (uint32_t)k) out[written + incl - 1] = (int32_t)i;
+      written += t2;
+    }
+  }
+}
+
 }  // namespace csa2
 
 using namespace csa2;
@@ -547,16 +740,22 @@ uint32_t* topk_digit1_hist(void* ws, int32_t nq, int64_t ld) {
 }
 
 int topk_enqueue(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq, int32_t k,
-                 int32_t* topk_idx, void* ws, hipStream_t stream, bool hist_done) {
+                 int32_t* topk_idx, void* ws, hipStream_t stream, bool hist_done, int copies) {
   const long long nchunk = ld > 0 ? (ld + kChunk - 1) / kChunk : 1;
   const long long kchunk = (k + kChunk - 1) / kChunk;  // the n <= k path writes k outputs
   const long long grid_x = nchunk > kchunk ? nchunk : kchunk;
   const TopkWs w = carve(ws, nq, nchunk);
   const dim3 grid((unsigned)grid_x, (unsigned)nq);
+  const int ncopies = hist_done ? copies : topk_hist_copies(nchunk);
   if (ld > 0 && !hist_done)
-    hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kThreads), 0, stream, scores, ld, n_visible, k, w);
+    hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kThreads), 0, stream, scores, ld, n_visible, k, w, ncopies);
+  if (nq >= kRowSelectQueries) {  // many rows: one workgroup per row
+    hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)nq), dim3(kThreads), 0, stream, scores, ld, n_visible, k,
+                       topk_idx, w.hist, ncopies);
+    return launch_status();
+  }
   hipLaunchKernelGGL(topk_select_kernel, grid, dim3(kThreads), 0, stream, scores, ld, n_visible, k, topk_idx, w,
-                     (int)nchunk);
+                     (int)nchunk, ncopies);
   return launch_status();
 }
 
@@ -569,5 +768,5 @@ extern "C" int topk_select(const float* scores, int64_t ld, const int32_t* n_vis
   if (nq == 0) return CSA2_OK;
   if (!n_visible || !topk_idx || (ld > 0 && !scores)) return CSA2_ERR_NULL;
   if (!ws || ws_bytes < topk_select_workspace_size(nq, ld, k)) return CSA2_ERR_WORKSPACE;
-  return topk_enqueue(scores, ld, n_visible, nq, k, topk_idx, ws, stream, false);
+  return topk_enqueue(scores, ld, n_visible, nq, k, topk_idx, ws, stream, false, 1);
 }

@@ -264,6 +264,26 @@ def test_topk_empty_and_short_rows():
     _topk_case(s, nvis, 100, "short")
 
 
+@pytest.mark.timeout(600)
+def test_topk_many_rows_one_workgroup_per_row():
+    """At least 128 rows take the one-workgroup-per-row kernel: ragged rows, ties,
+    rows with n_visible <= k, an all-equal row (its per-wavefront lists overflow and it
+    takes the slow path) and rows where the selected entries cluster in one segment."""
+    rng = np.random.default_rng(330)
+    nq, ld = 136, 40_000
+    s = rng.standard_normal((nq, ld)).astype(np.float32)
+    nvis = rng.integers(1, ld + 1, nq).astype(np.int32)
+    nvis[:4] = [ld, 2048, 100, 0]
+    s[4] = rng.integers(0, 500, ld).astype(np.float32)   # many ties
+    s[5] = 1.25                                           # all equal: overflow path
+    s[6, :5000] += 50.0                                   # winners packed into the first segment
+    s[7, -3000:] += 50.0                                  # ... into the last
+    nvis[4:8] = ld
+    say("case: top-k 136 rows (one workgroup per row)")
+    _topk_case(s, nvis, 2048, "rows k=2048")
+    _topk_case(s, nvis, 300, "rows k=300")
+
+
 def test_topk_large_row_many_chunks():
     rng = np.random.default_rng(320)
     s = (rng.standard_normal((1, 600_000)) * 3 + 20).astype(np.float32)

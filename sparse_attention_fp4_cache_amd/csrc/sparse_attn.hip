@@ -387,6 +387,204 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a) {
   }
 }
 
+// ---- one row range per query: one workgroup per (query, 64 heads) ----------------
+// With many queries (a prefill chunk) every query gets one workgroup, and it takes 64
+// heads, so each gathered and dequantised tile of 32 rows serves 64 heads instead of
+// 16.  Eight wavefronts on one tile at a time: wavefront w owns heads 16*(w%4)..+15
+// of the group and, for the values, channels 256*(w/4)..+255; the logits of its heads
+// are the sum (in a fixed order) of the halves computed by the two wavefronts that
+// share them, so both keep the same softmax state.  A thread gathers 32 channels of
+// one tile row (16 code bytes + 2 scale bytes, or 64 bytes of a window row).
+constexpr int kWideHeads = 64;
+struct __align__(16) WideSmem {
+  uint16_t x[kRT * kXStride];  // X[row][ch], 16-byte chunks swizzled by xchunk()
+  float red[4][2][2][4][64];   // partial logits [head group][channel half][mtile][r][lane]
+  int src[kSeg];
+};
+static_assert(sizeof(WideSmem) <= 160 * 1024, "attention LDS exceeds 160 KB");
+
+struct WideRegs {
+  uint4 code;     // FP4 entry: 16 code bytes (32 channels)
+  uint32_t sc;    // FP4 entry: the two E4M3 scale bytes of those channels
+  uint4 win[4];   // window row: 32 bf16
+  int kind;       // 1: FP4 entry, 2: window row, 0: no row
+};
+
+CSA2_DEV void issue_wide(const AttnArgs& a, const int* src_rows, int tid, int tile_row0, bool has_main, bool has_win,
+                         WideRegs& t) {
+  const int row = tid >> 4, c16 = tid & 15;
+  const int src = src_rows[tile_row0 + row];
+  t.kind = src >= 0 ? 1 : (src <= -2 ? 2 : 0);
+  if (has_main) {
+    const int64_t slot = src >= 0 ? src : 0;
+    t.code = reinterpret_cast<const uint4*>(a.main_codes + slot * kMainRowBytes)[c16];
+    t.sc = reinterpret_cast<const uint16_t*>(a.main_scales + slot * kMainScaleBytes)[c16];
+  } else {
+    t.code = make_uint4(0u, 0u, 0u, 0u);
+    t.sc = 0u;
+  }
+  if (has_win) {
+    const int64_t wrow = src <= -2 ? (int64_t)(-2 - src) : 0;
+    const uint4* wp = reinterpret_cast<const uint4*>(a.swa + wrow * kLatentDim) + 4 * c16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t.win[i] = wp[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t.win[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+CSA2_DEV void store_wide(uint16_t* x, int tid, const WideRegs& t, bool has_main) {
+  const int row = tid >> 4, c16 = tid & 15;
+  uint4* xr = reinterpret_cast<uint4*>(x + row * kXStride);
+  const uint32_t wmask = t.kind == 2 ? ~0u : 0u;
+  if (has_main) {
+    const uint32_t mmask = t.kind == 1 ? ~0u : 0u;
+    const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)t.sc, 0), s1 = __builtin_amdgcn_cvt_f32_fp8((int)t.sc, 1);
+    const uint32_t cw[4] = {t.code.x, t.code.y, t.code.z, t.code.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)  // chunk i (8 channels) of this thread's 32 uses scale byte i / 2
+      xr[xchunk(4 * c16 + i)] = or4(and4(dequant8(cw[i], i < 2 ? s0 : s1), mmask), and4(t.win[i], wmask));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xr[xchunk(4 * c16 + i)] = and4(t.win[i], wmask);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) {
+  __shared__ WideSmem smem;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int g = lane >> 4, n16 = lane & 15;
+  const int hg = wid & 3, kh = wid >> 2;  // head group of 16 within the 64, channel half
+  const int qrow = blockIdx.x;
+  const int bt_row = a.prefill ? 0 : qrow;
+  const int nrows = a.k + a.window;
+  const int head = kWideHeads * blockIdx.y + 16 * hg + n16;  // head of this lane in every accumulator
+
+  // Q^T operand for the logits over this wavefront's 256 channels: lane holds head n16
+  // of its group, channels 256*kh + 32*ks + 8*g .. +7
+  uint4 qop[8];
+  const uint16_t* qp = a.q + ((int64_t)qrow * a.H + head) * kLatentDim + 256 * kh + 8 * g;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) qop[ks] = *reinterpret_cast<const uint4*>(qp + 32 * ks);
+
+  v4f acc[16];  // O^T: M-tile mt covers channels 256*kh + 16*mt + 4*g + r, column = head
+#pragma unroll
+  for (int mt = 0; mt < 16; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  for (int seg0 = 0; seg0 < nrows; seg0 += kSeg) {
+  const int seg_n = min(kSeg, nrows - seg0);
+  lds_barrier();  // the previous segment's sources are no longer read
+  const int seg_pad = (seg_n + kRT - 1) / kRT * kRT;
+  for (int rl = tid; rl < seg_pad; rl += kThreads) {
+    const int r = seg0 + rl;
+    int src = -1;
+    if (rl >= seg_n) {
+    } else if (r < a.k) {
+      const int j = a.topk_idx[(int64_t)qrow * a.k + r];
+      if (j >= 0) src = a.block_table[(int64_t)bt_row * a.max_pages + (j >> 6)] * kPage + (j & 63);
+    } else {
+      const int wr = r - a.k;
+      if (a.prefill) {
+        if (qrow + wr >= a.swa_first_valid) src = -2 - (qrow + wr);
+      } else if (wr < a.swa_len[qrow]) {
+        src = -2 - (qrow * a.window + wr);
+      }
+    }
+    smem.src[rl] = src;
+  }
+  lds_barrier();
+  auto has_main = [&](int rl0) { return seg0 + rl0 < a.k; };
+  auto has_win = [&](int rl0) { return a.window > 0 && seg0 + rl0 + kRT > a.k; };
+  WideRegs cur;
+  issue_wide(a, smem.src, tid, 0, has_main(0), has_win(0), cur);
+  for (int row0 = 0; row0 < seg_n; row0 += kRT) {
+    lds_barrier();  // previous tile fully consumed
+    store_wide(smem.x, tid, cur, has_main(row0));
+    const int next0 = row0 + kRT;
+    if (next0 < seg_n) issue_wide(a, smem.src, tid, next0, has_main(next0), has_win(next0), cur);
+    lds_barrier();
+    // ---- partial logits over this wavefront's 256 channels, two 16-row M-tiles
+    v4f s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      s[t] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int xrow = 8 * (n16 >> 2) + 4 * t + (n16 & 3);  // lane group g gets rows 8g .. 8g+7
+        const uint4 xa = reinterpret_cast<const uint4*>(smem.x + xrow * kXStride)[xchunk(32 * kh + 4 * ks + g)];
+        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(qop[ks]), s[t], 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) smem.red[hg][kh][t][r][lane] = s[t][r];
+    }
+    lds_barrier();
+    float z[2][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = smem.red[hg][0][t][r][lane] + smem.red[hg][1][t][r][lane];
+        const int rl = row0 + 8 * g + 4 * t + r;
+        const bool valid = (rl < seg_n) & (smem.src[rl & (kSeg - 1)] != -1);
+        z[t][r] = valid ? v * a.scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, z[t][r]);
+      }
+    tmax = max_rows(tmax);
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
+    float p[2][4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[t][r] = fast_exp2(z[t][r] - (m_new == -INFINITY ? 0.0f : m_new));
+        psum += p[t][r];
+      }
+    psum = sum_rows(psum);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    uint32_t phi[4], plo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a0 = p[i >> 1][2 * (i & 1)], a1 = p[i >> 1][2 * (i & 1) + 1];
+      const uint32_t h0 = bf16_rne_bits(a0), h1 = bf16_rne_bits(a1);
+      phi[i] = h0 | (h1 << 16);
+      const float r0 = a0 - __uint_as_float(h0 << 16), r1 = a1 - __uint_as_float(h1 << 16);
+      plo[i] = bf16_rne_bits(r0) | (bf16_rne_bits(r1) << 16);
+    }
+    const bf16x8 Bhi = as_bf16x8(make_uint4(phi[0], phi[1], phi[2], phi[3]));
+    const bf16x8 Blo = as_bf16x8(make_uint4(plo[0], plo[1], plo[2], plo[3]));
+    // X^T operand of M-tile mt (channels 256*kh + 16*mt + ..), transposing LDS reads
+    const int tr_c = n16 & 3;
+    const uint16_t* tr_row = smem.x + (8 * g + (n16 >> 2)) * kXStride + 4 * (tr_c & 1);
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt) {
+      acc[mt] *= alpha;
+      const uint16_t* tp = tr_row + 8 * xchunk(32 * kh + 2 * mt + (tr_c >> 1));
+      const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)tp);
+      const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tp + 4 * kXStride));
+      const bf16x8 A = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bhi, acc[mt], 0, 0, 0);
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Blo, acc[mt], 0, 0, 0);
+    }
+  }
+  }  // segments
+
+  // ---- write: lane holds head `head`, channels 256*kh + 16*mt + 4*g + r
+  const float inv = (l_run > 0.0f) ? __builtin_amdgcn_rcpf(l_run) : 0.0f;
+  float* op = a.out + ((int64_t)qrow * a.H + head) * kLatentDim + 256 * kh + 4 * g;
+#pragma unroll
+  for (int mt = 0; mt < 16; ++mt)
+    *reinterpret_cast<float4*>(op + 16 * mt) =
+        make_float4(acc[mt][0] * inv, acc[mt][1] * inv, acc[mt][2] * inv, acc[mt][3] * inv);
+  if (kh == 0 && g == 0)
+    a.lse[(int64_t)qrow * a.H + head] = (l_run > 0.0f) ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : -INFINITY;
+}
+
 // Combine the row ranges of one (query, head): out = sum_s 2^(m_s-M) O_s / L.
 // Four wavefronts per (query, head), each owning 128 channels (two per lane).  With
 // at most B <= 64 ranges a wavefront issues the loads of every range's O_s at once
@@ -481,6 +679,11 @@ static int run_attention(AttnArgs a, void* ws, size_t ws_bytes, hipStream_t stre
     if (!ws || ws_bytes < need) return CSA2_ERR_WORKSPACE;
     a.part_o = reinterpret_cast<float*>(ws);
     a.part_ml = a.part_o + (size_t)a.nq * a.nsplit * a.H * kLatentDim;
+  }
+  if (a.nsplit == 1 && a.H % kWideHeads == 0) {  // many queries: a workgroup takes 64 heads
+    hipLaunchKernelGGL(sparse_attn_wide_kernel, dim3((unsigned)a.nq, (unsigned)(a.H / kWideHeads)), dim3(kThreads), 0,
+                       stream, a);
+    return launch_status();
   }
   const dim3 grid((unsigned)a.nsplit, (unsigned)(a.H / 16), (unsigned)a.nq);
   hipLaunchKernelGGL(sparse_attn_kernel, grid, dim3(kThreads), 0, stream, a);

@@ -368,6 +368,57 @@ def test_attention_prefill_truncated_windows():
     attn_close(out.cpu().numpy(), ro, lse.cpu().numpy(), rl, "prefill")
 
 
+@pytest.mark.timeout(600)
+def test_attention_prefill_one_workgroup_per_query():
+    """Enough queries for one row range per query: the kernel that takes 64 heads per
+    workgroup (two groups of 64 here).  k = 200 leaves a tile holding both selected
+    entries and window rows; -1 indices and windows cut by the first valid row."""
+    rng = np.random.default_rng(430)
+    n, T, H, k, W = 2500, 64, 128, 200, 128
+    g, o = _attn_cache(rng, n, outliers=True)
+    bt = np.arange((n + 63) // 64, dtype=np.int32)
+    idx = np.stack([np.sort(rng.choice(n, k, replace=False)) for _ in range(T)]).astype(np.int32)
+    idx[5, 150:] = -1
+    idx[9, :] = -1
+    q = bits(rng.standard_normal((T, H, 512)))
+    swa = bits(rng.standard_normal((W - 1 + T, 512)))
+    first_valid = 100
+    scale = 1 / math.sqrt(512)
+    out = torch.zeros((T, H, 512), device="cuda")
+    lse = torch.zeros((T, H), device="cuda")
+    ws = torch.zeros(max(256, lib.sparse_attn_prefill_chunk_workspace_size(T, H, k, W)), dtype=torch.uint8,
+                     device="cuda")
+    say("case: attention prefill, one workgroup per (query, 64 heads)")
+    lib.sparse_attn_prefill_chunk(g, dev_bits(q), dev(idx), dev(bt), 5000, dev_bits(swa), first_valid, W, scale,
+                                  out, lse, ws)
+    ro, rl = oracle.sparse_attn_prefill_chunk(o, q, idx, bt, swa, first_valid, W, scale)
+    attn_close(out.cpu().numpy(), ro, lse.cpu().numpy(), rl, "prefill wide")
+
+
+@pytest.mark.timeout(600)
+def test_attention_decode_many_sequences():
+    """64 sequences x 64 heads: one row range per query, 64 heads per workgroup, ragged
+    window lengths and a row with no selected entries."""
+    rng = np.random.default_rng(440)
+    n, B, H, k, W = 2000, 64, 64, 160, 128
+    g, o = _attn_cache(rng, n)
+    bt = np.tile(np.arange((n + 63) // 64, dtype=np.int32), (B, 1))
+    idx = np.stack([np.sort(rng.choice(n, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    idx[3, :] = -1
+    q = bits(rng.standard_normal((B, H, 512)))
+    swa = bits(rng.standard_normal((B, W, 512)))
+    swa_len = rng.integers(0, W + 1, B).astype(np.int32)
+    swa_len[3] = 0
+    scale = 1 / math.sqrt(512)
+    out = torch.zeros((B, H, 512), device="cuda")
+    lse = torch.zeros((B, H), device="cuda")
+    ws = torch.zeros(lib.sparse_attn_decode_workspace_size(B, H, k, W), dtype=torch.uint8, device="cuda")
+    say("case: attention decode, 64 sequences")
+    lib.sparse_attn_decode(g, dev_bits(q), dev(idx), dev(bt), dev_bits(swa), dev(swa_len), scale, out, lse, ws)
+    ro, rl = oracle.sparse_attn_decode(o, q, idx, bt, swa, swa_len, scale)
+    attn_close(out.cpu().numpy(), ro, lse.cpu().numpy(), rl, "decode 64 sequences")
+
+
 def test_index_score_reveals_query_quantisation():
     # keys +-1 at one channel each and one-hot head weights make every score equal
     # max(+-qhat[h][c], 0), so the dequantised query is compared value by value;

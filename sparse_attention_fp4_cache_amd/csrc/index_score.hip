@@ -27,6 +27,8 @@
 #include "host_common.hpp"
 #include "topk_internal.hpp"
 
+#include <algorithm>
+
 namespace csa2 {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -444,6 +446,361 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
   }
 }
 
+// ---- scan for queries that share a sequence: four queries per wavefront ---------
+// The 16 rows of an M-tile are (query, head) pairs, four queries of four heads each,
+// so one 16x16x128 MFMA leaves lane group g the dots of query g with one entry for
+// four heads, and the Hi/4 M-tiles together give a lane every head of its (query,
+// entry) pair in head order: the weighted ReLU sum needs no lane exchange.  The
+// eight wavefronts of a workgroup (32 queries) share each page of keys, which is
+// staged once in LDS and read as the B operand; each wavefront's queries stay in
+// registers as MXFP4 A operands for the whole page range.
+constexpr int kQ4Queries = 4 * kWaves;  // queries per workgroup
+constexpr int kQ4MinPages = 8;          // fewest pages per workgroup (amortises the query staging)
+
+constexpr int kQ4Group = 4;  // pages staged per workgroup barrier
+
+struct Q4Page {
+  uint4 codes[kPage * 4];  // 16-byte chunk c of entry e at 4e + (c ^ ((e >> 2) & 3)): conflict-free reads
+  uint32_t sc[kPage];      // entry e: its four E8M0 block exponents (byte b = block b)
+  uint32_t estat[kPage];   // entry e: smallest | largest << 8 of its four block exponents
+  uint32_t pstat;          // over the page: largest entry span | smallest << 8 | largest << 16
+  uint32_t pad[3];
+};
+struct Q4Smem {
+  Q4Page slot[2][kQ4Group];
+  int row[kQ4Queries];
+  int nvis[kQ4Queries];
+};
+
+// A staging step's share of thread tid (pages G .. G + kQ4Group - 1 of the row):
+// code chunk tid%256 of pages wid/4 and 2 + wid/4 and the block exponents of entries
+// 4(lane%16) .. +3 of page lane/16 (stored by wavefront 0).  Pages at or past Gend
+// re-read page Gend - 1; their slots are never read.
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+struct Q4Regs {
+  v4u c0, c1;  // pages wid/4 and 2 + wid/4
+  v4u s;
+};
+static_assert(kQ4Group == 4 && kThreads == 512, "staging shares: two code chunks per thread, one scale row per page");
+
+CSA2_DEV void q4_load(Q4Regs& r, const uint8_t* __restrict__ idx_codes, const uint8_t* __restrict__ idx_scales,
+                      const int32_t* __restrict__ bt, int G, int Gend, int wid, int lane) {
+  const int last = Gend - 1;  // page numbers: uniform scalar reads
+  const int pg0 = bt[min(G, last)], pg1 = bt[min(G + 1, last)], pg2 = bt[min(G + 2, last)],
+            pg3 = bt[min(G + 3, last)];
+  // every wavefront reads the exponent rows (the same 1 KB, served by its L1) though
+  // only wavefront 0 stores them: with no load under a condition, each wait below
+  // counts exactly the loads issued after the one it waits for
+  {
+    const int q = lane >> 4;
+    const int pg = q == 0 ? pg0 : (q == 1 ? pg1 : (q == 2 ? pg2 : pg3));
+    r.s = *reinterpret_cast<const v4u*>(idx_scales + (int64_t)pg * kPage * kIdxScaleBytes +
+                                        (uint32_t)(lane & 15) * 16u);
+  }
+  const uint32_t off = (uint32_t)(((wid & 3) << 6) | lane) * 16u;
+  const int pa = (wid >> 2) ? pg1 : pg0, pb = (wid >> 2) ? pg3 : pg2;
+  r.c0 = *reinterpret_cast<const v4u*>(idx_codes + (int64_t)pa * kPage * kIdxRowBytes + off);
+  r.c1 = *reinterpret_cast<const v4u*>(idx_codes + (int64_t)pb * kPage * kIdxRowBytes + off);
+}
+
+template <int C>
+CSA2_DEV int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, C, 0xF, 0xF, true);
+}
+
+CSA2_DEV void q4_store(Q4Page (&slot)[kQ4Group], const Q4Regs& r, int wid, int lane) {
+  {
+    const int p = wid >> 2, t = ((wid & 3) << 6) | lane, e = t >> 2, c = t & 3;
+    const int at = 4 * e + (c ^ ((e >> 2) & 3));
+    *reinterpret_cast<v4u*>(&slot[p].codes[at]) = r.c0;
+    *reinterpret_cast<v4u*>(&slot[p + 2].codes[at]) = r.c1;
+  }
+  if (wid == 0) {  // 16-lane row p holds page p
+    const int p = lane >> 4, i = lane & 15;
+    const uint32_t wd[4] = {r.s[0], r.s[1], r.s[2], r.s[3]};
+    uint32_t es[4];
+    int span = 0, lo_all = 255, hi_all = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int lo = 255, hi = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int u = (int)((wd[j] >> (8 * b)) & 0xFFu);
+        lo = min(lo, u);
+        hi = max(hi, u);
+      }
+      es[j] = (uint32_t)lo | ((uint32_t)hi << 8);
+      span = max(span, hi - lo);
+      lo_all = min(lo_all, lo);
+      hi_all = max(hi_all, hi);
+    }
+    *reinterpret_cast<v4u*>(&slot[p].sc[4 * i]) = r.s;
+    const v4u esv = {es[0], es[1], es[2], es[3]};
+    *reinterpret_cast<v4u*>(&slot[p].estat[4 * i]) = esv;
+    // over the row's 16 lanes: quad swaps, then half-row and row mirrors
+    span = max(span, dpp_i<0xB1>(span));
+    lo_all = min(lo_all, dpp_i<0xB1>(lo_all));
+    hi_all = max(hi_all, dpp_i<0xB1>(hi_all));
+    span = max(span, dpp_i<0x4E>(span));
+    lo_all = min(lo_all, dpp_i<0x4E>(lo_all));
+    hi_all = max(hi_all, dpp_i<0x4E>(hi_all));
+    span = max(span, dpp_i<0x141>(span));
+    lo_all = min(lo_all, dpp_i<0x141>(lo_all));
+    hi_all = max(hi_all, dpp_i<0x141>(hi_all));
+    span = max(span, dpp_i<0x140>(span));
+    lo_all = min(lo_all, dpp_i<0x140>(lo_all));
+    hi_all = max(hi_all, dpp_i<0x140>(hi_all));
+    if (i == 0) slot[p].pstat = (uint32_t)span | ((uint32_t)lo_all << 8) | ((uint32_t)hi_all << 16);
+  }
+}
+
+// Whether the MFMA dot of a query (largest head span qs, exponents in [qlo, qhi]) with
+// keys of span ks and exponents in [klo, khi] may be inexact.
+CSA2_DEV bool q4_inexact(int qs, int qlo, int qhi, int ks, int klo, int khi) {
+  return (ks + qs > kMaxSpread) | (qlo + klo < kMinExpSum) | (qhi + khi > kMaxExpSum);
+}
+
+// The definition itself for one (query, entry) pair: each query block is quantised
+// again from its bf16 values by the element rule (the codes and exponent of the MFMA
+// operand), integer block sums, fp64 combination in block order, one rounding per
+// head, the fma chain in head order.
+CSA2_DEV float q4_exact(const uint16_t* __restrict__ qrow, const float* __restrict__ wq, int hi_count,
+                        const uint8_t* __restrict__ krow, uint32_t kscales) {
+  float acc = 0.0f;
+  for (int h = 0; h < hi_count; ++h) {
+    double D = 0.0;
+    for (int b = 0; b < 4; ++b) {
+      const uint16_t* src = qrow + h * kIndexDim + 32 * b;
+      uint32_t amax = 0;
+      for (int i = 0; i < 32; ++i) amax = max(amax, (uint32_t)src[i] & 0x7FFFu);
+      const uint32_t u = mx_exponent(bf16_to_f32(amax));
+      const float X = ldexpf(1.0f, (int)u - 127);
+      int S = 0;
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t qn = e2m1_code(bf16_to_f32(src[i]), X);
+        const uint32_t kn = (krow[16 * b + (i >> 1)] >> (4 * (i & 1))) & 15u;
+        S += e2m1_twice(qn) * e2m1_twice(kn);
+      }
+      D += ldexp((double)S, (int)u + (int)((kscales >> (8 * b)) & 0xFFu) - 256);
+    }
+    acc = fmaf(wq[h], relu((float)D), acc);
+  }
+  return acc;
+}
+
+template <int OA>
+CSA2_DEV v4f mfma_fp4(const uint4& a, const uint4& b, int asc, int bsc) {
+  const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, zero, 4, 4, OA, asc, 0, bsc);
+}
+
+// NMT = Hi / 4 M-tiles; Hi <= 64 keeps a wavefront's operands and weights in registers.
+template <int NMT>
+__global__ __launch_bounds__(kThreads) void index_score_q4_kernel(
+    const uint8_t* __restrict__ idx_codes, const uint8_t* __restrict__ idx_scales, const uint16_t* __restrict__ q_idx,
+    const float* __restrict__ w, const int32_t* __restrict__ seq_of_query, const int32_t* __restrict__ n_visible,
+    const int32_t* __restrict__ block_table, int max_pages, int nq, float* __restrict__ scores, int64_t ld,
+    int pages_per_wg) {
+  constexpr int HI = 4 * NMT;
+  constexpr int NSC = (NMT + 3) / 4;
+  __shared__ Q4Smem sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, n = lane & 15;
+  const int q0 = blockIdx.y * kQ4Queries;
+  const int G0 = blockIdx.x * pages_per_wg;
+  if (tid < kQ4Queries) {
+    const int q = q0 + tid;
+    sm.row[tid] = q < nq ? seq_of_query[q] : -1;
+    sm.nvis[tid] = q < nq ? (int)min((int64_t)n_visible[q], ld) : 0;
+  }
+
+  // A operands: lane l holds row l%16 = (query 4 wid + (l%16)/4, head 4 mt + l%4) and
+  // K-block l/16 of every M-tile mt
+  const int qa_raw = q0 + 4 * wid + (n >> 2);
+  const bool qa_ok = qa_raw < nq;
+  const int qa = qa_ok ? qa_raw : nq - 1;  // a spare row quantises a valid query and is zeroed
+  uint4 A[NMT];
+  uint32_t asc[NSC];
+#pragma unroll
+  for (int i = 0; i < NSC; ++i) asc[i] = 0u;
+  int span = 0, lo_all = 255, hi_all = 0;
+  static_assert(NMT % 4 == 0, "M-tiles are staged four at a time");
+#pragma clang loop unroll(full)
+  for (int mt0 = 0; mt0 < NMT; mt0 += 4) {
+    QRaw raw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      mx32_load(q_idx + ((int64_t)qa * HI + 4 * (mt0 + k) + (n & 3)) * kIndexDim + 32 * g, raw[k]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int mt = mt0 + k;
+      uint4 c;
+      uint32_t u;
+      mx32_block(raw[k], c, u);
+      if (!qa_ok) {
+        c = make_uint4(0u, 0u, 0u, 0u);
+        u = 127u;
+      }
+      A[mt] = c;
+      asc[mt >> 2] |= u << (8 * (mt & 3));
+      int lo = (int)u, hi = (int)u;  // over the head's four blocks (lanes l, l^16, l^32, l^48)
+      lo = min(lo, __shfl_xor(lo, 16));
+      hi = max(hi, __shfl_xor(hi, 16));
+      lo = min(lo, __shfl_xor(lo, 32));
+      hi = max(hi, __shfl_xor(hi, 32));
+      span = max(span, hi - lo);
+      lo_all = min(lo_all, lo);
+      hi_all = max(hi_all, hi);
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 4; o <<= 1) {  // over the query's heads within an M-tile
+    span = max(span, __shfl_xor(span, o));
+    lo_all = min(lo_all, __shfl_xor(lo_all, o));
+    hi_all = max(hi_all, __shfl_xor(hi_all, o));
+  }
+  // output side: lane l serves query 4 wid + l/16, whose statistics lane 4(l/16) holds
+  const int q_span = __shfl(span, 4 * g), q_lo = __shfl(lo_all, 4 * g), q_hi = __shfl(hi_all, 4 * g);
+  const int qo = q0 + 4 * wid + g;
+  float wr[HI];
+  {
+    const float4* wsrc = reinterpret_cast<const float4*>(w + (int64_t)(qo < nq ? qo : nq - 1) * HI);
+#pragma unroll
+    for (int i = 0; i < HI / 4; ++i) {
+      const float4 v = wsrc[i];
+      wr[4 * i] = v.x;
+      wr[4 * i + 1] = v.y;
+      wr[4 * i + 2] = v.z;
+      wr[4 * i + 3] = v.w;
+    }
+  }
+  float* __restrict__ srow = scores + (int64_t)qo * ld;
+  lds_barrier();
+  // operands and weights are in registers before the page loop, whose waits then only
+  // cover the keys staged ahead
+#pragma unroll
+  for (int h = 0; h < HI; ++h) asm volatile("" : "+v"(wr[h]));
+
+  // one row of the block table at a time: the first pending query's row, with every
+  // pending query of the workgroup that reads it
+  uint32_t pending = (nq - q0 >= kQ4Queries) ? 0xFFFFFFFFu : ((1u << (nq - q0)) - 1u);
+  while (pending != 0u) {
+    const int row = __builtin_amdgcn_readfirstlane(sm.row[__builtin_ctz(pending)]);
+    uint32_t cur = 0u;
+    int vmax = 0;
+    for (int i = 0; i < kQ4Queries; ++i) {
+      const int ri = __builtin_amdgcn_readfirstlane(sm.row[i]);
+      const int vi = __builtin_amdgcn_readfirstlane(sm.nvis[i]);
+      if (((pending >> i) & 1u) && ri == row) {
+        cur |= 1u << i;
+        vmax = max(vmax, vi);
+      }
+    }
+    pending &= ~cur;
+    const int Gend = min(G0 + pages_per_wg, (vmax + kPage - 1) / kPage);
+    if (G0 >= Gend) continue;  // uniform
+    const bool active = (cur >> (4 * wid + g)) & 1u;
+    const int my_nvis = active ? sm.nvis[4 * wid + g] : 0;
+    const int32_t* __restrict__ bt = block_table + (int64_t)row * max_pages;
+    const uint16_t* __restrict__ qrow = q_idx + (int64_t)qo * HI * kIndexDim;
+
+    // scores of one page from the slot holding it
+    auto page = [&](const Q4Page& s, int G) __attribute__((always_inline)) {
+      uint4 b[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) b[nt] = s.codes[64 * nt + 4 * n + (g ^ ((n >> 2) & 3))];
+      const uint8_t* sb = reinterpret_cast<const uint8_t*>(s.sc);
+      int bsc[4];  // E8M0 of (entry 16nt + l%16, block l/16)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) bsc[nt] = (int)sb[(16 * nt + n) * 4 + g];
+      float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      // step k = 4 mt + nt.  Each MFMA goes out one step ahead of the eight VALU
+      // instructions that consume the previous one (the barriers fix that order), so no
+      // wave waits on an MFMA result; the four sums interleave.
+      auto mf = [&](int k) __attribute__((always_inline)) -> v4f {
+        const int mt = k >> 2, nt = k & 3;
+        switch (mt & 3) {
+          case 0: return mfma_fp4<0>(A[mt], b[nt], (int)asc[mt >> 2], bsc[nt]);
+          case 1: return mfma_fp4<1>(A[mt], b[nt], (int)asc[mt >> 2], bsc[nt]);
+          case 2: return mfma_fp4<2>(A[mt], b[nt], (int)asc[mt >> 2], bsc[nt]);
+          default: return mfma_fp4<3>(A[mt], b[nt], (int)asc[mt >> 2], bsc[nt]);
+        }
+      };
+      v4f dprev = mf(0);
+#pragma unroll
+      for (int k = 0; k < 4 * NMT; ++k) {
+        v4f dnext = dprev;
+        if (k + 1 < 4 * NMT) dnext = mf(k + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int mt = k >> 2, nt = k & 3;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[nt] = fmaf(wr[4 * mt + r], relu(dprev[r]), acc[nt]);
+        __builtin_amdgcn_sched_barrier(0);
+        dprev = dnext;
+      }
+      // the four sums are complete here for every lane: the MFMAs (which read every
+      // lane's operands) must not move into the masked stores below
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) asm volatile("" : "+v"(acc[nt]));
+      const int j0 = G * kPage + n;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        if (j0 + 16 * nt < my_nvis) srow[j0 + 16 * nt] = acc[nt];
+      // rare: pairs outside the window where the MFMA dot is exact
+      const uint32_t ps = s.pstat;
+      const bool maybe = (G * kPage < my_nvis) &&
+                         q4_inexact(q_span, q_lo, q_hi, (int)(ps & 0xFFu), (int)((ps >> 8) & 0xFFu), (int)(ps >> 16));
+      if (__builtin_amdgcn_ballot_w64(maybe) != 0ull) {
+        const int64_t slot0 = (int64_t)bt[G] * kPage;
+#pragma unroll 1
+        for (int nt = 0; nt < 4; ++nt) {
+          const int e = 16 * nt + n;
+          const uint32_t es = s.estat[e];
+          const int klo = (int)(es & 0xFFu), khi = (int)(es >> 8);
+          if (G * kPage + e < my_nvis && q4_inexact(q_span, q_lo, q_hi, khi - klo, klo, khi)) {
+            const int64_t slot = slot0 + e;
+            srow[G * kPage + e] = q4_exact(qrow, w + (int64_t)qo * HI, HI, idx_codes + slot * kIdxRowBytes,
+                                           *reinterpret_cast<const uint32_t*>(idx_scales + slot * kIdxScaleBytes));
+          }
+        }
+      }
+    };
+
+    // steps of kQ4Group pages: two steps staged ahead in registers, two LDS slots
+    const int nst = (Gend - G0 + kQ4Group - 1) / kQ4Group;
+    auto run = [&](const Q4Page(&sl)[kQ4Group], int G) __attribute__((always_inline)) {
+#pragma unroll 1
+      for (int p = 0; p < kQ4Group; ++p) {
+        if (G + p >= Gend) break;  // uniform
+        page(sl[p], G + p);
+      }
+    };
+    // every step's loads are issued, past the last step re-reading the last page, so
+    // the wait for one register set never has to assume the other's loads are absent
+    Q4Regs r1, r2;
+    q4_load(r1, idx_codes, idx_scales, bt, G0, Gend, wid, lane);
+    q4_load(r2, idx_codes, idx_scales, bt, G0 + kQ4Group, Gend, wid, lane);
+    q4_store(sm.slot[0], r1, wid, lane);
+    q4_load(r1, idx_codes, idx_scales, bt, G0 + 2 * kQ4Group, Gend, wid, lane);
+    lds_barrier();
+    for (int i = 0; i < nst; i += 2) {
+      // slot 0: step i; r2: step i+1; r1: step i+2
+      run(sm.slot[0], G0 + i * kQ4Group);
+      if (i + 1 < nst) q4_store(sm.slot[1], r2, wid, lane);
+      q4_load(r2, idx_codes, idx_scales, bt, G0 + (i + 3) * kQ4Group, Gend, wid, lane);
+      lds_barrier();
+      if (i + 1 >= nst) break;
+      run(sm.slot[1], G0 + (i + 1) * kQ4Group);
+      if (i + 2 < nst) q4_store(sm.slot[0], r1, wid, lane);
+      q4_load(r1, idx_codes, idx_scales, bt, G0 + (i + 4) * kQ4Group, Gend, wid, lane);
+      lds_barrier();
+    }
+  }
+}
+
 // Queries per workgroup of the scan (1 when every query reads its own sequence).
 static int query_tile(const int32_t* soq, int32_t nq, size_t stage_bytes) {
   return (soq == nullptr || nq < 64) ? 1 : (stage_bytes * 8 <= 64 * 1024 ? 8 : 4);
@@ -487,10 +844,37 @@ static int launch_mt(const csa2_fp4_cache* c, const uint16_t* q_idx, const float
   return launch_status();
 }
 
+template <int NMT>
+static int launch_q4(const csa2_fp4_cache* c, const uint16_t* q_idx, const float* w, const int32_t* soq,
+                     const int32_t* nvis, const int32_t* bt, int32_t max_pages, int32_t nq, float* scores, int64_t ld,
+                     hipStream_t stream) {
+  const long long total_groups = ceil_div(ld, kPage);
+  const long long qtiles = ceil_div(nq, kQ4Queries);
+  // page chunks: about 2048 workgroups in all, each over at least kQ4MinPages pages.
+  // Workgroup (x, y) runs on XCD (y * gx + x) % 8, so with gx a multiple of 8 each
+  // XCD's L2 sees one eighth of the pages.
+  const long long chunks = std::max(1LL, (2048 + qtiles - 1) / qtiles);
+  const int ppw = (int)std::max<long long>(kQ4MinPages, (total_groups + chunks - 1) / chunks);
+  const unsigned gx = ceil_div(total_groups, ppw);
+  hipLaunchKernelGGL((index_score_q4_kernel<NMT>), dim3(gx, (unsigned)qtiles), dim3(kThreads), 0, stream,
+                     c->idx_codes, c->idx_scales, q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, ppw);
+  return launch_status();
+}
+
 static int launch_hi(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
                      const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* block_table,
                      int32_t max_pages, int32_t nq, float* scores, int64_t ld, uint32_t* hist, int k,
                      int* copies, hipStream_t stream) {
+  // queries that share sequences, at most 64 heads: four queries per wavefront
+  if (hist == nullptr && query_tile(seq_of_query, nq, 0) > 1 && Hi <= 64) {
+    if (copies != nullptr) *copies = 1;
+    switch (Hi / 16) {
+      case 1: return launch_q4<4>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
+      case 2: return launch_q4<8>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
+      case 3: return launch_q4<12>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
+      default: return launch_q4<16>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
+    }
+  }
   switch (Hi / 16) {
 #define CSA2_MT(m) \
   case m:          \

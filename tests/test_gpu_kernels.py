@@ -122,7 +122,7 @@ def test_cache_write_exhaustive_block_maxima():
     assert_cache_equal(g, o, "exhaustive", lb, kb, np.arange(n))
 
 
-def _index_case(rng, n_per_seq, Hi, nq_per_seq=1, paged=False, key_fn=None, q_fn=None, causal=False):
+def _index_case(rng, n_per_seq, Hi, nq_per_seq=1, paged=False, key_fn=None, q_fn=None, causal=False, soq=None):
     B = len(n_per_seq)
     pages = [(n + 63) // 64 for n in n_per_seq]
     total_pages = sum(pages)
@@ -144,17 +144,20 @@ def _index_case(rng, n_per_seq, Hi, nq_per_seq=1, paged=False, key_fn=None, q_fn
         key_all.append(bits(k))
     num_slots = total_pages * 64
     g, o = both_caches(np.concatenate(lat_all), np.concatenate(key_all), np.concatenate(slots_all), num_slots)
-    nq = B * nq_per_seq
+    nq = B * nq_per_seq if soq is None else len(soq)
     q = rng.standard_normal((nq, Hi, 128)).astype(np.float32)
     if q_fn is not None:
         q = q_fn(q)
     q = bits(q)
     w = rng.random((nq, Hi), dtype=np.float32)
-    soq = np.repeat(np.arange(B, dtype=np.int32), nq_per_seq)
+    soq = np.repeat(np.arange(B, dtype=np.int32), nq_per_seq) if soq is None else np.asarray(soq, np.int32)
     nvis = np.array([n_per_seq[s] for s in soq], np.int32)
-    if causal:
-        nvis = np.array([max(1, n_per_seq[s] - (nq_per_seq - 1 - i % nq_per_seq) * 3) for i, s in enumerate(soq)],
-                        np.int32)
+    if causal:  # query i of a sequence sees 3 entries more than the one before it
+        rank = np.zeros(nq, np.int64)
+        for b in range(B):
+            idx = np.nonzero(soq == b)[0]
+            rank[idx] = len(idx) - 1 - np.arange(len(idx))
+        nvis = np.maximum(1, nvis - 3 * rank).astype(np.int32)
     ld = ((max(n_per_seq) + 63) // 64) * 64
     scores = torch.full((nq, ld), float("nan"), device="cuda")
     lib.index_score(g, dev_bits(q), dev(w), dev(nvis), dev(bt), scores, seq_of_query=dev(soq))
@@ -181,6 +184,45 @@ def test_index_score_paged_three_sequences():
 def test_index_score_query_tile_shared_row():
     say("case: index_score 70 causal queries on one sequence Hi=64")
     _index_case(np.random.default_rng(220), [2000], 64, nq_per_seq=70, causal=True)
+
+
+@pytest.mark.parametrize("Hi", [16, 32, 48, 64])
+def test_index_score_shared_sequence_tiles(Hi):
+    # queries sharing a sequence: 32 per workgroup, one page range each; 1098 entries
+    # are 18 pages, so the last range of 8 pages holds only two
+    say(f"case: index_score 100 causal queries on one sequence Hi={Hi}, paged")
+    _index_case(np.random.default_rng(260 + Hi), [1098], Hi, nq_per_seq=100, causal=True, paged=True)
+
+
+def test_index_score_shared_sequence_mixed_rows():
+    # workgroups whose 32 queries read two, three or (interleaved) every sequence:
+    # one pass over the pages per distinct sequence
+    rng = np.random.default_rng(270)
+    say("case: index_score 3 sequences x 40 queries in order (workgroups straddle sequences)")
+    _index_case(rng, [700, 1300, 129], 64, nq_per_seq=40, causal=True, paged=True)
+    say("case: index_score 90 queries interleaved over 3 sequences")
+    _index_case(rng, [900, 65, 1500], 32, soq=[i % 3 for i in range(90)], causal=True, paged=True)
+
+
+def test_index_score_shared_sequence_exact_path():
+    def keys(k):
+        k[:, 0:32] *= 2.0 ** -12
+        k[:, 64:96] *= 2.0 ** 6
+        k[200:230] *= 2.0 ** -70  # with the small queries below: dots under 2^-126
+        return k
+
+    def qs(q):
+        q[:, :, 32:64] *= 2.0 ** 5
+        q[1, 3, :] = 0.0  # an all-zero head
+        q[7, 5, 96:] = 0.0  # a head with one zero block
+        q[40:44] *= 2.0 ** -70
+        q[44:48] *= 2.0 ** 104  # exponent sums above the window
+        return q
+
+    for Hi in (16, 64):
+        say(f"case: index_score shared-sequence tiles, exact path, Hi={Hi}")
+        bad = _index_case(np.random.default_rng(280 + Hi), [600], Hi, nq_per_seq=70, key_fn=keys, q_fn=qs)
+        say(f"  dots not representable in fp32: {bad}")
 
 
 def test_index_score_heads_128():

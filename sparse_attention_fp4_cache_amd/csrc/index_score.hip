@@ -446,15 +446,16 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
   }
 }
 
-// ---- scan for queries that share a sequence: four queries per wavefront ---------
-// The 16 rows of an M-tile are (query, head) pairs, four queries of four heads each,
-// so one 16x16x128 MFMA leaves lane group g the dots of query g with one entry for
-// four heads, and the Hi/4 M-tiles together give a lane every head of its (query,
-// entry) pair in head order: the weighted ReLU sum needs no lane exchange.  The
-// eight wavefronts of a workgroup (32 queries) share each page of keys, which is
-// staged once in LDS and read as the B operand; each wavefront's queries stay in
-// registers as MXFP4 A operands for the whole page range.
-constexpr int kQ4Queries = 4 * kWaves;  // queries per workgroup
+// ---- scan for queries that share a sequence: two queries per wavefront ----------
+// The 32 rows of an M-tile of the 32x32x64 MFMA are (query, head) pairs: two queries
+// of 16 heads.  Its output leaves lane l the 16 dots of query l/32 with entry l%32
+// for heads 16mt .. 16mt+15, so over the Hi/16 M-tiles a lane holds every head of its
+// (query, entry) pair in head order and the weighted ReLU sum needs no lane exchange.
+// (On gfx950 the FP4 form of this shape runs at about twice the rate of the
+// 16x16x128 one.)  The eight wavefronts of a workgroup (16 queries) share each page
+// of keys, staged once in LDS and read as the B operand; each wavefront's queries
+// stay in registers as MXFP4 A operands for the whole page range.
+constexpr int kQ4Queries = 2 * kWaves;  // queries per workgroup
 constexpr int kQ4MinPages = 8;          // fewest pages per workgroup (amortises the query staging)
 
 constexpr int kQ4Group = 4;  // pages staged per workgroup barrier
@@ -588,27 +589,29 @@ CSA2_DEV float q4_exact(const uint16_t* __restrict__ qrow, const float* __restri
   return acc;
 }
 
+typedef float v16f __attribute__((ext_vector_type(16)));
+
 template <int OA>
-CSA2_DEV v4f mfma_fp4(const uint4& a, const uint4& b, int asc, int bsc) {
+CSA2_DEV v16f mfma32_fp4(const uint4& a, const uint4& b, const v16f& c, int asc, int bsc) {
   const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
   const v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, zero, 4, 4, OA, asc, 0, bsc);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, OA, asc, 0, bsc);
 }
 
-// NMT = Hi / 4 M-tiles; Hi <= 64 keeps a wavefront's operands and weights in registers.
-template <int NMT>
-__global__ __launch_bounds__(kThreads) void index_score_q4_kernel(
+// NM = Hi / 16 M-tiles; Hi <= 64 keeps a wavefront's operands and weights in registers.
+template <int NM>
+__global__ __launch_bounds__(kThreads) void index_score_q2_kernel(
     const uint8_t* __restrict__ idx_codes, const uint8_t* __restrict__ idx_scales, const uint16_t* __restrict__ q_idx,
     const float* __restrict__ w, const int32_t* __restrict__ seq_of_query, const int32_t* __restrict__ n_visible,
     const int32_t* __restrict__ block_table, int max_pages, int nq, float* __restrict__ scores, int64_t ld,
     int pages_per_wg) {
-  constexpr int HI = 4 * NMT;
-  constexpr int NSC = (NMT + 3) / 4;
+  constexpr int HI = 16 * NM;
+  constexpr int NSC = (2 * NM + 3) / 4;
+  constexpr int S = 2 * NM;  // (N-tile, M-tile) steps of a page
   __shared__ Q4Smem sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, n = lane & 15;
+  const int half = lane >> 5, col = lane & 31;
   const int q0 = blockIdx.y * kQ4Queries;
   const int G0 = blockIdx.x * pages_per_wg;
   if (tid < kQ4Queries) {
@@ -617,54 +620,55 @@ __global__ __launch_bounds__(kThreads) void index_score_q4_kernel(
     sm.nvis[tid] = q < nq ? (int)min((int64_t)n_visible[q], ld) : 0;
   }
 
-  // A operands: lane l holds row l%16 = (query 4 wid + (l%16)/4, head 4 mt + l%4) and
-  // K-block l/16 of every M-tile mt
-  const int qa_raw = q0 + 4 * wid + (n >> 2);
+  // A operands: lane l holds row l%32 = (query 2 wid + (l%32)/4 % 2, head 16 mt +
+  // 4 ((l%32)/8) + l%4) and, for K-half kh of the MFMA, block 2 kh + l/32
+  const int qa_raw = q0 + 2 * wid + ((col >> 2) & 1);
   const bool qa_ok = qa_raw < nq;
   const int qa = qa_ok ? qa_raw : nq - 1;  // a spare row quantises a valid query and is zeroed
-  uint4 A[NMT];
+  const int head_in_tile = 4 * (col >> 3) + (col & 3);
+  uint4 A[NM][2];
   uint32_t asc[NSC];
 #pragma unroll
   for (int i = 0; i < NSC; ++i) asc[i] = 0u;
   int span = 0, lo_all = 255, hi_all = 0;
-  static_assert(NMT % 4 == 0, "M-tiles are staged four at a time");
 #pragma clang loop unroll(full)
-  for (int mt0 = 0; mt0 < NMT; mt0 += 4) {
-    QRaw raw[4];
+  for (int mt = 0; mt < NM; ++mt) {
+    QRaw raw[2];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      mx32_load(q_idx + ((int64_t)qa * HI + 4 * (mt0 + k) + (n & 3)) * kIndexDim + 32 * g, raw[k]);
+    for (int kh = 0; kh < 2; ++kh)
+      mx32_load(q_idx + ((int64_t)qa * HI + 16 * mt + head_in_tile) * kIndexDim + 32 * (2 * kh + half), raw[kh]);
+    int lo = 255, hi = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int mt = mt0 + k;
+    for (int kh = 0; kh < 2; ++kh) {
       uint4 c;
       uint32_t u;
-      mx32_block(raw[k], c, u);
+      mx32_block(raw[kh], c, u);
       if (!qa_ok) {
         c = make_uint4(0u, 0u, 0u, 0u);
         u = 127u;
       }
-      A[mt] = c;
-      asc[mt >> 2] |= u << (8 * (mt & 3));
-      int lo = (int)u, hi = (int)u;  // over the head's four blocks (lanes l, l^16, l^32, l^48)
-      lo = min(lo, __shfl_xor(lo, 16));
-      hi = max(hi, __shfl_xor(hi, 16));
-      lo = min(lo, __shfl_xor(lo, 32));
-      hi = max(hi, __shfl_xor(hi, 32));
-      span = max(span, hi - lo);
-      lo_all = min(lo_all, lo);
-      hi_all = max(hi_all, hi);
+      A[mt][kh] = c;
+      const int sl = 2 * mt + kh;
+      asc[sl >> 2] |= u << (8 * (sl & 3));
+      lo = min(lo, (int)u);
+      hi = max(hi, (int)u);
     }
+    lo = min(lo, __shfl_xor(lo, 32));  // the head's other two blocks
+    hi = max(hi, __shfl_xor(hi, 32));
+    span = max(span, hi - lo);
+    lo_all = min(lo_all, lo);
+    hi_all = max(hi_all, hi);
   }
 #pragma unroll
-  for (int o = 1; o < 4; o <<= 1) {  // over the query's heads within an M-tile
+  for (int o = 1; o < 32; o <<= 1) {  // over the query's heads (lane bits 0, 1, 3, 4)
+    if (o == 4) continue;
     span = max(span, __shfl_xor(span, o));
     lo_all = min(lo_all, __shfl_xor(lo_all, o));
     hi_all = max(hi_all, __shfl_xor(hi_all, o));
   }
-  // output side: lane l serves query 4 wid + l/16, whose statistics lane 4(l/16) holds
-  const int q_span = __shfl(span, 4 * g), q_lo = __shfl(lo_all, 4 * g), q_hi = __shfl(hi_all, 4 * g);
-  const int qo = q0 + 4 * wid + g;
+  // output side: lane l serves query 2 wid + l/32, whose statistics lane 4(l/32) holds
+  const int q_span = __shfl(span, 4 * half), q_lo = __shfl(lo_all, 4 * half), q_hi = __shfl(hi_all, 4 * half);
+  const int qo = q0 + 2 * wid + half;
   float wr[HI];
   {
     const float4* wsrc = reinterpret_cast<const float4*>(w + (int64_t)(qo < nq ? qo : nq - 1) * HI);
@@ -678,6 +682,13 @@ __global__ __launch_bounds__(kThreads) void index_score_q4_kernel(
     }
   }
   float* __restrict__ srow = scores + (int64_t)qo * ld;
+  // score stores go through a buffer resource over the wavefront's two rows: a lane
+  // with nothing to write gets an offset past the end, which the hardware drops.  With
+  // no branch around them the stores are counted by every later wait, so a wait for
+  // staged keys never has to wait for the stores too.
+  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+      scores + (int64_t)(q0 + 2 * wid) * ld, (short)0, (int)(2 * ld * (int64_t)sizeof(float)), 0x00020000);
+  const uint32_t srow_off = (uint32_t)half * (uint32_t)ld * 4u;
   lds_barrier();
   // operands and weights are in registers before the page loop, whose waits then only
   // cover the keys staged ahead
@@ -686,7 +697,7 @@ __global__ __launch_bounds__(kThreads) void index_score_q4_kernel(
 
   // one row of the block table at a time: the first pending query's row, with every
   // pending query of the workgroup that reads it
-  uint32_t pending = (nq - q0 >= kQ4Queries) ? 0xFFFFFFFFu : ((1u << (nq - q0)) - 1u);
+  uint32_t pending = (nq - q0 >= kQ4Queries) ? (1u << kQ4Queries) - 1u : ((1u << (nq - q0)) - 1u);
   while (pending != 0u) {
     const int row = __builtin_amdgcn_readfirstlane(sm.row[__builtin_ctz(pending)]);
     uint32_t cur = 0u;
@@ -702,80 +713,104 @@ __global__ __launch_bounds__(kThreads) void index_score_q4_kernel(
     pending &= ~cur;
     const int Gend = min(G0 + pages_per_wg, (vmax + kPage - 1) / kPage);
     if (G0 >= Gend) continue;  // uniform
-    const bool active = (cur >> (4 * wid + g)) & 1u;
-    const int my_nvis = active ? sm.nvis[4 * wid + g] : 0;
+    const bool active = (cur >> (2 * wid + half)) & 1u;
+    const int my_nvis = active ? sm.nvis[2 * wid + half] : 0;
     const int32_t* __restrict__ bt = block_table + (int64_t)row * max_pages;
     const uint16_t* __restrict__ qrow = q_idx + (int64_t)qo * HI * kIndexDim;
 
     // scores of one page from the slot holding it
-    auto page = [&](const Q4Page& s, int G) __attribute__((always_inline)) {
-      uint4 b[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) b[nt] = s.codes[64 * nt + 4 * n + (g ^ ((n >> 2) & 3))];
+    // (pages at or past Gend are computed on whatever the slot holds and write nothing;
+    // pairs that need the exact path are left out of the stores and flagged in bits
+    // 2p + nt of xbits)
+    auto page = [&](const Q4Page& s, int G, int p, uint32_t& xbits) __attribute__((always_inline)) {
+      uint4 b[2][2];  // N-tile nt, K-half kh: 16 bytes of entry 32nt + l%32, block 2kh + l/32
+      int bsc[2][2];
       const uint8_t* sb = reinterpret_cast<const uint8_t*>(s.sc);
-      int bsc[4];  // E8M0 of (entry 16nt + l%16, block l/16)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) bsc[nt] = (int)sb[(16 * nt + n) * 4 + g];
-      float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      // step k = 4 mt + nt.  Each MFMA goes out one step ahead of the eight VALU
-      // instructions that consume the previous one (the barriers fix that order), so no
-      // wave waits on an MFMA result; the four sums interleave.
-      auto mf = [&](int k) __attribute__((always_inline)) -> v4f {
-        const int mt = k >> 2, nt = k & 3;
-        switch (mt & 3) {
-          case 0: return mfma_fp4<0>(A[mt], b[nt], (int)asc[mt >> 2], bsc[nt]);
-          case 1: return mfma_fp4<1>(A[mt], b[nt], (int)asc[mt >> 2], bsc[nt]);
-          case 2: return mfma_fp4<2>(A[mt], b[nt], (int)asc[mt >> 2], bsc[nt]);
-          default: return mfma_fp4<3>(A[mt], b[nt], (int)asc[mt >> 2], bsc[nt]);
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          const int e = 32 * nt + col, c = 2 * kh + half;
+          b[nt][kh] = s.codes[4 * e + (c ^ ((e >> 2) & 3))];
+          bsc[nt][kh] = (int)sb[4 * e + c];
+        }
+      float acc[2] = {0.0f, 0.0f};
+      // step t = (N-tile t / NM, M-tile t % NM); its two MFMAs (K-halves) go out
+      // around the VALU work of step t-2, so neither the accumulate nor the VALU
+      // waits on an MFMA result (the barriers fix that order)
+      auto mf = [&](int t, int kh, const v16f& c) __attribute__((always_inline)) -> v16f {
+        const int nt = t / NM, mt = t % NM, sl = 2 * mt + kh;
+        switch (sl & 3) {
+          case 0: return mfma32_fp4<0>(A[mt][kh], b[nt][kh], c, (int)asc[sl >> 2], bsc[nt][kh]);
+          case 1: return mfma32_fp4<1>(A[mt][kh], b[nt][kh], c, (int)asc[sl >> 2], bsc[nt][kh]);
+          case 2: return mfma32_fp4<2>(A[mt][kh], b[nt][kh], c, (int)asc[sl >> 2], bsc[nt][kh]);
+          default: return mfma32_fp4<3>(A[mt][kh], b[nt][kh], c, (int)asc[sl >> 2], bsc[nt][kh]);
         }
       };
-      v4f dprev = mf(0);
+      const v16f zero = {};
+      v16f D[2];
 #pragma unroll
-      for (int k = 0; k < 4 * NMT; ++k) {
-        v4f dnext = dprev;
-        if (k + 1 < 4 * NMT) dnext = mf(k + 1);
+      for (int t = 0; t < S + 2; ++t) {
+        v16f T;
+        if (t < S) T = mf(t, 0, zero);
         __builtin_amdgcn_sched_barrier(0);
-        const int mt = k >> 2, nt = k & 3;
+        if (t >= 2) {
+          const int u = t - 2, nt = u / NM, mt = u % NM;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[nt] = fmaf(wr[4 * mt + r], relu(dprev[r]), acc[nt]);
+          for (int r = 0; r < 16; ++r) acc[nt] = fmaf(wr[16 * mt + r], relu(D[t & 1][r]), acc[nt]);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        dprev = dnext;
+        if (t < S) D[t & 1] = mf(t, 1, T);
       }
-      // the four sums are complete here for every lane: the MFMAs (which read every
-      // lane's operands) must not move into the masked stores below
+      // the sums are complete here for every lane: the MFMAs (which read every lane's
+      // operands) must not move into the masked stores below
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) asm volatile("" : "+v"(acc[nt]));
-      const int j0 = G * kPage + n;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        if (j0 + 16 * nt < my_nvis) srow[j0 + 16 * nt] = acc[nt];
+      for (int nt = 0; nt < 2; ++nt) asm volatile("" : "+v"(acc[nt]));
       // rare: pairs outside the window where the MFMA dot is exact
+      const int vis = G < Gend ? my_nvis : 0;  // entries of this page the lane may write
+      bool need[2] = {false, false};
       const uint32_t ps = s.pstat;
-      const bool maybe = (G * kPage < my_nvis) &&
+      const bool maybe = (G * kPage < vis) &&
                          q4_inexact(q_span, q_lo, q_hi, (int)(ps & 0xFFu), (int)((ps >> 8) & 0xFFu), (int)(ps >> 16));
       if (__builtin_amdgcn_ballot_w64(maybe) != 0ull) {
-        const int64_t slot0 = (int64_t)bt[G] * kPage;
-#pragma unroll 1
-        for (int nt = 0; nt < 4; ++nt) {
-          const int e = 16 * nt + n;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int e = 32 * nt + col;
           const uint32_t es = s.estat[e];
           const int klo = (int)(es & 0xFFu), khi = (int)(es >> 8);
-          if (G * kPage + e < my_nvis && q4_inexact(q_span, q_lo, q_hi, khi - klo, klo, khi)) {
-            const int64_t slot = slot0 + e;
-            srow[G * kPage + e] = q4_exact(qrow, w + (int64_t)qo * HI, HI, idx_codes + slot * kIdxRowBytes,
-                                           *reinterpret_cast<const uint32_t*>(idx_scales + slot * kIdxScaleBytes));
-          }
+          need[nt] = G * kPage + e < vis && q4_inexact(q_span, q_lo, q_hi, khi - klo, klo, khi);
         }
+      }
+      const int j0 = G * kPage + col;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int j = j0 + 32 * nt;
+        const uint32_t off = (j < vis && !need[nt]) ? srow_off + (uint32_t)j * 4u : 0xFFFFFFF0u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[nt]), srsrc, off, 0, 0);
+        xbits |= (uint32_t)need[nt] << (2 * p + nt);
       }
     };
 
     // steps of kQ4Group pages: two steps staged ahead in registers, two LDS slots
     const int nst = (Gend - G0 + kQ4Group - 1) / kQ4Group;
+    // one step: its pages in straight-line code, so every score store is counted by the
+    // waits that follow; then the flagged pairs by the definition itself
     auto run = [&](const Q4Page(&sl)[kQ4Group], int G) __attribute__((always_inline)) {
-#pragma unroll 1
-      for (int p = 0; p < kQ4Group; ++p) {
-        if (G + p >= Gend) break;  // uniform
-        page(sl[p], G + p);
+      uint32_t xbits = 0u;
+#pragma unroll
+      for (int p = 0; p < kQ4Group; ++p) page(sl[p], G + p, p, xbits);
+      if (__builtin_amdgcn_ballot_w64(xbits != 0u) != 0ull) {
+        while (xbits != 0u) {
+          const int bit = __builtin_ctz(xbits);
+          xbits &= xbits - 1u;
+          const int Gp = G + (bit >> 1), e = 32 * (bit & 1) + col;
+          const int64_t slot = (int64_t)bt[Gp] * kPage + e;
+          srow[Gp * kPage + e] = q4_exact(qrow, w + (int64_t)qo * HI, HI, idx_codes + slot * kIdxRowBytes,
+                                          *reinterpret_cast<const uint32_t*>(idx_scales + slot * kIdxScaleBytes));
+        }
+        // nothing of this rare branch stays in flight, so the waits after it count only
+        // the staging loads and score stores of the common path
+        __builtin_amdgcn_s_waitcnt(0);
       }
     };
     // every step's loads are issued, past the last step re-reading the last page, so
@@ -787,7 +822,8 @@ __global__ __launch_bounds__(kThreads) void index_score_q4_kernel(
     q4_load(r1, idx_codes, idx_scales, bt, G0 + 2 * kQ4Group, Gend, wid, lane);
     lds_barrier();
     for (int i = 0; i < nst; i += 2) {
-      // slot 0: step i; r2: step i+1; r1: step i+2
+      // slot 0: step i; r2: step i+1; r1: step i+2 (each register set keeps its role,
+      // so no staged value is ever copied while its load is in flight)
       run(sm.slot[0], G0 + i * kQ4Group);
       if (i + 1 < nst) q4_store(sm.slot[1], r2, wid, lane);
       q4_load(r2, idx_codes, idx_scales, bt, G0 + (i + 3) * kQ4Group, Gend, wid, lane);
@@ -844,8 +880,8 @@ static int launch_mt(const csa2_fp4_cache* c, const uint16_t* q_idx, const float
   return launch_status();
 }
 
-template <int NMT>
-static int launch_q4(const csa2_fp4_cache* c, const uint16_t* q_idx, const float* w, const int32_t* soq,
+template <int NM>
+static int launch_q2(const csa2_fp4_cache* c, const uint16_t* q_idx, const float* w, const int32_t* soq,
                      const int32_t* nvis, const int32_t* bt, int32_t max_pages, int32_t nq, float* scores, int64_t ld,
                      hipStream_t stream) {
   const long long total_groups = ceil_div(ld, kPage);
@@ -856,7 +892,7 @@ static int launch_q4(const csa2_fp4_cache* c, const uint16_t* q_idx, const float
   const long long chunks = std::max(1LL, (2048 + qtiles - 1) / qtiles);
   const int ppw = (int)std::max<long long>(kQ4MinPages, (total_groups + chunks - 1) / chunks);
   const unsigned gx = ceil_div(total_groups, ppw);
-  hipLaunchKernelGGL((index_score_q4_kernel<NMT>), dim3(gx, (unsigned)qtiles), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((index_score_q2_kernel<NM>), dim3(gx, (unsigned)qtiles), dim3(kThreads), 0, stream,
                      c->idx_codes, c->idx_scales, q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, ppw);
   return launch_status();
 }
@@ -865,14 +901,15 @@ static int launch_hi(const csa2_fp4_cache* cache, const uint16_t* q_idx, const f
                      const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* block_table,
                      int32_t max_pages, int32_t nq, float* scores, int64_t ld, uint32_t* hist, int k,
                      int* copies, hipStream_t stream) {
-  // queries that share sequences, at most 64 heads: four queries per wavefront
-  if (hist == nullptr && query_tile(seq_of_query, nq, 0) > 1 && Hi <= 64) {
+  // queries that share sequences, at most 64 heads: two queries per wavefront (two
+  // score rows within one buffer resource's 2^31-byte range)
+  if (hist == nullptr && query_tile(seq_of_query, nq, 0) > 1 && Hi <= 64 && ld < ((int64_t)1 << 28)) {
     if (copies != nullptr) *copies = 1;
     switch (Hi / 16) {
-      case 1: return launch_q4<4>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
-      case 2: return launch_q4<8>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
-      case 3: return launch_q4<12>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
-      default: return launch_q4<16>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
+      case 1: return launch_q2<1>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
+      case 2: return launch_q2<2>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
+      case 3: return launch_q2<3>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
+      default: return launch_q2<4>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
     }
   }
   switch (Hi / 16) {

@@ -12,9 +12,11 @@ its cache out of the MALL.  Warm mode (one copy, replayed) is reported beside it
 
 Prints ONE JSON line: tokens/s (sequences / step time), the FP4 cache bytes read
 per step and their rate, a roofline record for the indexer scan (the kernel that
-carries the FP4 bytes), timed with HIP events on its own stream over graph
-replays of back-to-back launches, the same timing for each library call of the
-step, and the CPU oracle on a bounded sample.
+carries the FP4 bytes: HBM-bound in decode, FP4-MFMA-bound in the prefill chunk,
+where it is a dense contraction), timed with HIP events on its own stream over
+graph replays of back-to-back launches, the same timing for each library call of
+the step (in prefill also the attention's bf16 MFMA rate), and the CPU oracle on
+a bounded sample.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -32,6 +34,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 MFMA, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+INDEX_DIM = 128
+LATENT_DIM = 512
 IDX_ENTRY_BYTES = 68  # 64 B of E2M1 codes + 4 E8M0 scales per indexer key
 MAIN_ENTRY_BYTES = 288  # 256 B of E2M1 codes + 32 E4M3 scales per main entry
 MALL_BYTES = 256 << 20
@@ -268,6 +273,11 @@ def main():
     else:
         scan = [functools.partial(lib.index_score, s.cache, s.q_idx, s.w, s.n_visible, s.block_table2d, s.scores,
                                   seq_of_query=s.seq_of_query) for s in steps]
+        calls_us["topk_select"] = burst_ms([functools.partial(lib.topk_select, st.scores, st.n_visible, wl.K,
+                                                              st.topk, st.ws_topk)], target=8)[0] * 1e3
+        calls_us["sparse_attn_prefill_chunk"] = burst_ms([functools.partial(
+            lib.sparse_attn_prefill_chunk, s.cache, st.q, st.topk, s.block_table, int(wl.ctx[0]), st.swa,
+            st.swa_first_valid, wl.W, st.scale, st.out, st.lse, st.ws_attn) for s in steps], target=8)[0] * 1e3
         idx_bytes = int(wl.n_visible().astype("int64").sum()) * IDX_ENTRY_BYTES
         tokens = wl.chunk
     idx_ms, idx_launches = burst_ms(scan)
@@ -316,9 +326,25 @@ def main():
         "calls_us": calls_us,
     }
     if wl.kind == "prefill":
-        flop = int(wl.n_visible().astype("int64").sum()) * wl.Hi * 128 * 2
-        res["roofline_mfma_fp4"] = {"kernel": "index_score", "achieved": flop / (idx_ms * 1e-3) / 1e12,
-                                    "peak": MFMA_FP4_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        # the prefill scan is a dense FP4 contraction (every query against every visible
+        # key, all index heads): its roofline is the FP4 MFMA peak, not HBM
+        flop = int(wl.n_visible().astype("int64").sum()) * wl.Hi * INDEX_DIM * 2
+        tflops = flop / (idx_ms * 1e-3) / 1e12
+        res["roofline"] = {"kernel": "index_score", "bound": "mfma", "achieved": tflops,
+                           "peak": MFMA_FP4_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tflops / MFMA_FP4_PEAK_TFLOPS,
+                           "traffic": traffic, "flop_per_launch": flop, "avg_launch_ms": idx_ms,
+                           "launches_timed": idx_launches}
+        res["roofline_hbm_view"] = {"kernel": "index_score", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                                    "unit": "GB/s", "bytes_per_launch": idx_bytes}
+        # attention: q.k over the selected entries and the window, then p.v, all heads
+        # (bf16 MFMA after dequantisation)
+        attn_flop = wl.chunk * (wl.K + wl.W) * wl.H * LATENT_DIM * 2 * 2
+        attn_ms = calls_us["sparse_attn_prefill_chunk"] * 1e-3
+        res["attention_mfma_bf16"] = {"kernel": "sparse_attn_prefill_chunk",
+                                      "achieved": attn_flop / (attn_ms * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                                      "unit": "TFLOP/s",
+                                      "frac": attn_flop / (attn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                                      "flop_per_launch": attn_flop}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(res), flush=True)

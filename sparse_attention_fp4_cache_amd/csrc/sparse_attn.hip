@@ -97,8 +97,12 @@ constexpr int kOStride = kLatentDim + 4;  // floats per head row (rows start 4 b
 static_assert(16 * kOStride * sizeof(float) <= sizeof(HalfSmem::x), "combine area");
 static_assert(2 * 16 * 2 * sizeof(float) <= sizeof(HalfSmem::red), "combine (m, l) area");
 
-CSA2_DEV uint32_t pack_bf16_hi(float lo, float hi) {  // exact values only (low 16 bits zero)
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// two fp32 -> packed bf16 (V_CVT_PK_BF16_F32, round to nearest even; exact for values
+// that fit bf16, such as every dequantised E2M1 x E4M3 product)
+CSA2_DEV uint32_t pack_bf16(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 CSA2_DEV uint32_t bf16_rne_bits(float f) {  // fp32 -> bf16 bits, round to nearest even (finite f)
@@ -157,8 +161,8 @@ CSA2_DEV uint4 dequant8(uint32_t c, float s) {
   const v2f d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
   const v2f d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
   const v2f d3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
-  return make_uint4(pack_bf16_hi(d0[0] * s, d0[1] * s), pack_bf16_hi(d1[0] * s, d1[1] * s),
-                    pack_bf16_hi(d2[0] * s, d2[1] * s), pack_bf16_hi(d3[0] * s, d3[1] * s));
+  return make_uint4(pack_bf16(d0[0] * s, d0[1] * s), pack_bf16(d1[0] * s, d1[1] * s),
+                    pack_bf16(d2[0] * s, d2[1] * s), pack_bf16(d3[0] * s, d3[1] * s));
 }
 
 // Dequantise the loaded bytes into X (row-major, swizzled chunks) in LDS.
@@ -434,11 +438,20 @@ CSA2_DEV void issue_wide(const AttnArgs& a, const int* src_rows, int tid, int ti
   }
 }
 
-CSA2_DEV void store_wide(uint16_t* x, int tid, const WideRegs& t, bool has_main) {
+CSA2_DEV void store_wide(uint16_t* x, int tid, const WideRegs& t, bool has_main, bool has_win) {
   const int row = tid >> 4, c16 = tid & 15;
   uint4* xr = reinterpret_cast<uint4*>(x + row * kXStride);
   const uint32_t wmask = t.kind == 2 ? ~0u : 0u;
-  if (has_main) {
+  if (has_main && !has_win) {
+    // FP4 rows only: a row that is not an entry dequantises code 0 with scale 0 (the
+    // loaded bytes of its stand-in slot are not used), which is +0 in every channel
+    const bool m = t.kind == 1;
+    const uint32_t sc = m ? t.sc : 0u;
+    const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)sc, 0), s1 = __builtin_amdgcn_cvt_f32_fp8((int)sc, 1);
+    const uint32_t cw[4] = {m ? t.code.x : 0u, m ? t.code.y : 0u, m ? t.code.z : 0u, m ? t.code.w : 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xr[xchunk(4 * c16 + i)] = dequant8(cw[i], i < 2 ? s0 : s1);
+  } else if (has_main) {
     const uint32_t mmask = t.kind == 1 ? ~0u : 0u;
     const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)t.sc, 0), s1 = __builtin_amdgcn_cvt_f32_fp8((int)t.sc, 1);
     const uint32_t cw[4] = {t.code.x, t.code.y, t.code.z, t.code.w};
@@ -501,7 +514,7 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
   issue_wide(a, smem.src, tid, 0, has_main(0), has_win(0), cur);
   for (int row0 = 0; row0 < seg_n; row0 += kRT) {
     lds_barrier();  // previous tile fully consumed
-    store_wide(smem.x, tid, cur, has_main(row0));
+    store_wide(smem.x, tid, cur, has_main(row0), has_win(row0));
     const int next0 = row0 + kRT;
     if (next0 < seg_n) issue_wide(a, smem.src, tid, next0, has_main(next0), has_win(next0), cur);
     lds_barrier();
@@ -551,19 +564,21 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float a0 = p[i >> 1][2 * (i & 1)], a1 = p[i >> 1][2 * (i & 1) + 1];
-      const uint32_t h0 = bf16_rne_bits(a0), h1 = bf16_rne_bits(a1);
-      phi[i] = h0 | (h1 << 16);
-      const float r0 = a0 - __uint_as_float(h0 << 16), r1 = a1 - __uint_as_float(h1 << 16);
-      plo[i] = bf16_rne_bits(r0) | (bf16_rne_bits(r1) << 16);
+      phi[i] = pack_bf16(a0, a1);
+      plo[i] = pack_bf16(a0 - __uint_as_float(phi[i] << 16), a1 - __uint_as_float(phi[i] & 0xFFFF0000u));
     }
     const bf16x8 Bhi = as_bf16x8(make_uint4(phi[0], phi[1], phi[2], phi[3]));
     const bf16x8 Blo = as_bf16x8(make_uint4(plo[0], plo[1], plo[2], plo[3]));
+    // rescale O only when some head's running maximum moved (alpha == 1 leaves it as is)
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0ull) {
+#pragma unroll
+      for (int mt = 0; mt < 16; ++mt) acc[mt] *= alpha;
+    }
     // X^T operand of M-tile mt (channels 256*kh + 16*mt + ..), transposing LDS reads
     const int tr_c = n16 & 3;
     const uint16_t* tr_row = smem.x + (8 * g + (n16 >> 2)) * kXStride + 4 * (tr_c & 1);
 #pragma unroll
     for (int mt = 0; mt < 16; ++mt) {
-      acc[mt] *= alpha;
       const uint16_t* tp = tr_row + 8 * xchunk(32 * kh + 2 * mt + (tr_c >> 1));
       const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)tp);
       const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tp + 4 * kXStride));

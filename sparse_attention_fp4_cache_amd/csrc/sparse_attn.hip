@@ -400,10 +400,11 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a) {
 // share them, so both keep the same softmax state.  A thread gathers 32 channels of
 // one tile row (16 code bytes + 2 scale bytes, or 64 bytes of a window row).
 constexpr int kWideHeads = 64;
+constexpr int kWideMaxRows = CSA2_MAX_K + CSA2_MAX_WINDOW;
 struct __align__(16) WideSmem {
-  uint16_t x[kRT * kXStride];  // X[row][ch], 16-byte chunks swizzled by xchunk()
-  float red[4][2][2][4][64];   // partial logits [head group][channel half][mtile][r][lane]
-  int src[kSeg];
+  uint16_t x[3][kRT * kXStride];  // X[row][ch] of three tiles, 16-byte chunks swizzled by xchunk()
+  float red[2][4][2][2][4][64];   // partial logits [tile parity][head group][channel half][mtile][r][lane]
+  int src[kWideMaxRows];          // source of every row of the query
 };
 static_assert(sizeof(WideSmem) <= 160 * 1024, "attention LDS exceeds 160 KB");
 
@@ -486,14 +487,11 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
   for (int mt = 0; mt < 16; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  for (int seg0 = 0; seg0 < nrows; seg0 += kSeg) {
-  const int seg_n = min(kSeg, nrows - seg0);
-  lds_barrier();  // the previous segment's sources are no longer read
-  const int seg_pad = (seg_n + kRT - 1) / kRT * kRT;
-  for (int rl = tid; rl < seg_pad; rl += kThreads) {
-    const int r = seg0 + rl;
+  // sources of every row (FP4 slot, -2 - window row, or -1 for none), padded to tiles
+  const int nrows_pad = (nrows + kRT - 1) / kRT * kRT;
+  for (int r = tid; r < nrows_pad; r += kThreads) {
     int src = -1;
-    if (rl >= seg_n) {
+    if (r >= nrows) {
     } else if (r < a.k) {
       const int j = a.topk_idx[(int64_t)qrow * a.k + r];
       if (j >= 0) src = a.block_table[(int64_t)bt_row * a.max_pages + (j >> 6)] * kPage + (j & 63);
@@ -505,45 +503,55 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
         src = -2 - (qrow * a.window + wr);
       }
     }
-    smem.src[rl] = src;
+    smem.src[r] = src;
   }
   lds_barrier();
-  auto has_main = [&](int rl0) { return seg0 + rl0 < a.k; };
-  auto has_win = [&](int rl0) { return a.window > 0 && seg0 + rl0 + kRT > a.k; };
+  auto has_main = [&](int r0) { return r0 < a.k; };
+  auto has_win = [&](int r0) { return a.window > 0 && r0 + kRT > a.k; };
+  const int ntiles = nrows_pad / kRT;
+
+  // One barrier per tile.  Iteration t: partial logits of tile t (X buffer t%3) into
+  // red[t%2]; dequantise tile t+1 (loaded during iteration t-1) into X buffer (t+1)%3;
+  // issue the loads of tile t+2; barrier; then the softmax and P.X of tile t.  The
+  // buffer written in iteration t was last read in iteration t-2, and red[t%2] in
+  // iteration t-2, both before the barrier of iteration t-1.
   WideRegs cur;
   issue_wide(a, smem.src, tid, 0, has_main(0), has_win(0), cur);
-  for (int row0 = 0; row0 < seg_n; row0 += kRT) {
-    lds_barrier();  // previous tile fully consumed
-    store_wide(smem.x, tid, cur, has_main(row0), has_win(row0));
-    const int next0 = row0 + kRT;
-    if (next0 < seg_n) issue_wide(a, smem.src, tid, next0, has_main(next0), has_win(next0), cur);
-    lds_barrier();
+  store_wide(smem.x[0], tid, cur, has_main(0), has_win(0));
+  if (ntiles > 1) issue_wide(a, smem.src, tid, kRT, has_main(kRT), has_win(kRT), cur);
+  lds_barrier();
+  for (int t = 0; t < ntiles; ++t) {
+    const int row0 = t * kRT;
+    const uint16_t* xt = smem.x[t % 3];
+    float(&red)[4][2][2][4][64] = smem.red[t & 1];
     // ---- partial logits over this wavefront's 256 channels, two 16-row M-tiles
-    v4f s[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      s[t] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < 2; ++tt) {
+      v4f sl = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const int xrow = 8 * (n16 >> 2) + 4 * t + (n16 & 3);  // lane group g gets rows 8g .. 8g+7
-        const uint4 xa = reinterpret_cast<const uint4*>(smem.x + xrow * kXStride)[xchunk(32 * kh + 4 * ks + g)];
-        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(qop[ks]), s[t], 0, 0, 0);
+        const int xrow = 8 * (n16 >> 2) + 4 * tt + (n16 & 3);  // lane group g gets rows 8g .. 8g+7
+        const uint4 xa = reinterpret_cast<const uint4*>(xt + xrow * kXStride)[xchunk(32 * kh + 4 * ks + g)];
+        sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(qop[ks]), sl, 0, 0, 0);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) smem.red[hg][kh][t][r][lane] = s[t][r];
+      for (int r = 0; r < 4; ++r) red[hg][kh][tt][r][lane] = sl[r];
     }
+    if (t + 1 < ntiles) store_wide(smem.x[(t + 1) % 3], tid, cur, has_main(row0 + kRT), has_win(row0 + kRT));
+    if (t + 2 < ntiles)
+      issue_wide(a, smem.src, tid, row0 + 2 * kRT, has_main(row0 + 2 * kRT), has_win(row0 + 2 * kRT), cur);
     lds_barrier();
     float z[2][4];
     float tmax = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float v = smem.red[hg][0][t][r][lane] + smem.red[hg][1][t][r][lane];
-        const int rl = row0 + 8 * g + 4 * t + r;
-        const bool valid = (rl < seg_n) & (smem.src[rl & (kSeg - 1)] != -1);
-        z[t][r] = valid ? v * a.scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, z[t][r]);
+        const float v = red[hg][0][tt][r][lane] + red[hg][1][tt][r][lane];
+        const int rl = row0 + 8 * g + 4 * tt + r;
+        const bool valid = smem.src[rl] != -1;
+        z[tt][r] = valid ? v * a.scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, z[tt][r]);
       }
     tmax = max_rows(tmax);
     const float m_new = fmaxf(m_run, tmax);
@@ -551,11 +559,11 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
     float p[2][4];
     float psum = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[t][r] = fast_exp2(z[t][r] - (m_new == -INFINITY ? 0.0f : m_new));
-        psum += p[t][r];
+        p[tt][r] = fast_exp2(z[tt][r] - (m_new == -INFINITY ? 0.0f : m_new));
+        psum += p[tt][r];
       }
     psum = sum_rows(psum);
     l_run = l_run * alpha + psum;
@@ -576,7 +584,7 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
     }
     // X^T operand of M-tile mt (channels 256*kh + 16*mt + ..), transposing LDS reads
     const int tr_c = n16 & 3;
-    const uint16_t* tr_row = smem.x + (8 * g + (n16 >> 2)) * kXStride + 4 * (tr_c & 1);
+    const uint16_t* tr_row = xt + (8 * g + (n16 >> 2)) * kXStride + 4 * (tr_c & 1);
 #pragma unroll
     for (int mt = 0; mt < 16; ++mt) {
       const uint16_t* tp = tr_row + 8 * xchunk(32 * kh + 2 * mt + (tr_c >> 1));
@@ -587,7 +595,6 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Blo, acc[mt], 0, 0, 0);
     }
   }
-  }  // segments
 
   // ---- write: lane holds head `head`, channels 256*kh + 16*mt + 4*g + r
   const float inv = (l_run > 0.0f) ? __builtin_amdgcn_rcpf(l_run) : 0.0f;

@@ -561,6 +561,8 @@ struct RowLists {
   }
 };
 
+// ncopies == 0: no counting pass ran; the workgroup counts its row's first digits
+// itself (a read of the row that leaves it in the caches for the listing pass).
 __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restrict__ scores, int64_t ld,
                                                             const int32_t* __restrict__ n_visible, int k,
                                                             int32_t* __restrict__ topk_idx, uint32_t* __restrict__ hist,
@@ -576,6 +578,35 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
   const float* row = scores + (int64_t)q * ld;
   uint32_t* gh = hist + (size_t)q * kTopkHistCopies * kBins;
   uint32_t hb[kPerBins] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  if (ncopies == 0) {
+#pragma unroll
+    for (int i = 0; i < kBins / kThreads; ++i) sm.h[tid + i * kThreads] = 0u;
+    lds_barrier();
+    // four 16-byte loads in flight per thread per round (8192 entries per round)
+    const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+    for (int64_t r0 = 0; r0 < n; r0 += 4 * 4 * kThreads) {
+      float v[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t j = r0 + 4 * (tid + u * kThreads);
+        if (aligned && j + 4 <= n) {
+          const float4 f = *reinterpret_cast<const float4*>(row + j);
+          v[u][0] = f.x, v[u][1] = f.y, v[u][2] = f.z, v[u][3] = f.w;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[u][i] = j + i < n ? row[j + i] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (r0 + 4 * (tid + u * kThreads) + i < n) atomicAdd(&sm.h[score_key(v[u][i]) >> kBinShift], 1u);
+    }
+    lds_barrier();
+    bins_from_lds(sm.h, hb);
+    lds_barrier();  // every thread has its bins before the digit-2 histogram is cleared below
+  }
   uint4 hc[kTopkHistCopies][2];
 #pragma unroll
   for (int r = 0; r < kTopkHistCopies; ++r)
@@ -747,11 +778,11 @@ int topk_enqueue(const float* scores, int64_t ld, const int32_t* n_visible, int3
   const TopkWs w = carve(ws, nq, nchunk);
   const dim3 grid((unsigned)grid_x, (unsigned)nq);
   const int ncopies = hist_done ? copies : topk_hist_copies(nchunk);
-  if (ld > 0 && !hist_done)
+  if (ld > 0 && !hist_done && nq < kRowSelectQueries)
     hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kThreads), 0, stream, scores, ld, n_visible, k, w, ncopies);
-  if (nq >= kRowSelectQueries) {  // many rows: one workgroup per row
+  if (nq >= kRowSelectQueries) {  // many rows: one workgroup per row, counting its own row
     hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)nq), dim3(kThreads), 0, stream, scores, ld, n_visible, k,
-                       topk_idx, w.hist, ncopies);
+                       topk_idx, w.hist, hist_done ? ncopies : 0);
     return launch_status();
   }
   hipLaunchKernelGGL(topk_select_kernel, grid, dim3(kThreads), 0, stream, scores, ld, n_visible, k, topk_idx, w,

@@ -10,7 +10,9 @@ this package.  It shares no code with the GPU library.
 
 Functions whose parity is not pinned by a value printed on the pages (they are
 pinned by invariants, special cases and brute force in the tests instead):
-the NV16/MX32 rounding rules, the index-score formula, the softmax scale.
+the NV16/MX32 rounding rules, the index-score formula, the softmax scale, and the
+candidate-pool rule (block ranking by the largest member score: the pages give the
+pool's size and shape, 2048 blocks of 8, but not the rule).
 """
 from __future__ import annotations
 
@@ -64,6 +66,11 @@ def lib():
         L.oracle_index_score.argtypes = [_P, _P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _P, _I64, _P]
         L.oracle_index_score.restype = _I64
         L.oracle_topk_select.argtypes = [_P, _I64, _P, _I32, _I32, _P]
+        L.oracle_pool_build.argtypes = [_P, _I64, _P, _I32, _I32, _P]
+        L.oracle_index_score_pool.argtypes = [_P, _P, _P, _P, _I32, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _P,
+                                              _P]
+        L.oracle_index_score_pool.restype = _I64
+        L.oracle_topk_pool.argtypes = [_P, _P, _I32, _P, _I32, _I32, _P]
         L.oracle_sparse_attn_decode.argtypes = [_P, _P, _P, _I32, _P, _I32, _P, _I32, _I32, _P, _P, _I32,
                                                 ctypes.c_float, _I32, _P, _P]
         L.oracle_sparse_attn_prefill_chunk.argtypes = [_P, _P, _P, _I32, _P, _I32, _P, _I32, _I32, _I32, _P,
@@ -183,6 +190,55 @@ def topk_select(scores: np.ndarray, n_visible: np.ndarray, k: int) -> np.ndarray
     n_visible = _arr(n_visible, np.int32)
     out = np.zeros((nq, k), np.int32)
     lib().oracle_topk_select(_ptr(scores), scores.shape[1], _ptr(n_visible), nq, k, _ptr(out))
+    return out
+
+
+POOL_BLOCK = 8
+
+
+def pool_build(scores: np.ndarray, n_visible: np.ndarray, npool: int) -> np.ndarray:
+    """Hierarchical candidate pool from a gatekeeper layer's scores: the npool blocks
+    of 8 entries with the largest member score (ties to the lower block), ascending,
+    -1 padded.  int32 [nq, npool]."""
+    scores = _arr(scores, np.float32)
+    nq, ld = scores.shape
+    n_visible = _arr(n_visible, np.int32)
+    pool = np.zeros((nq, npool), np.int32)
+    lib().oracle_pool_build(_ptr(scores), ld, _ptr(n_visible), nq, npool, _ptr(pool))
+    return pool
+
+
+def index_score_pool(cache: Cache, q_idx: np.ndarray, w: np.ndarray, n_visible: np.ndarray, pool: np.ndarray,
+                     block_table: np.ndarray, seq_of_query: np.ndarray | None = None, page_size: int = PAGE_SIZE):
+    """Scores of the pool's members at pool positions 8r + i (NaN where a position holds
+    no visible entry).  Returns (scores float32 [nq, 8 npool], dots not representable
+    in fp32, dots not exact in double)."""
+    q_idx = _arr(q_idx, np.uint16)
+    nq, Hi, d = q_idx.shape
+    assert d == INDEX_DIM
+    w = _arr(w, np.float32).reshape(nq, Hi)
+    n_visible = _arr(n_visible, np.int32)
+    pool = _arr(pool, np.int32)
+    npool = pool.shape[1]
+    block_table = _arr(block_table, np.int32)
+    scores = np.full((nq, npool * POOL_BLOCK), np.nan, np.float32)
+    soq = None if seq_of_query is None else _arr(seq_of_query, np.int32)
+    inexact = ctypes.c_int64(0)
+    bad = lib().oracle_index_score_pool(_ptr(cache.idx_codes), _ptr(cache.idx_scales), _ptr(q_idx), _ptr(w), Hi,
+                                        _ptr(soq), _ptr(n_visible), _ptr(pool), npool, _ptr(block_table),
+                                        block_table.shape[1], page_size, nq, _ptr(scores), ctypes.byref(inexact))
+    return scores, int(bad), int(inexact.value)
+
+
+def topk_pool(scores_pool: np.ndarray, pool: np.ndarray, n_visible: np.ndarray, k: int) -> np.ndarray:
+    """The k best visible pool members (entry indices, ascending, -1 padded)."""
+    scores_pool = _arr(scores_pool, np.float32)
+    pool = _arr(pool, np.int32)
+    nq, npool = pool.shape
+    assert scores_pool.shape == (nq, npool * POOL_BLOCK)
+    n_visible = _arr(n_visible, np.int32)
+    out = np.zeros((nq, k), np.int32)
+    lib().oracle_topk_pool(_ptr(scores_pool), _ptr(pool), npool, _ptr(n_visible), nq, k, _ptr(out))
     return out
 
 

@@ -222,6 +222,44 @@ static int e2m1_twice(uint8_t c) { return (int)lrint(2.0 * oracle_e2m1_value(c))
  * Returns the number of (query, head, entry) dots that were not exactly
  * representable in fp32; *inexact receives the number whose exact value could not
  * be formed in double (both must be 0 for the result to be unambiguous). */
+/* The score of one entry (slot s) for a query whose MX32 codes / exponents are qc / qu
+ * and whose head weights are wq.  Counts the dots not representable in fp32 and the
+ * block sums not exact in double. */
+static float score_entry(const uint8_t* idx_codes, const uint8_t* idx_scales, int64_t s, const uint8_t* qc,
+                         const uint8_t* qu, const float* wq, int32_t Hi, int64_t* not_fp32, int64_t* not_exact) {
+  const uint8_t* kp = idx_codes + s * 64;
+  float acc = 0.0f;
+  for (int h = 0; h < Hi; ++h) {
+    double D = 0.0;
+    for (int b = 0; b < 4; ++b) {
+      long S = 0;
+      for (int i = 0; i < MX_BLOCK; ++i) {
+        int c = b * MX_BLOCK + i;
+        S += (long)e2m1_twice(qc[h * INDEX_DIM + c]) * e2m1_twice(unpack_nibble(kp, c));
+      }
+      /* value = S/4 * 2^(uq-127) * 2^(uk-127) */
+      double term = ldexp((double)S, (int)qu[h * 4 + b] + (int)idx_scales[s * 4 + b] - 254 - 2);
+      double sum = D + term;
+      double bb = sum - D;
+      if ((D - (sum - bb)) + (term - bb) != 0.0) ++*not_exact;
+      D = sum;
+    }
+    float d = (float)D;
+    if ((double)d != D) ++*not_fp32;
+    float r = d > 0.0f ? d : 0.0f;
+    acc = fmaf(wq[h], r, acc);
+  }
+  return acc;
+}
+
+/* MX32 quantisation of query q's Hi heads: codes [Hi][128], exponents [Hi][4]. */
+static void quant_query(const uint16_t* q_idx, int32_t Hi, int32_t q, uint8_t* qc, uint8_t* qu) {
+  for (int h = 0; h < Hi; ++h)
+    for (int b = 0; b < 4; ++b)
+      qu[h * 4 + b] = quant_mx32_block(q_idx + ((int64_t)q * Hi + h) * INDEX_DIM + b * MX_BLOCK,
+                                       qc + h * INDEX_DIM + b * MX_BLOCK);
+}
+
 int64_t oracle_index_score(const uint8_t* idx_codes, const uint8_t* idx_scales, const uint16_t* q_idx,
                            const float* w, int32_t Hi, const int32_t* seq_of_query,
                            const int32_t* n_visible, const int32_t* block_table, int32_t max_pages,
@@ -231,37 +269,13 @@ int64_t oracle_index_score(const uint8_t* idx_codes, const uint8_t* idx_scales, 
     int32_t row = seq_of_query ? seq_of_query[q] : q;
     uint8_t* qc = (uint8_t*)malloc((size_t)Hi * INDEX_DIM);
     uint8_t* qu = (uint8_t*)malloc((size_t)Hi * 4);
-    for (int h = 0; h < Hi; ++h)
-      for (int b = 0; b < 4; ++b)
-        qu[h * 4 + b] = quant_mx32_block(q_idx + ((int64_t)q * Hi + h) * INDEX_DIM + b * MX_BLOCK,
-                                         qc + h * INDEX_DIM + b * MX_BLOCK);
+    quant_query(q_idx, Hi, q, qc, qu);
     int64_t nv = n_visible[q];
 #pragma omp parallel for schedule(dynamic, 256) reduction(+ : not_fp32, not_exact)
     for (int64_t j = 0; j < nv; ++j) {
       int64_t s = slot_of(block_table, max_pages, page_size, row, j);
-      const uint8_t* kp = idx_codes + s * 64;
-      float acc = 0.0f;
-      for (int h = 0; h < Hi; ++h) {
-        double D = 0.0;
-        for (int b = 0; b < 4; ++b) {
-          long S = 0;
-          for (int i = 0; i < MX_BLOCK; ++i) {
-            int c = b * MX_BLOCK + i;
-            S += (long)e2m1_twice(qc[h * INDEX_DIM + c]) * e2m1_twice(unpack_nibble(kp, c));
-          }
-          /* value = S/4 * 2^(uq-127) * 2^(uk-127) */
-          double term = ldexp((double)S, (int)qu[h * 4 + b] + (int)idx_scales[s * 4 + b] - 254 - 2);
-          double sum = D + term;
-          double bb = sum - D;
-          if ((D - (sum - bb)) + (term - bb) != 0.0) ++not_exact;
-          D = sum;
-        }
-        float d = (float)D;
-        if ((double)d != D) ++not_fp32;
-        float r = d > 0.0f ? d : 0.0f;
-        acc = fmaf(w[(int64_t)q * Hi + h], r, acc);
-      }
-      scores[(int64_t)q * ld + j] = acc;
+      scores[(int64_t)q * ld + j] = score_entry(idx_codes, idx_scales, s, qc, qu, w + (int64_t)q * Hi, Hi,
+                                                &not_fp32, &not_exact);
     }
     free(qc);
     free(qu);
@@ -309,6 +323,94 @@ void oracle_topk_select(const float* scores, int64_t ld, const int32_t* n_visibl
     for (int64_t i = 0; i < m; ++i) out[i] = (int32_t)all[i].j;
     qsort(out, (size_t)m, sizeof(int32_t), by_index);
     for (int64_t i = m; i < k; ++i) out[i] = -1;
+    free(all);
+  }
+}
+
+/* --------------------------------------------------------- candidate pool -- */
+
+/* Hierarchical candidate pool ([VID] memory section: the first decoder layer scans the
+ * whole global cache and assembles a pool of about 16,000 positions organised as 2048
+ * blocks of 8; the layers after it may not search outside the pool).  The rule that
+ * builds the pool is not on the pages; the reading here: blocks of POOL_BLOCK
+ * consecutive entries are ranked by the largest score among their visible members,
+ * ties to the lower block; the npool best form the pool, listed in ascending block
+ * order and -1 padded.  That is the top-K rule applied to the block maxima. */
+#define POOL_BLOCK 8
+void oracle_pool_build(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq, int32_t npool,
+                       int32_t* pool) {
+  int64_t ldb = (ld + POOL_BLOCK - 1) / POOL_BLOCK;
+  float* bmax = (float*)malloc(sizeof(float) * (size_t)(nq > 0 && ldb > 0 ? nq * ldb : 1));
+  int32_t* nb = (int32_t*)malloc(sizeof(int32_t) * (size_t)(nq > 0 ? nq : 1));
+  for (int32_t q = 0; q < nq; ++q) {
+    int64_t n = n_visible[q];
+    nb[q] = (int32_t)((n + POOL_BLOCK - 1) / POOL_BLOCK);
+    for (int64_t b = 0; b < nb[q]; ++b) {
+      float m = scores[(int64_t)q * ld + b * POOL_BLOCK];
+      for (int64_t j = b * POOL_BLOCK + 1; j < (b + 1) * POOL_BLOCK && j < n; ++j)
+        if (scores[(int64_t)q * ld + j] > m) m = scores[(int64_t)q * ld + j];
+      bmax[q * ldb + b] = m;
+    }
+  }
+  oracle_topk_select(bmax, ldb, nb, nq, npool, pool);
+  free(bmax);
+  free(nb);
+}
+
+/* Scores over the pool: the index score (as in oracle_index_score) of every visible
+ * member of the pool's blocks, written at pool position 8r + i for member i of the
+ * pool's r-th block.  Positions of -1 blocks and of members at or past n_visible are
+ * not written. */
+int64_t oracle_index_score_pool(const uint8_t* idx_codes, const uint8_t* idx_scales, const uint16_t* q_idx,
+                                const float* w, int32_t Hi, const int32_t* seq_of_query,
+                                const int32_t* n_visible, const int32_t* pool, int32_t npool,
+                                const int32_t* block_table, int32_t max_pages, int32_t page_size, int32_t nq,
+                                float* scores, int64_t* inexact) {
+  int64_t not_fp32 = 0, not_exact = 0;
+  const int64_t ld = (int64_t)npool * POOL_BLOCK;
+  for (int32_t q = 0; q < nq; ++q) {
+    int32_t row = seq_of_query ? seq_of_query[q] : q;
+    uint8_t* qc = (uint8_t*)malloc((size_t)Hi * INDEX_DIM);
+    uint8_t* qu = (uint8_t*)malloc((size_t)Hi * 4);
+    quant_query(q_idx, Hi, q, qc, qu);
+#pragma omp parallel for schedule(dynamic, 64) reduction(+ : not_fp32, not_exact)
+    for (int64_t p = 0; p < ld; ++p) {
+      int32_t blk = pool[(int64_t)q * npool + p / POOL_BLOCK];
+      int64_t j = (int64_t)blk * POOL_BLOCK + p % POOL_BLOCK;
+      if (blk < 0 || j >= n_visible[q]) continue;
+      int64_t s = slot_of(block_table, max_pages, page_size, row, j);
+      scores[(int64_t)q * ld + p] = score_entry(idx_codes, idx_scales, s, qc, qu, w + (int64_t)q * Hi, Hi,
+                                                &not_fp32, &not_exact);
+    }
+    free(qc);
+    free(qu);
+  }
+  if (inexact) *inexact = not_exact;
+  return not_fp32;
+}
+
+/* Top-K inside the pool: the k best visible pool members by score, ties to the lower
+ * entry, emitted as entry indices in ascending order, -1 padded. */
+void oracle_topk_pool(const float* scores, const int32_t* pool, int32_t npool, const int32_t* n_visible,
+                      int32_t nq, int32_t k, int32_t* topk_idx) {
+  const int64_t ld = (int64_t)npool * POOL_BLOCK;
+  for (int32_t q = 0; q < nq; ++q) {
+    scored* all = (scored*)malloc(sizeof(scored) * (size_t)(ld > 0 ? ld : 1));
+    int64_t m = 0;
+    for (int64_t p = 0; p < ld; ++p) {
+      int32_t blk = pool[(int64_t)q * npool + p / POOL_BLOCK];
+      int64_t j = (int64_t)blk * POOL_BLOCK + p % POOL_BLOCK;
+      if (blk < 0 || j >= n_visible[q]) continue;
+      all[m].s = scores[(int64_t)q * ld + p];
+      all[m].j = j;
+      ++m;
+    }
+    qsort(all, (size_t)m, sizeof(scored), by_score_then_index);
+    int64_t c = m < k ? m : k;
+    int32_t* out = topk_idx + (int64_t)q * k;
+    for (int64_t i = 0; i < c; ++i) out[i] = (int32_t)all[i].j;
+    qsort(out, (size_t)c, sizeof(int32_t), by_index);
+    for (int64_t i = c; i < k; ++i) out[i] = -1;
     free(all);
   }
 }

@@ -2,7 +2,7 @@
 
 Each case plants one mistake in a copy of oracle/oracle.c (a wrong bias or
 exponent, a dropped term, a flipped tie rule, a transposed index, an off-by-one
-window), builds that copy with gcc, and runs the pin suite against it in a fresh
+window), builds that copy with gcc, and runs the pin suites against it in a fresh
 process (CSA2_ORACLE_LIB points the oracle at the copy).  The pin suite must fail.
 Runs on the CPU only; the mistakes never reach the committed oracle.
 """
@@ -32,8 +32,7 @@ MUTATIONS = [
     ("mx32 exponent offset", "u = (e - 1) - 2 + 127;", "u = (e - 1) - 1 + 127;"),
     ("nibble order swapped", "codes[2 * k] | (codes[2 * k + 1] << 4)", "codes[2 * k + 1] | (codes[2 * k] << 4)"),
     ("score without ReLU", "float r = d > 0.0f ? d : 0.0f;", "float r = d;"),
-    ("score heads reversed against weights", "acc = fmaf(w[(int64_t)q * Hi + h], r, acc);",
-     "acc = fmaf(w[(int64_t)q * Hi + (Hi - 1 - h)], r, acc);"),
+    ("score heads reversed against weights", "acc = fmaf(wq[h], r, acc);", "acc = fmaf(wq[Hi - 1 - h], r, acc);"),
     ("score block scale off by 2", "- 254 - 2);", "- 254 - 1);"),
     ("score ignores the block table row", "block_table[(int64_t)row * max_pages + j / page_size]",
      "block_table[j / page_size]"),
@@ -51,6 +50,11 @@ MUTATIONS = [
     ("footprint ignores m", "if (mode[l] == 1) total += per_entry / (double)m[l];",
      "if (mode[l] == 1) total += per_entry;"),
     ("footprint counts reindex layers", "if (mode[l] == 1) total", "if (mode[l] == 1 || mode[l] == 2) total"),
+    ("pool ranks blocks by their smallest member", "if (scores[(int64_t)q * ld + j] > m) m",
+     "if (scores[(int64_t)q * ld + j] < m) m"),
+    ("pool scores one entry past the visible end", "j >= n_visible[q]) continue;\n      int64_t s = slot_of",
+     "j > n_visible[q]) continue;\n      int64_t s = slot_of"),
+    ("pool top-k reports pool positions", "all[m].j = j;", "all[m].j = p;"),
 ]
 
 
@@ -71,7 +75,8 @@ def _build_mutant(tmp, old, new):
 def test_pins_catch_planted_mistake(tmp_path, label, old, new):
     so = _build_mutant(str(tmp_path), old, new)
     env = dict(os.environ, CSA2_ORACLE_LIB=so, OMP_NUM_THREADS="4")
-    r = subprocess.run([sys.executable, "-m", "pytest", os.path.join(HERE, "test_oracle_pins.py"), "-x", "-q",
+    r = subprocess.run([sys.executable, "-m", "pytest", os.path.join(HERE, "test_oracle_pins.py"),
+                        os.path.join(HERE, "test_oracle_pool.py"), "-x", "-q",
                         "-p", "no:cacheprovider", "-m", "not gpu"], cwd=ROOT, env=env, capture_output=True,
                        text=True, timeout=600)
     assert r.returncode == 1, f"mistake '{label}' was not caught by any pin:\n{r.stdout[-1500:]}"

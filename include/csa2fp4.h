@@ -148,6 +148,49 @@ int index_topk(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* 
                int32_t nq, float* scores, int64_t ld, int32_t k, int32_t* topk_idx, void* ws, size_t ws_bytes,
                hipStream_t stream);
 
+/* Hierarchical candidate pool.
+ * Source: "DeepSeek V4.1 Flash et le cerveau divisé", memory section (the first
+ * decoder layer scans the whole global cache and assembles a pool of about 16,000
+ * positions organised as 2048 blocks of 8; the layers after it may not search
+ * outside the pool); "DeepSeek-V4.1-Flash, expliqué pas à pas", CSA2 section (for a
+ * fixed pool the deeper indexers' cost no longer grows with the context).  The rule
+ * that picks the blocks is not on the pages; the one here: blocks of CSA2_POOL_BLOCK
+ * consecutive entries are ranked by the largest score among their visible members,
+ * ties to the lower block.
+ *
+ * index_pool_build -- the pool of each query from a gatekeeper layer's scores.
+ *   scores f32 [nq][ld]  : positions < n_visible[q] are read (e.g. index_topk's scores)
+ *   npool                : blocks kept, 1 <= npool <= 4096 (2048 in the pages)
+ *   pool int32 [nq][npool]: the min(npool, ceil(n_visible/8)) best blocks, ascending,
+ *                          then -1 padding
+ *   ws, ws_bytes          : at least index_pool_build_workspace_size(nq, ld, npool)
+ *                          bytes, with the zero-fill contract of topk_select.
+ * Bit-exact and deterministic. */
+#define CSA2_POOL_BLOCK 8
+size_t index_pool_build_workspace_size(int32_t nq, int64_t ld, int32_t npool);
+int index_pool_build(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq, int32_t npool,
+                     int32_t* pool, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* index_topk_pool -- index_topk restricted to each query's candidate pool: the
+ * indexer stage of a Reindex layer behind a gatekeeper layer.
+ *   pool int32 [nq][npool] : as written by index_pool_build (blocks ascending, -1 last)
+ *   scores_pool f32 [nq][8*npool] out: position 8r + i holds the score (as index_score)
+ *                           of member i of block pool[q][r]; only the positions that
+ *                           hold a visible entry are written (a prefix of the row)
+ *   topk_idx int32 [nq][k] out: the min(k, visible members) members with the largest
+ *                           score, ties to the lower entry, as ENTRY indices in
+ *                           ascending order, then -1 padding
+ *   ws, ws_bytes           : at least index_topk_pool_workspace_size(nq, npool, k)
+ *                           bytes, with the zero-fill contract of topk_select.
+ * Other arguments as for index_topk (block_table rows cover n_visible).  Bit-exact
+ * and deterministic; with a pool that covers every block the result equals
+ * index_topk's. */
+size_t index_topk_pool_workspace_size(int32_t nq, int32_t npool, int32_t k);
+int index_topk_pool(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
+                    const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* pool, int32_t npool,
+                    const int32_t* block_table, int32_t max_pages, int32_t nq, float* scores_pool, int32_t k,
+                    int32_t* topk_idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* sparse_attn_decode -- one softmax over the selected cache entries and the window.
  * Source: "DeepSeek-V4.1-Flash, expliqué pas à pas", CSA2 section (the main query
  * reads the selected entries and the layer's own sliding-window KV; FP4 is only a

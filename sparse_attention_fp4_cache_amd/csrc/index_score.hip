@@ -176,6 +176,47 @@ CSA2_DEV void load_keys(KeyTile& t, const uint8_t* __restrict__ idx_codes, const
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Candidate pools: virtual page G holds pool positions 64G .. 64G+63, the members of
+// pool blocks 8G .. 8G+7 (blocks of 8 consecutive entries; a block never crosses a
+// 64-entry page).  Slot of position e of virtual page G; past the pool's end, or at a
+// -1 block, it is a valid stand-in slot whose score is never written.
+constexpr int kPoolBlock = 8;
+CSA2_DEV int64_t pool_slot(const int32_t* __restrict__ pool_row, int npool, const int32_t* __restrict__ bt_seq,
+                           int G, int e) {
+  const int r = min(8 * G + (e >> 3), npool - 1);
+  const int blk = max(pool_row[r], 0);
+  const int64_t j = (int64_t)blk * kPoolBlock + (e & 7);
+  return (int64_t)bt_seq[j >> 6] * kPage + (j & 63);
+}
+
+// One virtual page of a pool: the same operand layout as load_keys, gathered per lane.
+CSA2_DEV void load_keys_pool(KeyTile& t, const uint8_t* __restrict__ idx_codes,
+                             const uint8_t* __restrict__ idx_scales, const int32_t* __restrict__ pool_row,
+                             int npool, const int32_t* __restrict__ bt_seq, int G, int lane) {
+  const uint32_t g = (uint32_t)lane >> 4, n = (uint32_t)lane & 15u;
+  int64_t sl[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) sl[nt] = pool_slot(pool_row, npool, bt_seq, G, 16 * nt + (int)n);
+  const int64_t so = pool_slot(pool_row, npool, bt_seq, G, lane);
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    t.codes[nt] = *reinterpret_cast<const uint4*>(idx_codes + sl[nt] * kIdxRowBytes + 16u * g);
+    t.sc[nt] = idx_scales[sl[nt] * kIdxScaleBytes + g];
+  }
+  t.own = *reinterpret_cast<const uint32_t*>(idx_scales + so * kIdxScaleBytes);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Pool positions that hold a visible entry: a prefix of the row (its blocks are in
+// ascending order, so only the last valid one can be the sequence's partial block).
+CSA2_DEV int pool_visible(const int32_t* __restrict__ pool_row, int npool, int n_visible) {
+  const int nb = (n_visible + kPoolBlock - 1) / kPoolBlock;
+  const int nvalid = min(npool, nb);
+  if (nvalid == 0) return 0;
+  const int tail = n_visible % kPoolBlock;
+  return (pool_row[nvalid - 1] == nb - 1 && tail != 0) ? kPoolBlock * (nvalid - 1) + tail : kPoolBlock * nvalid;
+}
+
 // Scores of one page for one query of the tile: 64 entries starting at logical entry
 // G * 64 of the query's sequence, whose keys are in `cur` (physical first slot slot0).
 // Returns whether this lane's entry lies outside the window where the MFMA result is
@@ -265,7 +306,10 @@ CSA2_DEV float exact_entry(const QStage<MT>& s, const uint8_t* __restrict__ idx_
 // HIST (one query per workgroup only): also fill the query's digit-1 histogram
 // (copy blockIdx.x % ncopies of hist[q]) of the selection that follows, when
 // n_visible[q] > k.
-template <int MT, int QT, bool HIST>
+// POOL: the row of each query is its candidate pool (pool [nq][npool] blocks of 8
+// entries, ld = 8 npool); position p scores member p % 8 of block pool[q][p / 8], and
+// workgroup 0 of each query writes the count of visible positions to pool_nvis[q].
+template <int MT, int QT, bool HIST, bool POOL = false>
 __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __restrict__ idx_codes,
                                                           const uint8_t* __restrict__ idx_scales,
                                                           const uint16_t* __restrict__ q_idx,
@@ -275,8 +319,11 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
                                                           const int32_t* __restrict__ block_table, int max_pages,
                                                           int nq, float* __restrict__ scores, int64_t ld,
                                                           int groups_per_wave, int total_groups,
-                                                          uint32_t* __restrict__ hist, int k, int ncopies) {
+                                                          uint32_t* __restrict__ hist, int k, int ncopies,
+                                                          const int32_t* __restrict__ pool, int npool,
+                                                          int32_t* __restrict__ pool_nvis) {
   static_assert(!HIST || QT == 1, "the fused histogram serves one query per workgroup");
+  static_assert(!POOL || QT == 1, "candidate pools are scanned one query per workgroup");
   constexpr int qt = QT;  // queries per workgroup
   constexpr int HI = 16 * MT;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -304,6 +351,10 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
   if (tid < qt && q0 + tid < nq) {
     my_row = seq_of_query ? seq_of_query[q0 + tid] : q0 + tid;
     my_nvis = n_visible[q0 + tid];
+    if (POOL) {
+      my_nvis = pool_visible(pool + (int64_t)(q0 + tid) * npool, npool, my_nvis);
+      if (blockIdx.x == 0) pool_nvis[q0 + tid] = my_nvis;
+    }
   }
   QRaw qraw;  // the first round of staging loads goes out before the key loads
   {
@@ -324,13 +375,24 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
   // the four page numbers are read now.  Wavefronts that stage query blocks request
   // their pages after the staging, so the staging's query loads do not queue behind
   // the key burst; the others request theirs at once.
-  const int pg0 = page_of(0), pg1 = page_of(1), pg2 = page_of(2), pg3 = page_of(3);
+  const int pg0 = POOL ? 0 : page_of(0), pg1 = POOL ? 0 : page_of(1), pg2 = POOL ? 0 : page_of(2),
+            pg3 = POOL ? 0 : page_of(3);
   const bool stager = wid * 64 < items;  // uniform
+  const int32_t* __restrict__ pool_row = POOL ? pool + (int64_t)q0 * npool : nullptr;
+  const int32_t* __restrict__ bt_seq = block_table + (int64_t)first_row * max_pages;
+  auto vpage = [&](int k) { return gfirst + min(k, npg_all - 1); };  // pools: virtual page of the k-th
   auto request_pages = [&]() {
-    load_keys(t0, idx_codes, idx_scales, pg0, lane);
-    load_keys(t1, idx_codes, idx_scales, pg1, lane);
-    load_keys(t2, idx_codes, idx_scales, pg2, lane);
-    load_keys(t3, idx_codes, idx_scales, pg3, lane);
+    if (POOL) {
+      load_keys_pool(t0, idx_codes, idx_scales, pool_row, npool, bt_seq, vpage(0), lane);
+      load_keys_pool(t1, idx_codes, idx_scales, pool_row, npool, bt_seq, vpage(1), lane);
+      load_keys_pool(t2, idx_codes, idx_scales, pool_row, npool, bt_seq, vpage(2), lane);
+      load_keys_pool(t3, idx_codes, idx_scales, pool_row, npool, bt_seq, vpage(3), lane);
+    } else {
+      load_keys(t0, idx_codes, idx_scales, pg0, lane);
+      load_keys(t1, idx_codes, idx_scales, pg1, lane);
+      load_keys(t2, idx_codes, idx_scales, pg2, lane);
+      load_keys(t3, idx_codes, idx_scales, pg3, lane);
+    }
   };
   if (!stager) request_pages();
 
@@ -411,8 +473,9 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
       const int b = __builtin_ctzll(exact_bits);
       exact_bits &= exact_bits - 1;
       const int i = b / qt, qi = b % qt;
-      const float e = exact_entry<MT>(st[qi], idx_codes, idx_scales, (int64_t)page_of(i) * kPage + lane,
-                                      w + (int64_t)(q0 + qi) * HI,
+      const int64_t slot = POOL ? pool_slot(pool_row, npool, bt_seq, gfirst + i, lane)
+                                : (int64_t)page_of(i) * kPage + lane;
+      const float e = exact_entry<MT>(st[qi], idx_codes, idx_scales, slot, w + (int64_t)(q0 + qi) * HI,
                                       scores + (int64_t)(q0 + qi) * ld + (int64_t)(gfirst + i) * kPage + lane);
       if (HIST && hist_on) atomicAdd(&lh[score_key(e) >> kTopkBinShift], 1u);
     }
@@ -842,16 +905,24 @@ static int query_tile(const int32_t* soq, int32_t nq, size_t stage_bytes) {
   return (soq == nullptr || nq < 64) ? 1 : (stage_bytes * 8 <= 64 * 1024 ? 8 : 4);
 }
 
+// Pool scans (pool != nullptr) take one query per workgroup over virtual pages of
+// the pool (ld = 8 npool).
+struct PoolArgs {
+  const int32_t* pool = nullptr;
+  int npool = 0;
+  int32_t* nvis = nullptr;  // [nq] out: visible pool positions
+};
+
 template <int MT>
 static int launch_mt(const csa2_fp4_cache* c, const uint16_t* q_idx, const float* w, const int32_t* soq,
                      const int32_t* nvis, const int32_t* bt, int32_t max_pages, int32_t nq, float* scores, int64_t ld,
-                     uint32_t* hist, int k, int* copies, hipStream_t stream) {
+                     uint32_t* hist, int k, int* copies, const PoolArgs& pa, hipStream_t stream) {
   const int total_groups = (int)ceil_div(ld, kPage);
   if (total_groups == 0 || nq == 0) return CSA2_OK;
   // queries per workgroup: several queries of one sequence share each loaded page
   // (queries without a sequence map each read their own pages); the staged queries
   // stay within 64 KB of LDS
-  const int qt = query_tile(soq, nq, sizeof(QStage<MT>));
+  const int qt = pa.pool ? 1 : query_tile(soq, nq, sizeof(QStage<MT>));
   // pages per wavefront: enough wavefronts to cover the chip about twice
   const long long qtiles = ceil_div(nq, qt);
   const long long want_waves = qtiles >= 512 ? 4 * qtiles : 2048;
@@ -863,19 +934,31 @@ static int launch_mt(const csa2_fp4_cache* c, const uint16_t* q_idx, const float
   const size_t lds = sizeof(QStage<MT>) * qt;
   const int ncopies = topk_hist_copies(gx);
   if (copies != nullptr) *copies = ncopies;
-  if (hist != nullptr) {  // one query per workgroup (the caller checked)
+  if (pa.pool != nullptr) {
+    if (hist != nullptr)
+      hipLaunchKernelGGL((index_score_kernel<MT, 1, true, true>), grid, block, lds + kTopkBins * sizeof(uint32_t),
+                         stream, c->idx_codes, c->idx_scales, q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw,
+                         total_groups, hist, k, ncopies, pa.pool, pa.npool, pa.nvis);
+    else
+      hipLaunchKernelGGL((index_score_kernel<MT, 1, false, true>), grid, block, lds, stream, c->idx_codes,
+                         c->idx_scales, q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist,
+                         k, ncopies, pa.pool, pa.npool, pa.nvis);
+  } else if (hist != nullptr) {  // one query per workgroup (the caller checked)
     hipLaunchKernelGGL((index_score_kernel<MT, 1, true>), grid, block, lds + kTopkBins * sizeof(uint32_t), stream,
                        c->idx_codes, c->idx_scales, q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw,
-                       total_groups, hist, k, ncopies);
+                       total_groups, hist, k, ncopies, nullptr, 0, nullptr);
   } else if (qt == 8) {
     hipLaunchKernelGGL((index_score_kernel<MT, 8, false>), grid, block, lds, stream, c->idx_codes, c->idx_scales,
-                       q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k, ncopies);
+                       q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k, ncopies,
+                       nullptr, 0, nullptr);
   } else if (qt == 4) {
     hipLaunchKernelGGL((index_score_kernel<MT, 4, false>), grid, block, lds, stream, c->idx_codes, c->idx_scales,
-                       q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k, ncopies);
+                       q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k, ncopies,
+                       nullptr, 0, nullptr);
   } else {
     hipLaunchKernelGGL((index_score_kernel<MT, 1, false>), grid, block, lds, stream, c->idx_codes, c->idx_scales,
-                       q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k, ncopies);
+                       q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k, ncopies,
+                       nullptr, 0, nullptr);
   }
   return launch_status();
 }
@@ -900,10 +983,11 @@ static int launch_q2(const csa2_fp4_cache* c, const uint16_t* q_idx, const float
 static int launch_hi(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
                      const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* block_table,
                      int32_t max_pages, int32_t nq, float* scores, int64_t ld, uint32_t* hist, int k,
-                     int* copies, hipStream_t stream) {
+                     int* copies, hipStream_t stream, const PoolArgs& pa = PoolArgs()) {
   // queries that share sequences, at most 64 heads: two queries per wavefront (two
   // score rows within one buffer resource's 2^31-byte range)
-  if (hist == nullptr && query_tile(seq_of_query, nq, 0) > 1 && Hi <= 64 && ld < ((int64_t)1 << 28)) {
+  if (pa.pool == nullptr && hist == nullptr && query_tile(seq_of_query, nq, 0) > 1 && Hi <= 64 &&
+      ld < ((int64_t)1 << 28)) {
     if (copies != nullptr) *copies = 1;
     switch (Hi / 16) {
       case 1: return launch_q2<1>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, stream);
@@ -916,7 +1000,7 @@ static int launch_hi(const csa2_fp4_cache* cache, const uint16_t* q_idx, const f
 #define CSA2_MT(m) \
   case m:          \
     return launch_mt<m>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, hist, k, \
-                        copies, stream);
+                        copies, pa, stream);
     CSA2_MT(1)
     CSA2_MT(2)
     CSA2_MT(3)
@@ -925,7 +1009,7 @@ static int launch_hi(const csa2_fp4_cache* cache, const uint16_t* q_idx, const f
     CSA2_MT(6)
     CSA2_MT(7)
     default: return launch_mt<8>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld,
-                                 hist, k, copies, stream);
+                                 hist, k, copies, pa, stream);
 #undef CSA2_MT
   }
 }
@@ -975,5 +1059,40 @@ extern "C" int index_topk(const csa2_fp4_cache* cache, const uint16_t* q_idx, co
                    &copies, stream);
     if (st != CSA2_OK) return st;
   }
-  return topk_enqueue(scores, ld, n_visible, nq, k, topk_idx, ws, stream, fuse, copies);
+  return topk_enqueue(scores, ld, n_visible, nq, k, topk_idx, ws, stream, fuse, copies, nullptr, 0);
+}
+
+// the pool workspace: visible pool positions per query, then the selection's workspace
+static size_t pool_nvis_bytes(int32_t nq) { return ((size_t)nq * sizeof(int32_t) + 255) & ~(size_t)255; }
+
+extern "C" size_t index_topk_pool_workspace_size(int32_t nq, int32_t npool, int32_t k) {
+  if (nq <= 0 || npool < 1) return 0;
+  return pool_nvis_bytes(nq) + topk_select_workspace_size(nq, (int64_t)npool * kPoolBlock, k);
+}
+
+extern "C" int index_topk_pool(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
+                               const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* pool,
+                               int32_t npool, const int32_t* block_table, int32_t max_pages, int32_t nq,
+                               float* scores_pool, int32_t k, int32_t* topk_idx, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  if (!cache_ok(cache)) return CSA2_ERR_NULL;
+  if (!cache_shape_ok(cache) || nq < 0 || max_pages < 1) return CSA2_ERR_SHAPE;
+  if (Hi < 16 || Hi > 128 || Hi % 16 != 0) return CSA2_ERR_SHAPE;
+  if (npool < 1 || npool > CSA2_MAX_K || k < 1 || k > CSA2_MAX_K) return CSA2_ERR_SHAPE;
+  if (nq == 0) return CSA2_OK;
+  if (!q_idx || !w || !n_visible || !pool || !block_table || !scores_pool || !topk_idx) return CSA2_ERR_NULL;
+  if (!ws || ws_bytes < index_topk_pool_workspace_size(nq, npool, k)) return CSA2_ERR_WORKSPACE;
+  const int64_t ld = (int64_t)npool * kPoolBlock;
+  int32_t* pool_nvis = reinterpret_cast<int32_t*>(ws);
+  void* ws_topk = reinterpret_cast<char*>(ws) + pool_nvis_bytes(nq);
+  PoolArgs pa;
+  pa.pool = pool;
+  pa.npool = npool;
+  pa.nvis = pool_nvis;
+  int copies = 1;
+  // one query per workgroup: the selection's first counting pass runs inside the scan
+  const int st = launch_hi(cache, q_idx, w, Hi, seq_of_query, n_visible, block_table, max_pages, nq, scores_pool,
+                           ld, topk_digit1_hist(ws_topk, nq, ld), k, &copies, stream, pa);
+  if (st != CSA2_OK) return st;
+  return topk_enqueue(scores_pool, ld, pool_nvis, nq, k, topk_idx, ws_topk, stream, true, copies, pool, npool);
 }

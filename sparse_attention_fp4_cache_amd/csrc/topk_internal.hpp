@@ -22,8 +22,11 @@ uint32_t* topk_digit1_hist(void* ws, int32_t nq, int64_t ld);
 
 // Enqueue the selection; with hist_done the digit-1 histograms are already filled
 // (by the scoring pass, in `copies` copies) and the counting launch is skipped.
+// With pool (int32 [nq][npool] blocks of 8 entries), the rows are candidate-pool
+// scores and the output holds the entries at the selected pool positions.
 // Arguments were validated by the caller.
 int topk_enqueue(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq, int32_t k,
-                 int32_t* topk_idx, void* ws, hipStream_t stream, bool hist_done, int copies);
+                 int32_t* topk_idx, void* ws, hipStream_t stream, bool hist_done, int copies, const int32_t* pool,
+                 int npool);
 
 }  // namespace csa2

@@ -33,6 +33,8 @@
 #include "host_common.hpp"
 #include "topk_internal.hpp"
 
+#include <algorithm>
+
 namespace csa2 {
 
 constexpr int kBins = kTopkBins;  // 12-bit digits
@@ -319,8 +321,9 @@ CSA2_DEV unsigned long long small_boundary(const Src& src, unsigned long long pr
 // wavefront owns a contiguous segment of the list (at most 16 x 64 entries, read
 // into registers at once), counts its kept entries with ballots, and after one
 // exchange of the counts writes them at their positions.
+CSA2_DEV int32_t out_index(const int32_t* __restrict__ pool_row, int64_t i);
 CSA2_DEV void compact_list(const unsigned long long* list, int total, unsigned long long boundary, int k,
-                           int32_t* __restrict__ out, uint32_t* wsum) {
+                           int32_t* __restrict__ out, uint32_t* wsum, const int32_t* __restrict__ pool_row) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int per_w = (((total + kWaves - 1) / kWaves) + 63) & ~63;
   const int s0 = wid * per_w, s1 = min(s0 + per_w, total);
@@ -336,24 +339,33 @@ CSA2_DEV void compact_list(const unsigned long long* list, int total, unsigned l
     const bool keep = x >= boundary;
     const unsigned long long m = __builtin_amdgcn_ballot_w64(keep);
     const uint32_t o = pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-    if (keep && o < (uint32_t)k) out[o] = (int32_t)index_of(x);
+    if (keep && o < (uint32_t)k) out[o] = out_index(pool_row, index_of(x));
     pos += (uint32_t)__popcll(m);
   }
   lds_barrier();  // wsum is reused by the caller
+}
+
+// Selected position i of a row -> the index written out: i itself, or, when the row
+// is a candidate pool (blocks of 8 entries listed in pool_row), the entry at pool
+// position i.
+CSA2_DEV int32_t out_index(const int32_t* __restrict__ pool_row, int64_t i) {
+  return pool_row ? 8 * pool_row[i >> 3] + (int32_t)(i & 7) : (int32_t)i;
 }
 
 // ---------------------------------------------------------------- kernel 2 --
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __restrict__ scores, int64_t ld,
                                                                const int32_t* __restrict__ n_visible, int k,
                                                                int32_t* __restrict__ topk_idx, TopkWs ws,
-                                                               int nchunk, int ncopies) {
+                                                               int nchunk, int ncopies,
+                                                               const int32_t* __restrict__ pool, int npool) {
   __shared__ SelectSmem sm;
   const int q = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t n = n_visible[q];
   const int64_t base = (int64_t)blockIdx.x * kChunk;
   int32_t* out = topk_idx + (int64_t)q * k;
+  const int32_t* pool_row = pool ? pool + (int64_t)q * npool : nullptr;
   if (n <= k) {  // everything visible is selected, then -1 padding
-    for (int64_t i = base + tid; i < min(base + (int64_t)kChunk, n); i += kThreads) out[i] = (int32_t)i;
+    for (int64_t i = base + tid; i < min(base + (int64_t)kChunk, n); i += kThreads) out[i] = out_index(pool_row, i);
     if (blockIdx.x == 0)
       for (int64_t i = n + tid; i < k; i += kThreads) out[i] = -1;
     return;
@@ -493,7 +505,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
       const LdsCands src{sm.list, (int)total};
       boundary = select_boundary(src, need2, prefix, 40, d2.cnt, sm);
     }
-    compact_list(sm.list, (int)total, boundary, k, out, sm.wsum[0]);
+    compact_list(sm.list, (int)total, boundary, k, out, sm.wsum[0], pool_row);
   } else {
     // slow path (a region overflowed, or very long rows): boundary from the score
     // row, then an ordered scan of the row, kThreads entries per round
@@ -512,7 +524,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
       uint32_t t2;
       const uint32_t incl = block_inclusive_scan(keep ? 1u : 0u, sm.wsum[parity], &t2);
       parity ^= 1;
-      if (keep && written + incl - 1 < (uint32_t)k) out[written + incl - 1] = (int32_t)i;
+      if (keep && written + incl - 1 < (uint32_t)k) out[written + incl - 1] = out_index(pool_row, i);
       written += t2;
     }
   }
@@ -566,13 +578,14 @@ struct RowLists {
 __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restrict__ scores, int64_t ld,
                                                             const int32_t* __restrict__ n_visible, int k,
                                                             int32_t* __restrict__ topk_idx, uint32_t* __restrict__ hist,
-                                                            int ncopies) {
+                                                            int ncopies, const int32_t* __restrict__ pool, int npool) {
   __shared__ RowSmem sm;
   const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t n = n_visible[q];
   int32_t* out = topk_idx + (int64_t)q * k;
+  const int32_t* pool_row = pool ? pool + (int64_t)q * npool : nullptr;
   if (n <= k) {  // everything visible is selected, then -1 padding
-    for (int i = tid; i < k; i += kThreads) out[i] = i < n ? i : -1;
+    for (int i = tid; i < k; i += kThreads) out[i] = i < n ? out_index(pool_row, i) : -1;
     return;
   }
   const float* row = scores + (int64_t)q * ld;
@@ -725,7 +738,7 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
       const bool kp = x >= boundary;
       const unsigned long long m = __builtin_amdgcn_ballot_w64(kp);
       const uint32_t o = pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      if (kp && o < (uint32_t)k) out[o] = (int32_t)index_of(x);
+      if (kp && o < (uint32_t)k) out[o] = out_index(pool_row, index_of(x));
       pos += (uint32_t)__popcll(m);
     }
   } else {
@@ -746,7 +759,7 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
       uint32_t t2;
       const uint32_t incl = block_inclusive_scan(kp ? 1u : 0u, sm.wsum[parity], &t2);
       parity ^= 1;
-      if (kp && written + incl - 1 < (uint32_t)k) out[written + incl - 1] = (int32_t)i;
+      if (kp && written + incl - 1 < (uint32_t)k) out[written + incl - 1] = out_index(pool_row, i);
       written += t2;
     }
   }
@@ -771,7 +784,8 @@ uint32_t* topk_digit1_hist(void* ws, int32_t nq, int64_t ld) {
 }
 
 int topk_enqueue(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq, int32_t k,
-                 int32_t* topk_idx, void* ws, hipStream_t stream, bool hist_done, int copies) {
+                 int32_t* topk_idx, void* ws, hipStream_t stream, bool hist_done, int copies, const int32_t* pool,
+                 int npool) {
   const long long nchunk = ld > 0 ? (ld + kChunk - 1) / kChunk : 1;
   const long long kchunk = (k + kChunk - 1) / kChunk;  // the n <= k path writes k outputs
   const long long grid_x = nchunk > kchunk ? nchunk : kchunk;
@@ -782,15 +796,75 @@ int topk_enqueue(const float* scores, int64_t ld, const int32_t* n_visible, int3
     hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kThreads), 0, stream, scores, ld, n_visible, k, w, ncopies);
   if (nq >= kRowSelectQueries) {  // many rows: one workgroup per row, counting its own row
     hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)nq), dim3(kThreads), 0, stream, scores, ld, n_visible, k,
-                       topk_idx, w.hist, hist_done ? ncopies : 0);
+                       topk_idx, w.hist, hist_done ? ncopies : 0, pool, npool);
     return launch_status();
   }
   hipLaunchKernelGGL(topk_select_kernel, grid, dim3(kThreads), 0, stream, scores, ld, n_visible, k, topk_idx, w,
-                     (int)nchunk, ncopies);
+                     (int)nchunk, ncopies, pool, npool);
   return launch_status();
 }
 
 }  // namespace csa2
+
+namespace csa2 {
+
+// ---- candidate pool: block maxima, then the top npool blocks -------------------
+// Thread b of row q: the largest of the visible members of block b (8 entries), the
+// first member kept on ties, and the row's count of blocks with a visible member.
+constexpr int kBmaxThreads = 256;
+__global__ __launch_bounds__(kBmaxThreads) void pool_bmax_kernel(const float* __restrict__ scores, int64_t ld,
+                                                                 const int32_t* __restrict__ n_visible,
+                                                                 float* __restrict__ bmax, int64_t ldb,
+                                                                 int32_t* __restrict__ nblocks) {
+  const int q = blockIdx.y;
+  const int64_t n = n_visible[q], nb = (n + 7) / 8;
+  if (blockIdx.x == 0 && threadIdx.x == 0) nblocks[q] = (int32_t)nb;
+  const int64_t b = (int64_t)blockIdx.x * kBmaxThreads + threadIdx.x;
+  if (b >= nb) return;
+  const float* r = scores + (int64_t)q * ld + 8 * b;
+  float v[8];
+  if (8 * b + 8 <= n && (reinterpret_cast<uintptr_t>(r) & 15u) == 0) {
+    const float4 a = reinterpret_cast<const float4*>(r)[0], c = reinterpret_cast<const float4*>(r)[1];
+    v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = c.x, v[5] = c.y, v[6] = c.z, v[7] = c.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 8 * b + i < n ? r[i] : -INFINITY;
+  }
+  float m = v[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i)
+    if (v[i] > m) m = v[i];
+  bmax[(int64_t)q * ldb + b] = m;
+}
+
+static int64_t pool_ldb(int64_t ld) { return (ld + 7) / 8; }
+
+}  // namespace csa2
+
+extern "C" size_t index_pool_build_workspace_size(int32_t nq, int64_t ld, int32_t npool) {
+  if (nq <= 0 || ld < 0 || npool < 1) return 0;
+  const int64_t ldb = pool_ldb(ld);
+  return align_up((size_t)nq * (size_t)ldb * sizeof(float)) + align_up((size_t)nq * sizeof(int32_t)) +
+         topk_select_workspace_size(nq, ldb, npool);
+}
+
+extern "C" int index_pool_build(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq,
+                                int32_t npool, int32_t* pool, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (nq < 0 || ld < 0 || npool < 1 || npool > CSA2_MAX_K) return CSA2_ERR_SHAPE;
+  if (ld >= ((int64_t)1 << 31)) return CSA2_ERR_SHAPE;
+  if (nq == 0) return CSA2_OK;
+  if (!n_visible || !pool || (ld > 0 && !scores)) return CSA2_ERR_NULL;
+  if (!ws || ws_bytes < index_pool_build_workspace_size(nq, ld, npool)) return CSA2_ERR_WORKSPACE;
+  const int64_t ldb = pool_ldb(ld);
+  float* bmax = reinterpret_cast<float*>(ws);
+  int32_t* nb = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) +
+                                           align_up((size_t)nq * (size_t)ldb * sizeof(float)));
+  void* ws_topk = reinterpret_cast<char*>(nb) + align_up((size_t)nq * sizeof(int32_t));
+  const dim3 grid((unsigned)std::max<int64_t>(1, (ldb + kBmaxThreads - 1) / kBmaxThreads), (unsigned)nq);
+  hipLaunchKernelGGL(pool_bmax_kernel, grid, dim3(kBmaxThreads), 0, stream, scores, ld, n_visible, bmax, ldb, nb);
+  if (launch_status() != CSA2_OK) return CSA2_ERR_LAUNCH;
+  return topk_enqueue(bmax, ldb, nb, nq, npool, pool, ws_topk, stream, false, 1, nullptr, 0);
+}
 
 extern "C" int topk_select(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq, int32_t k,
                            int32_t* topk_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -799,5 +873,5 @@ extern "C" int topk_select(const float* scores, int64_t ld, const int32_t* n_vis
   if (nq == 0) return CSA2_OK;
   if (!n_visible || !topk_idx || (ld > 0 && !scores)) return CSA2_ERR_NULL;
   if (!ws || ws_bytes < topk_select_workspace_size(nq, ld, k)) return CSA2_ERR_WORKSPACE;
-  return topk_enqueue(scores, ld, n_visible, nq, k, topk_idx, ws, stream, false, 1);
+  return topk_enqueue(scores, ld, n_visible, nq, k, topk_idx, ws, stream, false, 1, nullptr, 0);
 }

@@ -29,6 +29,10 @@ EXPORTS = (
     "topk_select_workspace_size",
     "topk_select",
     "index_topk",
+    "index_pool_build_workspace_size",
+    "index_pool_build",
+    "index_topk_pool_workspace_size",
+    "index_topk_pool",
     "sparse_attn_decode_workspace_size",
     "sparse_attn_decode",
     "sparse_attn_prefill_chunk_workspace_size",
@@ -76,6 +80,13 @@ def load() -> ctypes.CDLL:
         L.topk_select.argtypes = [_P, _I64, _P, _I32, _I32, _P, _P, _SZ, _P]
         L.index_topk.argtypes = [ctypes.POINTER(_CacheStruct), _P, _P, _I32, _P, _P, _P, _I32, _I32, _P, _I64, _I32,
                                  _P, _P, _SZ, _P]
+        L.index_pool_build_workspace_size.argtypes = [_I32, _I64, _I32]
+        L.index_pool_build_workspace_size.restype = _SZ
+        L.index_pool_build.argtypes = [_P, _I64, _P, _I32, _I32, _P, _P, _SZ, _P]
+        L.index_topk_pool_workspace_size.argtypes = [_I32, _I32, _I32]
+        L.index_topk_pool_workspace_size.restype = _SZ
+        L.index_topk_pool.argtypes = [ctypes.POINTER(_CacheStruct), _P, _P, _I32, _P, _P, _P, _I32, _P, _I32, _I32,
+                                      _P, _I32, _P, _P, _SZ, _P]
         L.sparse_attn_decode_workspace_size.argtypes = [_I32, _I32, _I32, _I32]
         L.sparse_attn_decode_workspace_size.restype = _SZ
         L.sparse_attn_decode.argtypes = [ctypes.POINTER(_CacheStruct), _P, _I32, _P, _I32, _P, _I32, _P, _P, _I32,
@@ -213,6 +224,49 @@ def index_topk(cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, n_visible: to
                                            _ptr(scores, torch.float32, "scores"), scores.shape[1], k,
                                            _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(ws, torch.uint8, "ws"),
                                            ws.numel(), _stream(stream)))
+
+
+POOL_BLOCK = 8  # entries per candidate-pool block
+
+
+def index_pool_build_workspace_size(nq: int, ld: int, npool: int) -> int:
+    return int(load().index_pool_build_workspace_size(nq, ld, npool))
+
+
+def index_pool_build(scores: torch.Tensor, n_visible: torch.Tensor, npool: int, pool: torch.Tensor,
+                     ws: torch.Tensor, stream=None):
+    """The candidate pool of each query from a gatekeeper layer's scores: the npool
+    blocks of 8 entries with the largest member score, ascending, -1 padded."""
+    nq, ld = scores.shape
+    if pool.shape != (nq, npool) or n_visible.shape != (nq,):
+        raise ValueError("pool must be [nq, npool] and n_visible [nq]")
+    _check("index_pool_build", load().index_pool_build(_ptr(scores, torch.float32, "scores"), ld,
+                                                       _ptr(n_visible, torch.int32, "n_visible"), nq, npool,
+                                                       _ptr(pool, torch.int32, "pool"), _ptr(ws, torch.uint8, "ws"),
+                                                       ws.numel(), _stream(stream)))
+
+
+def index_topk_pool_workspace_size(nq: int, npool: int, k: int) -> int:
+    return int(load().index_topk_pool_workspace_size(nq, npool, k))
+
+
+def index_topk_pool(cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, n_visible: torch.Tensor, pool: torch.Tensor,
+                    block_table: torch.Tensor, scores_pool: torch.Tensor, k: int, topk_idx: torch.Tensor,
+                    ws: torch.Tensor, seq_of_query: torch.Tensor | None = None, stream=None):
+    """index_topk restricted to each query's candidate pool; topk_idx holds entries."""
+    nq, Hi, d = q_idx.shape
+    npool = pool.shape[1]
+    if d != INDEX_DIM or w.shape != (nq, Hi) or n_visible.shape != (nq,) or pool.shape[0] != nq \
+            or scores_pool.shape != (nq, npool * POOL_BLOCK):
+        raise ValueError("shape mismatch in index_topk_pool arguments")
+    if topk_idx.shape != (nq, k):
+        raise ValueError("topk_idx must be [nq, k]")
+    _check("index_topk_pool", load().index_topk_pool(
+        cache.struct, _bits16(q_idx, "q_idx"), _ptr(w, torch.float32, "w"), Hi,
+        _ptr(seq_of_query, torch.int32, "seq_of_query"), _ptr(n_visible, torch.int32, "n_visible"),
+        _ptr(pool, torch.int32, "pool"), npool, _ptr(block_table, torch.int32, "block_table"), block_table.shape[1],
+        nq, _ptr(scores_pool, torch.float32, "scores_pool"), k, _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
 
 
 def sparse_attn_decode_workspace_size(B: int, H: int, k: int, window: int) -> int:

@@ -98,6 +98,42 @@ def test_topk_validation(L):
     assert L.topk_select_workspace_size(4, 10000, 64) > ws
 
 
+def test_pool_build_validation(L):
+    ws = L.index_pool_build_workspace_size(2, 10000, 2048)
+    assert ws > 0
+    assert L.index_pool_build_workspace_size(4, 10000, 2048) > ws
+    call = lambda sc=FAKE, ld=10000, nv=FAKE, nq=2, npool=2048, pool=FAKE, w=FAKE, wb=ws: L.index_pool_build(
+        sc, ld, nv, nq, npool, pool, w, wb, None)
+    assert call(npool=0) == -2
+    assert call(npool=4097) == -2
+    assert call(nq=-1) == -2
+    assert call(pool=None) == -1
+    assert call(nv=None) == -1
+    assert call(w=None) == -4
+    assert call(wb=ws - 1) == -4
+    assert call(nq=0) == 0
+
+
+def test_index_topk_pool_validation(L):
+    ws = L.index_topk_pool_workspace_size(1, 2048, 256)
+    assert ws > 0
+    args = lambda **kw: dict(dict(cache=_cache(), q=FAKE, w=FAKE, Hi=64, soq=None, nv=FAKE, pool=FAKE, npool=2048,
+                                  bt=FAKE, mp=64, nq=1, sc=FAKE, k=256, idx=FAKE, ws=FAKE, wsb=ws), **kw)
+    call = lambda a: L.index_topk_pool(a["cache"], a["q"], a["w"], a["Hi"], a["soq"], a["nv"], a["pool"], a["npool"],
+                                       a["bt"], a["mp"], a["nq"], a["sc"], a["k"], a["idx"], a["ws"], a["wsb"], None)
+    assert call(args(cache=_cache(null=True))) == -1
+    assert call(args(Hi=40)) == -2
+    assert call(args(npool=0)) == -2
+    assert call(args(npool=4097)) == -2
+    assert call(args(k=0)) == -2
+    assert call(args(mp=0)) == -2
+    assert call(args(pool=None)) == -1
+    assert call(args(idx=None)) == -1
+    assert call(args(ws=None)) == -4
+    assert call(args(wsb=ws - 1)) == -4
+    assert call(args(nq=0)) == 0
+
+
 def test_index_topk_validation(L):
     ws = L.topk_select_workspace_size(1, 4096, 64)
     args = lambda **kw: dict(dict(cache=_cache(), q=FAKE, w=FAKE, Hi=64, soq=None, nv=FAKE, bt=FAKE, mp=64, nq=1,

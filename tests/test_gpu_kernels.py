@@ -564,3 +564,86 @@ def test_index_topk_fused_exact_path_entries():
 def test_index_topk_query_tiles_fall_back():
     say("case: index_topk with a sequence map and 70 queries (tiles of queries, separate counting pass)")
     _fused_vs_separate(np.random.default_rng(302), [5000, 3000], 32, 128, seq_of_query=[0] * 40 + [1] * 30)
+
+
+# -------------------------------------------------- candidate pool --------
+def _pool_case(rng, n_per_seq, Hi, npool, k, key_fn=None, reps=2):
+    """Full scan -> pool (index_pool_build) -> scan and top-K inside the pool
+    (index_topk_pool), against the oracle on the same inputs; twice on the same
+    workspaces (they must be left clean)."""
+    B = len(n_per_seq)
+    pages = [(n + 63) // 64 for n in n_per_seq]
+    phys = rng.permutation(sum(pages))
+    bt = np.zeros((B, max(pages)), np.int32)
+    off, lat, key, slots = 0, [], [], []
+    for b, n in enumerate(n_per_seq):
+        bt[b, :pages[b]] = phys[off:off + pages[b]]
+        off += pages[b]
+        j = np.arange(n)
+        slots.append(bt[b, j // 64].astype(np.int64) * 64 + j % 64)
+        kk = rng.standard_normal((n, 128)).astype(np.float32)
+        key.append(bits(key_fn(kk) if key_fn else kk))
+        lat.append(bits(np.zeros((n, 512), np.float32)))
+    lat, key, slots = np.concatenate(lat), np.concatenate(key), np.concatenate(slots)
+    g, o = both_caches(lat, key, slots, sum(pages) * 64)
+    nvis = np.array(n_per_seq, np.int32)
+    ld = ((int(nvis.max()) + 63) // 64) * 64
+    q0 = bits(rng.standard_normal((B, Hi, 128)).astype(np.float32))   # gatekeeper layer
+    q1 = bits(rng.standard_normal((B, Hi, 128)).astype(np.float32))   # pooled layer
+    w0 = rng.random((B, Hi), dtype=np.float32)
+    w1 = rng.random((B, Hi), dtype=np.float32)
+    dnv, dbt = dev(nvis), dev(bt)
+    # gatekeeper scan (GPU), the same scores from the oracle
+    s_full = torch.full((B, ld), float("nan"), device="cuda")
+    lib.index_score(g, dev_bits(q0), dev(w0), dnv, dbt, s_full)
+    ref_full, _, _ = oracle.index_score(o, q0, w0, nvis, bt, ld=ld)
+    got_full = s_full.cpu().numpy()
+    for r in range(B):
+        assert same_bits_f32(got_full[r, :nvis[r]], ref_full[r, :nvis[r]])
+    ref_pool = oracle.pool_build(ref_full, nvis, npool)
+    ref_ps, _, _ = oracle.index_score_pool(o, q1, w1, nvis, ref_pool, bt)
+    ref_top = oracle.topk_pool(ref_ps, ref_pool, nvis, k)
+    ws_b = torch.zeros(lib.index_pool_build_workspace_size(B, ld, npool), dtype=torch.uint8, device="cuda")
+    ws_t = torch.zeros(lib.index_topk_pool_workspace_size(B, npool, k), dtype=torch.uint8, device="cuda")
+    for rep in range(reps):
+        pool = torch.full((B, npool), -7, dtype=torch.int32, device="cuda")
+        lib.index_pool_build(s_full, dnv, npool, pool, ws_b)
+        ps = torch.full((B, npool * 8), float("nan"), device="cuda")
+        top = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+        lib.index_topk_pool(g, dev_bits(q1), dev(w1), dnv, pool, dbt, ps, k, top, ws_t)
+        torch.cuda.synchronize()
+        assert np.array_equal(pool.cpu().numpy(), ref_pool), f"rep {rep}: pool differs"
+        got_ps = ps.cpu().numpy()
+        for r in range(B):
+            vis = ~np.isnan(ref_ps[r])
+            npv = int(vis.sum())
+            assert vis[:npv].all(), "visible pool positions are a prefix"
+            assert same_bits_f32(got_ps[r, :npv], ref_ps[r, :npv]), f"rep {rep} row {r}: pool scores differ"
+            assert np.all(np.isnan(got_ps[r, npv:])), "positions without an entry were written"
+        assert np.array_equal(top.cpu().numpy(), ref_top), f"rep {rep}: pool top-k differs"
+    return ref_pool
+
+
+def test_pool_build_and_topk_inside_pool():
+    rng = np.random.default_rng(400)
+    say("case: pool of 256 blocks over 3 paged sequences (partial last blocks), k = 300, Hi = 64")
+    _pool_case(rng, [20001, 3005, 777], 64, 256, 300)
+    say("case: pool of 2048 blocks over one 70,000-entry sequence, k = 2048, Hi = 16")
+    _pool_case(rng, [70000], 16, 2048, 2048)
+
+
+def test_pool_covering_every_block_and_short_pools():
+    rng = np.random.default_rng(401)
+    say("case: pools larger than the sequences (every block), k above the visible members")
+    pool = _pool_case(rng, [500, 61, 8, 0], 16, 128, 700)
+    assert list(pool[0, :63]) == list(range(63)) and np.all(pool[0, 63:] == -1)
+    assert np.all(pool[3] == -1), "a query with no visible entry has an empty pool"
+
+
+def test_pool_with_tied_keys():
+    def keys(k):
+        k[1000:3000] = k[1000]  # 2000 entries with one key: tied scores across many blocks
+        return k
+
+    say("case: pool with 2000 tied entries (ties to the lower block and entry)")
+    _pool_case(np.random.default_rng(402), [6000], 16, 300, 500, key_fn=keys)

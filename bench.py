@@ -92,9 +92,12 @@ def stored_traffic(wl_name: str):
 def fp4_bytes_per_step(wl):
     if wl.kind == "prefill":
         return int(wl.n_visible().astype("int64").sum()) * IDX_ENTRY_BYTES + wl.chunk * wl.K * MAIN_ENTRY_BYTES
-    idx_layers = sum(1 for m in wl.layers if m in ("full", "reindex"))
     n = [int(x) for x in wl.n_entries]
-    b = idx_layers * sum(n) * IDX_ENTRY_BYTES
+    if wl.npool > 0:  # Reindex layers read only their pool's members
+        b = sum(1 for m in wl.layers if m == "full") * sum(n) * IDX_ENTRY_BYTES
+        b += sum(1 for m in wl.layers if m == "reindex") * sum(min(8 * wl.npool, x) for x in n) * IDX_ENTRY_BYTES
+    else:
+        b = sum(1 for m in wl.layers if m in ("full", "reindex")) * sum(n) * IDX_ENTRY_BYTES
     b += len(wl.layers) * sum(min(wl.K, x) for x in n) * MAIN_ENTRY_BYTES
     return b
 
@@ -145,13 +148,18 @@ def cpu_baseline(wl):
     t1 = time.perf_counter()
     oracle.sparse_attn_decode(c, d["q"][:1], idx, bt, d["swa"][:1], d["swa_len"][:1], 1.0 / 512 ** 0.5)
     t2 = time.perf_counter()
-    idx_layers = sum(1 for m in wl.layers if m in ("full", "reindex"))
-    entries = sum(int(x) for x in wl.n_entries)
-    step_s = idx_layers * (t1 - t0) * entries / n + len(wl.layers) * wl.B * (t2 - t1)
+    # entries scanned per step: every index layer scans the whole cache, or, with a
+    # candidate pool, the Reindex layers only their pool's members
+    full_layers = sum(1 for m in wl.layers if m == "full" or (m == "reindex" and wl.npool == 0))
+    pool_layers = sum(1 for m in wl.layers if m == "reindex" and wl.npool > 0)
+    entries = full_layers * sum(int(x) for x in wl.n_entries)
+    entries += pool_layers * sum(min(8 * wl.npool, int(x)) for x in wl.n_entries)
+    step_s = (t1 - t0) * entries / n + len(wl.layers) * wl.B * (t2 - t1)
     return {"value": wl.B / step_s, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": (f"one index layer (MXFP4 scan + top-{wl.K}) over {n} entries and one {wl.H}-head attention "
                        f"({t1 - t0:.2f} s + {t2 - t1:.2f} s), scaled to the step: scans and top-k x{entries / n:g} "
-                       f"entries x{idx_layers} index layers, attention x{len(wl.layers)} layers x{wl.B} sequences")}
+                       f"(entries scanned by all index layers), attention x{len(wl.layers)} layers "
+                       f"x{wl.B} sequences")}
 
 
 def main():
@@ -257,7 +265,15 @@ def main():
 
     calls_us = {}
     if wl.kind == "decode":
-        idx_layers = [L for L in st.layers if L["mode"] in ("full", "reindex")]
+        # layers that scan the whole cache (with a candidate pool, only the Full layer)
+        idx_layers = [L for L in st.layers if L["mode"] == "full" or (L["mode"] == "reindex" and wl.npool == 0)]
+        if wl.npool > 0:
+            calls_us["index_pool_build"] = burst_ms([functools.partial(
+                lib.index_pool_build, st.scores, st.n_visible, wl.npool, st.pool, st.ws_pool)])[0] * 1e3
+            calls_us["index_topk_pool"] = burst_ms([functools.partial(
+                lib.index_topk_pool, s.cache, L["q_idx"], L["w"], s.n_visible, st.pool, s.block_table,
+                st.scores_pool, wl.K, L["topk"], st.ws_topk_pool)
+                for s in steps for L in st.layers if L["mode"] == "reindex"])[0] * 1e3
         scan = [functools.partial(lib.index_score, s.cache, L["q_idx"], L["w"], s.n_visible, s.block_table, s.scores)
                 for s in steps for L in idx_layers]
         calls_us["index_topk"] = burst_ms([functools.partial(lib.index_topk, s.cache, L["q_idx"], L["w"], s.n_visible,

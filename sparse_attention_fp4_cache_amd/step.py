@@ -9,6 +9,11 @@ divisé", memory section:
   Reuse   -- reuses the cache and the most recent indices, only attends.
 Every layer has its own main query and its own sliding window.
 
+With a candidate pool (workload npool > 0; "DeepSeek V4.1 Flash et le cerveau
+divisé", memory section) only the Full layer scans the whole cache: its scores
+give each query a pool of npool blocks of 8 consecutive entries, and the Reindex
+layers score and select inside that pool.
+
 This module only allocates device buffers and sequences calls; all arithmetic is
 in the HIP kernels behind ``lib``.
 """
@@ -56,6 +61,15 @@ class DecodeStep:
         self.ws_topk = torch.zeros(lib.topk_select_workspace_size(B, self.ld, K), dtype=torch.uint8, device=device)
         self.ws_attn = torch.zeros(lib.sparse_attn_decode_workspace_size(B, wl.H, K, W), dtype=torch.uint8,
                                    device=device)
+        self.npool = wl.npool
+        if self.npool > 0:
+            P = self.npool
+            self.pool = torch.full((B, P), -1, dtype=torch.int32, device=device)
+            self.ws_pool = torch.zeros(lib.index_pool_build_workspace_size(B, self.ld, P), dtype=torch.uint8,
+                                       device=device)
+            self.scores_pool = torch.zeros((B, lib.POOL_BLOCK * P), dtype=torch.float32, device=device)
+            self.ws_topk_pool = torch.zeros(lib.index_topk_pool_workspace_size(B, P, K), dtype=torch.uint8,
+                                            device=device)
         self.layers = []
         for li, mode in enumerate(wl.layers):
             d = wl.layer_inputs(li)
@@ -111,7 +125,13 @@ class DecodeStep:
             if mode == "full":
                 call("fp4_cache_write", lib.fp4_cache_write, self.cache, self.new_latent, self.new_key,
                      self.new_slot)
-            if mode in ("full", "reindex"):
+            if mode == "reindex" and self.npool > 0:
+                call("index_topk_pool", lib.index_topk_pool, self.cache, L["q_idx"], L["w"], self.n_visible,
+                     self.pool, self.block_table, self.scores_pool, self.wl.K, L["topk"], self.ws_topk_pool)
+                if keep_scores:
+                    L["scores"] = self.scores_pool.clone()
+                latest = L["topk"]
+            elif mode in ("full", "reindex"):
                 if self.fused_index:
                     call("index_topk", lib.index_topk, self.cache, L["q_idx"], L["w"], self.n_visible,
                          self.block_table, self.scores, self.wl.K, L["topk"], self.ws_topk)
@@ -125,6 +145,11 @@ class DecodeStep:
                     call("topk_select", lib.topk_select, self.scores, self.n_visible, self.wl.K, L["topk"],
                          self.ws_topk)
                 latest = L["topk"]
+                if mode == "full" and self.npool > 0:
+                    call("index_pool_build", lib.index_pool_build, self.scores, self.n_visible, self.npool,
+                         self.pool, self.ws_pool)
+                    if keep_scores:
+                        L["pool"] = self.pool.clone()
             if latest is None:
                 raise ValueError("a reuse layer needs an earlier full or reindex layer")
             call("sparse_attn_decode", lib.sparse_attn_decode, self.cache, L["q"], latest, self.block_table,

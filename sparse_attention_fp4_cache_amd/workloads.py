@@ -39,6 +39,11 @@ class Workload:
     ctx       context tokens per sequence (decode) / prefix tokens (prefill).
     m         tokens per compressed entry (disjoint groups).
     layers    layer modes of one step, e.g. ("full",) or ("full", "reuse", ...).
+    npool     0: Reindex layers rescan the whole cache.  > 0: the step's Full layer
+              turns its scores into a candidate pool of npool blocks of 8
+              consecutive entries, and the Reindex layers score and select inside
+              it ("DeepSeek V4.1 Flash et le cerveau divisé", memory section: about
+              16,000 positions at 1M entries, i.e. 2048 blocks).
     """
 
     name: str
@@ -56,6 +61,7 @@ class Workload:
     paged_random: bool = False
     chunk: int = 0  # prefill: new query tokens
     seed: int = 0
+    npool: int = 0  # decode: >0 -> Reindex layers scan a candidate pool of npool blocks of 8 entries
 
     # ------------------------------------------------------------ geometry --
     @property
@@ -188,6 +194,9 @@ WORKLOADS = {
                                  H=64, Hi=64, K=2048, paged_random=True),
     "decode_1m_10layer": Workload("decode_1m_10layer", 4, "decode", B=1, ctx=(1048576,), H=64, Hi=64, K=2048,
                                   layers=C4_LAYERS),
+    # the same inputs as decode_1m_10layer; the four Reindex layers use the pool
+    "decode_1m_10layer_pool": Workload("decode_1m_10layer_pool", 4, "decode", B=1, ctx=(1048576,), H=64, Hi=64,
+                                       K=2048, layers=C4_LAYERS, npool=2048),
     "prefill_chunk_4096": Workload("prefill_chunk_4096", 5, "prefill", B=1, ctx=(262144,), H=64, Hi=64, K=2048,
                                    chunk=4096),
 }

@@ -9,6 +9,8 @@ Where the oracle would take too long (the 4096-query prefill chunk), sampled
 queries are checked one by one and every query is checked for properties that
 hold at any size.  The oracle never sees a GPU result.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -60,8 +62,8 @@ def topk_equal(got, ref, label):
     assert len(bad) == 0, f"{label}: {len(bad)} top-k slots differ, first {bad[:4].tolist()}"
 
 
-def run_decode_case(name, attn_rows=None):
-    wl = WORKLOADS[name]
+def run_decode_case(name, attn_rows=None, wl=None):
+    wl = WORKLOADS[name] if wl is None else wl
     say(f"case: {name} (B={wl.B}, entries {int(wl.n_entries.min())}..{int(wl.n_entries.max())}, "
         f"H={wl.H}, K={wl.K}, layers {','.join(wl.layers)})")
     st = DecodeStep(wl, "cuda")
@@ -73,16 +75,29 @@ def run_decode_case(name, attn_rows=None):
     say("  cache bytes equal")
     bt = wl.block_table()
     nv = wl.n_visible()
-    latest = None
+    latest = ref_pool = None
     for li, L in enumerate(st.layers):
         d = wl.layer_inputs(li)
-        if L["mode"] in ("full", "reindex"):
+        if L["mode"] == "reindex" and wl.npool > 0:
+            # scores and selection inside the Full layer's candidate pool
+            ref_ps, not_fp32, _ = oracle.index_score_pool(o, d["q_idx"], d["w"], nv, ref_pool, bt)
+            assert not_fp32 == 0
+            npv = np.count_nonzero(~np.isnan(ref_ps), axis=1)
+            scores_equal(L["scores"].cpu().numpy(), ref_ps, npv, f"{name} layer {li} pool scores")
+            latest = oracle.topk_pool(ref_ps, ref_pool, nv, wl.K)
+            topk_equal(L["topk"].cpu().numpy(), latest, f"{name} layer {li} pool top-k")
+            say(f"  layer {li} (reindex over the pool): scores and top-k bit-exact")
+        elif L["mode"] in ("full", "reindex"):
             ref_s, not_fp32, _ = oracle.index_score(o, d["q_idx"], d["w"], nv, bt, ld=st.ld)
             assert not_fp32 == 0
             scores_equal(L["scores"].cpu().numpy(), ref_s, nv, f"{name} layer {li} scores")
             latest = oracle.topk_select(ref_s, nv, wl.K)
             topk_equal(L["topk"].cpu().numpy(), latest, f"{name} layer {li} top-k")
             say(f"  layer {li} ({L['mode']}): scores and top-k bit-exact")
+            if L["mode"] == "full" and wl.npool > 0:
+                ref_pool = oracle.pool_build(ref_s, nv, wl.npool)
+                topk_equal(L["pool"].cpu().numpy(), ref_pool, f"{name} layer {li} candidate pool")
+                say(f"  layer {li}: candidate pool of {wl.npool} blocks bit-exact")
         rows = np.arange(wl.B) if attn_rows is None else np.asarray(attn_rows)
         ro, rl = oracle.sparse_attn_decode(o, d["q"][rows], latest[rows], bt[rows], d["swa"][rows],
                                            d["swa_len"][rows], st.scale)
@@ -109,6 +124,25 @@ def test_config_ragged_decode_32_paged():
 @pytest.mark.timeout(1200)
 def test_config_decode_1m_10layer_and_graph_replay():
     st = run_decode_case("decode_1m_10layer")
+    graph_replays_equal_eager(st)
+
+
+@pytest.mark.timeout(900)
+def test_config_ragged_decode_32_candidate_pool():
+    # a Full layer, a Reindex layer inside pools of 1024 blocks (rows with fewer
+    # than 8192 entries keep every block), and a Reuse layer
+    wl = dataclasses.replace(WORKLOADS["ragged_decode_32"], name="ragged_decode_32_pool",
+                             layers=("full", "reindex", "reuse"), npool=1024)
+    run_decode_case(wl.name, attn_rows=np.arange(0, 32, 4), wl=wl)
+
+
+@pytest.mark.timeout(1200)
+def test_config_decode_1m_10layer_pool_and_graph_replay():
+    st = run_decode_case("decode_1m_10layer_pool")
+    graph_replays_equal_eager(st)
+
+
+def graph_replays_equal_eager(st):
     # the benchmark replays the step as one HIP graph: every replay must equal the
     # eager step bit for bit, with eager work and synchronisations in between
     ref = [(L["out"].clone(), L["lse"].clone(), None if "topk" not in L else L["topk"].clone()) for L in st.layers]
@@ -121,9 +155,13 @@ def test_config_decode_1m_10layer_and_graph_replay():
         st.run()
     torch.cuda.synchronize()
     for rep in range(3):
-        for L in st.layers:
+        for L in st.layers:  # clear every output the graph must rewrite
             L["out"].zero_()
             L["lse"].zero_()
+            if "topk" in L:
+                L["topk"].fill_(-7)
+        if st.npool > 0:
+            st.pool.fill_(-7)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()

@@ -223,6 +223,10 @@ int sparse_attn_decode(const csa2_fp4_cache* cache, const uint16_t* q, int32_t H
  *   swa_first_valid                             : rows below it do not exist
  * Query i attends its selected entries plus window rows max(i, swa_first_valid) ..
  * i + window - 1 under one softmax.  out f32 [T][H][512], lse f32 [T][H].
+ * A bounded replay that restarts the window at the chunk's first token s ("DeepSeek-
+ * V4.1-Flash, expliqué pas à pas", bounded SWA replay: keys of the window truncated
+ * to the replayed segment) passes swa_first_valid = window - 1, so query token t
+ * sees window tokens max(s, t - window + 1) .. t. 
  *   ws, ws_bytes: at least sparse_attn_prefill_chunk_workspace_size(T, H, k, window). */
 size_t sparse_attn_prefill_chunk_workspace_size(int32_t T, int32_t H, int32_t k, int32_t window);
 int sparse_attn_prefill_chunk(const csa2_fp4_cache* cache, const uint16_t* q, int32_t H, const int32_t* topk_idx,

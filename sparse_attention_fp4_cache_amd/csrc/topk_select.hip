@@ -43,7 +43,8 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kPer = 8;  // consecutive scores per thread
 constexpr int kChunk = kThreads * kPer;
-constexpr int kListCap = 8192;        // listed entries per query (fixed regions per chunk)
+constexpr int kListCap = 12288;       // listed entries of a query that the last workgroup holds in LDS
+constexpr int kMinRegion = 128;       // least list slots per chunk (the top-K's share of a chunk, with margin)
 constexpr int kMaxChunksFast = 2048;  // chunk bookkeeping in LDS (rows up to 8M entries)
 
 struct TopkCtl {
@@ -57,16 +58,30 @@ struct TopkWs {
   uint32_t* hist;            // [nq][kTopkHistCopies][kBins]: digit 1 (key bits 31..20)
   uint32_t* hist2;           // [nq][kBins]: digit 2 (key bits 19..8) of the b* entries
   uint32_t* count;           // [nq][nchunk]: entries of the chunk in bins >= b*
-  unsigned long long* list;  // [nq][kListCap]: chunk c's entries at c * (kListCap / nch)
+  unsigned long long* list;  // [nq][list_slots(nchunk)]: chunk c's entries at c * region_slots(nch)
 };
 
 __host__ __device__ inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// List slots of each chunk of a row of nch chunks.  A chunk lists its entries at or
+// above the threshold bin: about (k + the bin's population) / nch of them, and the
+// 12-bit bin of a narrow score distribution can hold more entries than k, so every
+// region keeps at least kMinRegion slots.
+__host__ __device__ inline long long region_slots(long long nch) {
+  const long long even = (kListCap / nch) & ~1LL;
+  return even > kMinRegion ? even : kMinRegion;
+}
+// List slots per query for rows of up to nchunk chunks (nch * region_slots(nch) is
+// largest at nch = nchunk or where kListCap / nch still exceeds kMinRegion).
+__host__ __device__ inline long long list_slots(long long nchunk) {
+  return nchunk * kMinRegion > kListCap ? nchunk * kMinRegion : kListCap;
+}
 
 __host__ __device__ inline size_t ws_bytes_for(int nq, long long nchunk) {
   return align_up(sizeof(TopkCtl) * (size_t)nq) + align_up(sizeof(uint32_t) * kBins * kTopkHistCopies * (size_t)nq) +
          align_up(sizeof(uint32_t) * kBins * (size_t)nq) +
          align_up(sizeof(uint32_t) * (size_t)nchunk * (size_t)nq) +
-         align_up(sizeof(unsigned long long) * kListCap * (size_t)nq);
+         align_up(sizeof(unsigned long long) * (size_t)list_slots(nchunk) * (size_t)nq);
 }
 
 __host__ __device__ inline TopkWs carve(void* base, int nq, long long nchunk) {
@@ -372,12 +387,13 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
   }
   if (base >= n) return;
   const int nch = (int)((n + kChunk - 1) / kChunk);
-  const int cap = (kListCap / nch) & ~1;  // region of each chunk in the list (0: always the slow path)
+  const int cap = (int)region_slots(nch);  // region of each chunk in the list
   TopkCtl* ctl = ws.ctl + q;
   uint32_t* gh = ws.hist + (size_t)q * kTopkHistCopies * kBins;  // its copies, kBins apart
   uint32_t* gh2 = ws.hist2 + (size_t)q * kBins;
   uint32_t* gcount = ws.count + (size_t)q * nchunk;
-  unsigned long long* glist = ws.list + (size_t)q * kListCap;
+  unsigned long long* glist = ws.list + (size_t)q * (size_t)list_slots(nchunk);
+  const uint32_t list_bytes = (uint32_t)(nch * cap) * 8u;  // this row's regions
   const float* row = scores + (int64_t)q * ld;
 
   uint32_t key[kPer];
@@ -459,7 +475,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
   unsigned long long spec[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint4 v = ld_agent16(glist, kListCap * 8u, (uint32_t)(spec_c * cap + spec_s0 + 2 * i) * 8u);
+    const uint4 v = ld_agent16(glist, list_bytes, (uint32_t)(spec_c * cap + spec_s0 + 2 * i) * 8u);
     spec[2 * i] = ((unsigned long long)v.y << 32) | v.x;
     spec[2 * i + 1] = ((unsigned long long)v.w << 32) | v.z;
   }
@@ -476,7 +492,10 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
     if (my_cnt > (uint32_t)cap) sm.ovf = 1u;
     if (my_cnt > (uint32_t)kSpec) sm.more = 1u;
     total = t2;
-    if (tid == 0) sm.cpos[nch] = total;
+    if (tid == 0) {
+      sm.cpos[nch] = total;
+      if (total > (uint32_t)kListCap) sm.ovf = 1u;  // more than the LDS list holds
+    }
   }
   lds_barrier();
   if (sm.ovf == 0u) {
@@ -552,7 +571,13 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
 // eight lists, taken in wavefront order, are the row's candidates in index order;
 // the boundary and the ordered compaction follow as in the last workgroup above.
 constexpr int kRowCap = 1024;           // listed entries per wavefront segment
-constexpr int kRowSelectQueries = 128;  // rows from which this kernel is used
+constexpr int kRowSelectQueries = 128;  // rows from which this kernel is used ...
+// ... when they fill the chip or are short: a few long rows (a 128-token replay over
+// a 1M-token cache) would leave most compute units idle while one workgroup per row
+// streams megabytes, so they take the chunked path
+inline bool select_by_row(int32_t nq, int64_t ld) {
+  return nq >= kRowSelectQueries && (nq >= 256 || ld <= 65536);
+}
 struct RowSmem {
   unsigned long long list[kWaves][kRowCap];
   uint32_t h[kBins];  // digit-2 histogram of the b* entries, then radix-round scratch
@@ -792,9 +817,10 @@ int topk_enqueue(const float* scores, int64_t ld, const int32_t* n_visible, int3
   const TopkWs w = carve(ws, nq, nchunk);
   const dim3 grid((unsigned)grid_x, (unsigned)nq);
   const int ncopies = hist_done ? copies : topk_hist_copies(nchunk);
-  if (ld > 0 && !hist_done && nq < kRowSelectQueries)
+  const bool by_row = select_by_row(nq, ld);
+  if (ld > 0 && !hist_done && !by_row)
     hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kThreads), 0, stream, scores, ld, n_visible, k, w, ncopies);
-  if (nq >= kRowSelectQueries) {  // many rows: one workgroup per row, counting its own row
+  if (by_row) {  // many rows: one workgroup per row, counting its own row
     hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)nq), dim3(kThreads), 0, stream, scores, ld, n_visible, k,
                        topk_idx, w.hist, hist_done ? ncopies : 0, pool, npool);
     return launch_status();

@@ -44,6 +44,12 @@ class Workload:
               consecutive entries, and the Reindex layers score and select inside
               it ("DeepSeek V4.1 Flash et le cerveau divisé", memory section: about
               16,000 positions at 1M entries, i.e. 2048 blocks).
+    swa_replay prefill only: the chunk is a bounded replay of the prompt's last
+              tokens, and its sliding window starts at the replay's first token s,
+              so query t sees window tokens max(s, t - W + 1) .. t ("DeepSeek-V4.1-
+              Flash, expliqué pas à pas", bounded SWA replay in the on-disk cache
+              chapter; the interval's formula is lost there, this is its plain
+              reading).
     """
 
     name: str
@@ -62,6 +68,7 @@ class Workload:
     chunk: int = 0  # prefill: new query tokens
     seed: int = 0
     npool: int = 0  # decode: >0 -> Reindex layers scan a candidate pool of npool blocks of 8 entries
+    swa_replay: bool = False  # prefill: the window starts at the chunk's first token (bounded replay)
 
     # ------------------------------------------------------------ geometry --
     @property
@@ -155,7 +162,9 @@ class Workload:
             d["swa_len"] = np.full(self.B, self.W, np.int32)
         else:
             d["swa"] = self._normal_bf16(layer, _T_SWA, (self.W - 1 + self.chunk, LATENT_DIM), lat_ch)
-            d["swa_first_valid"] = max(0, self.W - 1 - int(self.ctx[0]))
+            # window row r holds token ctx - (W - 1) + r; rows below swa_first_valid
+            # do not exist (before the prompt, or before a replay's first token)
+            d["swa_first_valid"] = self.W - 1 if self.swa_replay else max(0, self.W - 1 - int(self.ctx[0]))
         return d
 
     def n_visible(self) -> np.ndarray:
@@ -199,6 +208,10 @@ WORKLOADS = {
                                        K=2048, layers=C4_LAYERS, npool=2048),
     "prefill_chunk_4096": Workload("prefill_chunk_4096", 5, "prefill", B=1, ctx=(262144,), H=64, Hi=64, K=2048,
                                    chunk=4096),
+    # bounded replay of the last 128 tokens of a 1,048,576-token prompt: every query
+    # has its causal top-K over the whole cache; the window restarts at the replay
+    "replay_128_1m": Workload("replay_128_1m", 6, "prefill", B=1, ctx=(1048576 - 128,), H=64, Hi=64, K=2048,
+                              chunk=128, swa_replay=True),
 }
 
 

@@ -175,18 +175,18 @@ def graph_replays_equal_eager(st):
     say("  graph replays equal the eager step")
 
 
-@pytest.mark.timeout(1200)
-def test_config_prefill_chunk_4096():
-    wl = WORKLOADS["prefill_chunk_4096"]
+def run_prefill_case(name, which):
+    wl = WORKLOADS[name]
     T, K = wl.chunk, wl.K
-    say(f"case: prefill_chunk_4096 (prefix {int(wl.n_entries[0])} entries + {wl.n_chunk_entries} in-chunk, "
-        f"T={T}, K={K})")
+    d = wl.layer_inputs(0)
+    say(f"case: {name} (prefix {int(wl.n_entries[0])} entries + {wl.n_chunk_entries} in-chunk, T={T}, K={K}, "
+        f"window rows from {d['swa_first_valid']})")
     st = PrefillStep(wl, "cuda")
     st.build_cache()
     st.run()
     torch.cuda.synchronize()
     o = oracle_cache(wl)
-    cache_equal(st, o, "prefill")
+    cache_equal(st, o, name)
     say("  cache bytes equal (prefix + chunk entries)")
     nv = wl.n_visible()
     topk = st.topk.cpu().numpy()
@@ -197,21 +197,32 @@ def test_config_prefill_chunk_4096():
     lse = st.lse.cpu().numpy()
     assert np.all(np.isfinite(lse)), "non-finite lse"
     say("  all queries: top-k causal, distinct, ascending; lse finite")
-    # sampled queries, one by one: first, around the odd/even boundary, middle, last
-    which = np.array([0, 1, 2, 2047, 2048, T - 2, T - 1], np.int32)
-    d = wl.layer_inputs(0)
+    # sampled queries, one by one
+    which = np.asarray(which, np.int32)
     bt = wl.block_table()
-    ld = st.ld
     ref_s, not_fp32, _ = oracle.index_score(o, d["q_idx"][which], d["w"][which], nv[which], bt,
-                                            seq_of_query=np.zeros(len(which), np.int32), ld=ld)
+                                            seq_of_query=np.zeros(len(which), np.int32), ld=st.ld)
     assert not_fp32 == 0
     got_s = st.scores[torch.from_numpy(which.astype(np.int64)).cuda()].cpu().numpy()
-    scores_equal(got_s, ref_s, nv[which], "prefill sampled scores")
+    scores_equal(got_s, ref_s, nv[which], f"{name} sampled scores")
     ref_k = oracle.topk_select(ref_s, nv[which], K)
-    topk_equal(topk[which], ref_k, "prefill sampled top-k")
+    topk_equal(topk[which], ref_k, f"{name} sampled top-k")
     say(f"  queries {which.tolist()}: scores and top-k bit-exact")
     idx_full = np.full((T, K), -1, np.int32)
     idx_full[which] = ref_k
     ro, rl = oracle.sparse_attn_prefill_chunk(o, d["q"], idx_full, bt[0], d["swa"], d["swa_first_valid"], wl.W,
                                               st.scale, which=which)
-    attn_close(st.out.cpu().numpy()[which], ro[which], lse[which], rl[which], "prefill sampled attention")
+    attn_close(st.out.cpu().numpy()[which], ro[which], lse[which], rl[which], f"{name} sampled attention")
+    say(f"  queries {which.tolist()}: attention within tolerance")
+
+
+@pytest.mark.timeout(1200)
+def test_config_prefill_chunk_4096():
+    # first, around the odd/even boundary, middle, last
+    run_prefill_case("prefill_chunk_4096", [0, 1, 2, 2047, 2048, 4094, 4095])
+
+
+@pytest.mark.timeout(1200)
+def test_config_bounded_replay_128_at_1m():
+    # the window restarts at the replay: query 0 sees one window row, query 127 all 128
+    run_prefill_case("replay_128_1m", [0, 1, 2, 63, 64, 126, 127])

@@ -272,7 +272,6 @@ def _topk_case(scores, nvis, k, label, runs=2):
         got = out.cpu().numpy()
         for q in range(nq):
             assert np.array_equal(got[q], ref[q]), f"{label} run {r} query {q}"
-    assert int(ws.cpu().numpy().astype(np.int64).sum()) == 0 or True
     say(f"  {label}: ok")
 
 
@@ -324,6 +323,21 @@ def test_topk_many_rows_one_workgroup_per_row():
     say("case: top-k 136 rows (one workgroup per row)")
     _topk_case(s, nvis, 2048, "rows k=2048")
     _topk_case(s, nvis, 300, "rows k=300")
+
+
+def test_topk_few_long_rows_take_chunks():
+    """130 rows of 70,000 scores (too few rows to fill the chip with one workgroup
+    each): the chunked path with many rows, ragged, tied and short rows included."""
+    rng = np.random.default_rng(331)
+    nq, ld = 130, 70_000
+    s = rng.standard_normal((nq, ld)).astype(np.float32)
+    nvis = rng.integers(1, ld + 1, nq).astype(np.int32)
+    nvis[:4] = [ld, 2048, 100, 0]
+    s[4] = rng.integers(0, 500, ld).astype(np.float32)   # many ties
+    s[5] = -0.5                                           # all equal
+    nvis[4:6] = ld
+    say("case: top-k 130 rows of 70,000 (chunked)")
+    _topk_case(s, nvis, 2048, "long rows k=2048")
 
 
 def test_topk_large_row_many_chunks():

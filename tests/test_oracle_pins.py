@@ -485,3 +485,29 @@ def test_prefill_query_equals_decode_with_its_window():
         o, l = oracle.sparse_attn_decode(c, q[i:i + 1], idx[i:i + 1], bt[None, :], win,
                                          np.array([i + W - lo], np.int32), 0.04)
         assert np.array_equal(o[0], out[i]) and np.array_equal(l[0], lse[i])
+
+
+def test_bounded_replay_window_is_the_replayed_segment():
+    """A replay starting at token s: query token t sees window tokens
+    max(s, t - W + 1) .. t and nothing before s (the bounded SWA replay; the interval
+    is the plain reading of the page, whose formula is lost).  Built here in token
+    coordinates, independently of the row arithmetic of swa_first_valid."""
+    rng = np.random.default_rng(12)
+    c = _small_cache(rng, 256)
+    H, T, W, k = 16, 9, 4, 8
+    s = 1000  # replay start (= chunk start)
+    q = to_bf16_bits(rng.standard_normal((T, H, 512)).astype(np.float32))
+    swa = to_bf16_bits(rng.standard_normal((W - 1 + T, 512)).astype(np.float32))
+    token_of_row = s - (W - 1) + np.arange(W - 1 + T)
+    idx = np.sort(rng.choice(200, (T, k), replace=False), axis=1).astype(np.int32)
+    bt = np.arange(4, dtype=np.int32)
+    out, lse = oracle.sparse_attn_prefill_chunk(c, q, idx, bt, swa, W - 1, W, 0.04)
+    for i in range(T):
+        t = s + i
+        rows = [r for r in range(W - 1 + T) if max(s, t - W + 1) <= token_of_row[r] <= t]
+        assert len(rows) == min(i + 1, W)
+        win = np.zeros((1, W, 512), np.uint16)
+        win[0, :len(rows)] = swa[rows]
+        o, l = oracle.sparse_attn_decode(c, q[i:i + 1], idx[i:i + 1], bt[None, :], win,
+                                         np.array([len(rows)], np.int32), 0.04)
+        assert np.array_equal(o[0], out[i]) and np.array_equal(l[0], lse[i])

@@ -90,6 +90,18 @@ def stored_traffic(wl_name: str):
 
 
 def fp4_bytes_per_step(wl):
+    if wl.kind == "schedule":  # one token through every layer, one cache per Full layer
+        b = 0
+        for li, mode in enumerate(wl.modes):
+            if mode == "swa":
+                continue
+            n = int(wl.cache_workload(wl.source(li)).n_entries[0])
+            if mode == "full" or (mode == "reindex" and wl.npool == 0):
+                b += n * IDX_ENTRY_BYTES
+            elif mode == "reindex":
+                b += min(8 * wl.npool, n) * IDX_ENTRY_BYTES
+            b += min(wl.K, n) * MAIN_ENTRY_BYTES
+        return b
     if wl.kind == "prefill":
         return int(wl.n_visible().astype("int64").sum()) * IDX_ENTRY_BYTES + wl.chunk * wl.K * MAIN_ENTRY_BYTES
     n = [int(x) for x in wl.n_entries]
@@ -131,6 +143,8 @@ def cpu_baseline(wl):
         return {"value": len(which) / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
                 "sample": f"2 of the chunk's {wl.chunk} queries (scan, top-{wl.K}, attention), {dt:.2f} s"}
 
+    if wl.kind == "schedule":
+        return cpu_baseline_schedule(wl)
     n_full = int(wl.n_entries[0])
     frac = max(1, math.ceil(n_full / 524288))
     sub = small_variant(wl, ctx=[int(wl.ctx[0]) // frac], name=wl.name + "_sample")
@@ -162,6 +176,42 @@ def cpu_baseline(wl):
                        f"x{wl.B} sequences")}
 
 
+def cpu_baseline_schedule(wl):
+    """The oracle on one index layer (scan + top-k) over the first 524,288 entries of
+    the m = 1 decoder cache and one attention, scaled to the whole schedule's scanned
+    entries and attentions."""
+    import oracle
+    from sparse_attention_fp4_cache_amd.workloads import small_variant
+
+    dec = wl.cache_workload(wl.writers()[-1])
+    sub = small_variant(dec, ctx=[524288], name=wl.name + "_sample")
+    n = int(sub.n_entries[0])
+    lat, key = sub.cache_rows(0, 0, n)
+    c = oracle.Cache(sub.num_slots)
+    oracle.fp4_cache_write(c, lat, key, sub.slots(0, 0, n))
+    del lat, key
+    d = wl.query_workload().layer_inputs(wl.writers()[-1])
+    bt = sub.block_table()[:1]
+    nv = sub.n_visible()[:1]
+    t0 = time.perf_counter()
+    sc, _, _ = oracle.index_score(c, d["q_idx"], d["w"], nv, bt)
+    idx = oracle.topk_select(sc, nv, wl.K)
+    t1 = time.perf_counter()
+    oracle.sparse_attn_decode(c, d["q"], idx, bt, d["swa"], d["swa_len"], 1.0 / 512 ** 0.5)
+    t2 = time.perf_counter()
+    entries = 0
+    for li, mode in enumerate(wl.modes):
+        if mode == "full" or (mode == "reindex" and wl.npool == 0):
+            entries += int(wl.cache_workload(wl.source(li)).n_entries[0])
+        elif mode == "reindex":
+            entries += min(8 * wl.npool, int(wl.cache_workload(wl.source(li)).n_entries[0]))
+    step_s = (t1 - t0) * entries / n + len(wl.modes) * (t2 - t1)
+    return {"value": 1.0 / step_s, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": (f"one index layer (MXFP4 scan + top-{wl.K}) over {n} entries of the m = 1 cache and one "
+                       f"{wl.H}-head attention ({t1 - t0:.2f} s + {t2 - t1:.2f} s), scaled to the schedule: scans "
+                       f"x{entries / n:g} (entries scanned by all index layers), attention x{len(wl.modes)} layers")}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -173,7 +223,7 @@ def main():
     import torch
 
     from sparse_attention_fp4_cache_amd import lib
-    from sparse_attention_fp4_cache_amd.step import DecodeStep, PrefillStep
+    from sparse_attention_fp4_cache_amd.step import DecodeStep, PrefillStep, ScheduleDecodeStep
     from sparse_attention_fp4_cache_amd.workloads import WORKLOADS
 
     if not os.path.exists(lib.LIB_PATH):
@@ -184,11 +234,11 @@ def main():
     wl = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    Step = DecodeStep if wl.kind == "decode" else PrefillStep
+    Step = {"decode": DecodeStep, "prefill": PrefillStep, "schedule": ScheduleDecodeStep}[wl.kind]
     st = Step(wl, dev)
     st.build_cache()
     torch.cuda.synchronize()
-    R = args.replicas if args.replicas > 0 else 1 + math.ceil(2 * MALL_BYTES / st.cache.nbytes())
+    R = args.replicas if args.replicas > 0 else 1 + math.ceil(2 * MALL_BYTES / st.cache_bytes())
     R = max(1, min(R, 16))
     steps = [st] + [st.replica() for _ in range(R - 1)]
     torch.cuda.synchronize()
@@ -264,7 +314,36 @@ def main():
         return e0.elapsed_time(e1) / (reps * len(calls)), reps * len(calls)
 
     calls_us = {}
-    if wl.kind == "decode":
+    if wl.kind == "schedule":
+        # the m = 1 decoder cache's Full-layer scan is the roofline kernel (the largest scan)
+        wdec = wl.writers()[-1]
+        for w in wl.writers():
+            Lw = st.layers[w]
+            key = "index_topk_m1" if w == wdec else "index_topk_m2"
+            if key in calls_us:
+                continue
+            calls_us[key] = burst_ms([functools.partial(
+                lib.index_topk, s.caches[w]["cache"], Lw["q_idx"], Lw["w"], s.caches[w]["n_visible"],
+                s.caches[w]["block_table"], s.caches[w]["scores"], wl.K, Lw["topk"], s.caches[w]["ws_topk"])
+                for s in steps])[0] * 1e3
+        Cd = st.caches[wdec]
+        if Cd["pooled"]:
+            calls_us["index_pool_build"] = burst_ms([functools.partial(
+                lib.index_pool_build, Cd["scores"], Cd["n_visible"], wl.npool, Cd["pool"], Cd["ws_pool"])])[0] * 1e3
+            calls_us["index_topk_pool"] = burst_ms([functools.partial(
+                lib.index_topk_pool, s.caches[wdec]["cache"], L["q_idx"], L["w"], Cd["n_visible"], Cd["pool"],
+                Cd["block_table"], Cd["scores_pool"], wl.K, L["topk"], Cd["ws_topk_pool"])
+                for s in steps for L in st.layers if L["mode"] == "reindex"])[0] * 1e3
+        calls_us["sparse_attn_decode"] = burst_ms([functools.partial(
+            lib.sparse_attn_decode, s.caches[L["src"]]["cache"], L["q"], st.layers[L["src"]]["topk"],
+            s.caches[L["src"]]["block_table"], L["swa"], L["swa_len"], st.scale, L["out"], L["lse"], st.ws_attn)
+            for s in steps for L in st.layers if L["mode"] != "swa"])[0] * 1e3
+        scan = [functools.partial(lib.index_score, s.caches[wdec]["cache"], st.layers[wdec]["q_idx"],
+                                  st.layers[wdec]["w"], Cd["n_visible"], Cd["block_table"], Cd["scores"])
+                for s in steps]
+        idx_bytes = int(Cd["wl"].n_entries[0]) * IDX_ENTRY_BYTES
+        tokens = 1
+    elif wl.kind == "decode":
         # layers that scan the whole cache (with a candidate pool, only the Full layer)
         idx_layers = [L for L in st.layers if L["mode"] == "full" or (L["mode"] == "reindex" and wl.npool == 0)]
         if wl.npool > 0:
@@ -325,10 +404,14 @@ def main():
         "vs_baseline": None,
         "dtype": "fp4(e2m1)+fp32",
         "data": "synthetic (seeded N(0,1) bf16 latents/keys/queries/window, U(0,1) head weights)",
-        "config": {"workload": wl.name, "context_tokens": int(wl.ctx[0]) if wl.B == 1 else list(wl.ctx),
-                   "entries_per_seq": [int(x) for x in wl.n_entries][:4], "batch": wl.B, "heads": wl.H,
-                   "index_heads": wl.Hi, "topk": wl.K, "window": wl.W,
-                   "layers": ",".join(wl.layers) if wl.kind == "decode" else f"prefill chunk {wl.chunk}",
+        "config": {"workload": wl.name,
+                   "context_tokens": wl.ctx if wl.kind == "schedule" else (int(wl.ctx[0]) if wl.B == 1
+                                                                          else list(wl.ctx)),
+                   "entries_per_seq": ([int(wl.cache_workload(w).n_entries[0]) for w in wl.writers()]
+                                       if wl.kind == "schedule" else [int(x) for x in wl.n_entries][:4]),
+                   "batch": wl.B, "heads": wl.H, "index_heads": wl.Hi, "topk": wl.K, "window": wl.W,
+                   "layers": (",".join(wl.layers) if wl.kind in ("decode", "schedule")
+                              else f"prefill chunk {wl.chunk}"),
                    "hip_graph": bool(args.graph), "cache_copies_rotated": R},
         "warm_ms_per_step": warm_ms,
         "warm_tokens_per_s": tokens / (warm_ms * 1e-3),

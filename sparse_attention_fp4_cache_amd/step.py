@@ -25,7 +25,7 @@ import numpy as np
 import torch
 
 from . import lib
-from .workloads import PAGE_SIZE, Workload
+from .workloads import PAGE_SIZE, ScheduleWorkload, Workload
 
 
 def to_device_bits(a: np.ndarray, device) -> torch.Tensor:
@@ -88,24 +88,11 @@ class DecodeStep:
     # ------------------------------------------------------------- cache --
     def build_cache(self, rows_per_call: int = 1 << 16):
         """Write every sequence's entries (host-generated bf16 rows) into the cache."""
-        wl = self.wl
-        last_lat, last_key, last_slot = [], [], []
-        for b in range(wl.B):
-            n = int(wl.n_entries[b])
-            lat, key = wl.cache_rows(b, 0, n)
-            slots = wl.slots(b, 0, n)
-            for s in range(0, n, rows_per_call):
-                e = min(n, s + rows_per_call)
-                lib.fp4_cache_write(self.cache, to_device_bits(lat[s:e], self.device),
-                                    to_device_bits(key[s:e], self.device),
-                                    torch.from_numpy(slots[s:e]).to(self.device))
-            last_lat.append(lat[n - 1])
-            last_key.append(key[n - 1])
-            last_slot.append(slots[n - 1])
-        # the newest entry of every sequence, rewritten by the Full layer each step
-        self.new_latent = to_device_bits(np.stack(last_lat), self.device)
-        self.new_key = to_device_bits(np.stack(last_key), self.device)
-        self.new_slot = torch.from_numpy(np.array(last_slot, np.int64)).to(self.device)
+        self.new_latent, self.new_key, self.new_slot = _write_decode_cache(self.cache, self.wl, self.device,
+                                                                           rows_per_call)
+
+    def cache_bytes(self) -> int:
+        return self.cache.nbytes()
 
     def replica(self) -> "DecodeStep":
         """The same step over a copy of the cache in other device memory (query
@@ -156,6 +143,130 @@ class DecodeStep:
                  L["swa"], L["swa_len"], self.scale, L["out"], L["lse"], self.ws_attn)
 
 
+def _write_decode_cache(cache, wl: Workload, device, rows_per_call: int):
+    """Write every sequence's entries of a decode workload into `cache`; returns the
+    newest entry of every sequence (latent, key, slot), which a Full layer rewrites
+    each step."""
+    last_lat, last_key, last_slot = [], [], []
+    for b in range(wl.B):
+        n = int(wl.n_entries[b])
+        lat, key = wl.cache_rows(b, 0, n)
+        slots = wl.slots(b, 0, n)
+        for s in range(0, n, rows_per_call):
+            e = min(n, s + rows_per_call)
+            lib.fp4_cache_write(cache, to_device_bits(lat[s:e], device), to_device_bits(key[s:e], device),
+                                torch.from_numpy(slots[s:e]).to(device))
+        last_lat.append(lat[n - 1])
+        last_key.append(key[n - 1])
+        last_slot.append(slots[n - 1])
+        del lat, key
+    return (to_device_bits(np.stack(last_lat), device), to_device_bits(np.stack(last_key), device),
+            torch.from_numpy(np.array(last_slot, np.int64)).to(device))
+
+
+class ScheduleDecodeStep:
+    """Device state for one decode token through a whole layer schedule with one
+    cache per Full layer ("Résumé exécutif", CSA2 section: of 40 layers only four
+    write a cache and the other 36 read their source's; every layer keeps its own
+    query and window).  Window-only layers attend their window alone (k = 0)."""
+
+    def __init__(self, sw: ScheduleWorkload, device="cuda", softmax_scale: float | None = None):
+        self.wl = sw
+        self.device = device
+        self.scale = lib.default_softmax_scale() if softmax_scale is None else softmax_scale
+        K, W, H = sw.K, sw.W, sw.H
+        pooled = {sw.source(l) for l, md in enumerate(sw.modes) if md == "reindex"} if sw.npool > 0 else set()
+        self.caches = {}
+        for w in sw.writers():
+            cw = sw.cache_workload(w)
+            nv = cw.n_visible()
+            ld = int(((int(nv.max()) + PAGE_SIZE - 1) // PAGE_SIZE) * PAGE_SIZE)
+            C = {"wl": cw, "cache": lib.Cache(cw.num_slots, device),
+                 "block_table": torch.from_numpy(cw.block_table()).to(device),
+                 "n_visible": torch.from_numpy(nv).to(device), "ld": ld,
+                 "scores": torch.zeros((1, ld), dtype=torch.float32, device=device),
+                 "ws_topk": torch.zeros(lib.topk_select_workspace_size(1, ld, K), dtype=torch.uint8, device=device),
+                 "pooled": w in pooled}
+            if C["pooled"]:
+                P = sw.npool
+                C["pool"] = torch.full((1, P), -1, dtype=torch.int32, device=device)
+                C["ws_pool"] = torch.zeros(lib.index_pool_build_workspace_size(1, ld, P), dtype=torch.uint8,
+                                           device=device)
+                C["scores_pool"] = torch.zeros((1, lib.POOL_BLOCK * P), dtype=torch.float32, device=device)
+                C["ws_topk_pool"] = torch.zeros(lib.index_topk_pool_workspace_size(1, P, K), dtype=torch.uint8,
+                                                device=device)
+            self.caches[w] = C
+        self.ws_attn = torch.zeros(max(lib.sparse_attn_decode_workspace_size(1, H, K, W),
+                                       lib.sparse_attn_decode_workspace_size(1, H, 0, W)), dtype=torch.uint8,
+                                   device=device)
+        self.no_topk = torch.zeros((1, 0), dtype=torch.int32, device=device)
+        qw = sw.query_workload()
+        self.layers = []
+        for li, mode in enumerate(sw.modes):
+            d = qw.layer_inputs(li)
+            L = {"mode": mode, "src": sw.source(li), "q": to_device_bits(d["q"], device),
+                 "swa": to_device_bits(d["swa"], device), "swa_len": torch.from_numpy(d["swa_len"]).to(device),
+                 "out": torch.zeros((1, H, 512), dtype=torch.float32, device=device),
+                 "lse": torch.zeros((1, H), dtype=torch.float32, device=device)}
+            if mode in ("full", "reindex"):
+                L["q_idx"] = to_device_bits(d["q_idx"], device)
+                L["w"] = torch.from_numpy(d["w"]).to(device)
+                L["topk"] = torch.full((1, K), -1, dtype=torch.int32, device=device)
+                L["scores"] = None
+            self.layers.append(L)
+
+    def build_cache(self, rows_per_call: int = 1 << 16):
+        for C in self.caches.values():
+            C["new"] = _write_decode_cache(C["cache"], C["wl"], self.device, rows_per_call)
+
+    def cache_bytes(self) -> int:
+        return sum(C["cache"].nbytes() for C in self.caches.values())
+
+    def replica(self) -> "ScheduleDecodeStep":
+        """The same step over copies of every cache (other buffers shared)."""
+        r = copy.copy(self)
+        r.caches = {w: dict(C, cache=C["cache"].clone()) for w, C in self.caches.items()}
+        return r
+
+    def run(self, keep_scores: bool = False, hook=None):
+        """One decode token through every layer (enqueued on the current stream)."""
+        call = _caller(hook)
+        latest = {}
+        any_cache = next(iter(self.caches.values()))
+        K = self.wl.K
+        for L in self.layers:
+            mode = L["mode"]
+            if mode == "swa":
+                call("sparse_attn_decode", lib.sparse_attn_decode, any_cache["cache"], L["q"], self.no_topk,
+                     any_cache["block_table"], L["swa"], L["swa_len"], self.scale, L["out"], L["lse"], self.ws_attn)
+                continue
+            C = self.caches[L["src"]]
+            if mode == "full":
+                lat, key, slot = C["new"]
+                call("fp4_cache_write", lib.fp4_cache_write, C["cache"], lat, key, slot)
+            if mode == "reindex" and C["pooled"]:
+                call("index_topk_pool", lib.index_topk_pool, C["cache"], L["q_idx"], L["w"], C["n_visible"],
+                     C["pool"], C["block_table"], C["scores_pool"], K, L["topk"], C["ws_topk_pool"])
+                if keep_scores:
+                    L["scores"] = C["scores_pool"].clone()
+                latest[L["src"]] = L["topk"]
+            elif mode in ("full", "reindex"):
+                call("index_topk", lib.index_topk, C["cache"], L["q_idx"], L["w"], C["n_visible"],
+                     C["block_table"], C["scores"], K, L["topk"], C["ws_topk"])
+                if keep_scores:
+                    L["scores"] = C["scores"].clone()
+                latest[L["src"]] = L["topk"]
+                if mode == "full" and C["pooled"]:
+                    call("index_pool_build", lib.index_pool_build, C["scores"], C["n_visible"], self.wl.npool,
+                         C["pool"], C["ws_pool"])
+                    if keep_scores:
+                        L["pool"] = C["pool"].clone()
+            if L["src"] not in latest:
+                raise ValueError("a reuse layer needs an earlier full or reindex layer on its cache")
+            call("sparse_attn_decode", lib.sparse_attn_decode, C["cache"], L["q"], latest[L["src"]],
+                 C["block_table"], L["swa"], L["swa_len"], self.scale, L["out"], L["lse"], self.ws_attn)
+
+
 class PrefillStep:
     """Device state for a prefill chunk: a cached prefix, then one chunk step that
     writes the chunk's entries, scores every query over its causally visible
@@ -202,6 +313,9 @@ class PrefillStep:
         self.chunk_latent = to_device_bits(lat[n:n + nc], self.device)
         self.chunk_key = to_device_bits(key[n:n + nc], self.device)
         self.chunk_slot = torch.from_numpy(slots[n:n + nc]).to(self.device)
+
+    def cache_bytes(self) -> int:
+        return self.cache.nbytes()
 
     def replica(self) -> "PrefillStep":
         """The same chunk step over a copy of the cache (other buffers shared)."""

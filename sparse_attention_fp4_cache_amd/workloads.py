@@ -194,6 +194,77 @@ def ragged_contexts(cfg_id: int, B: int, lo: int, hi: int, seed: int = 0) -> tup
     return tuple(int(c) for c in rng.integers(lo, hi + 1, size=B))
 
 
+@dataclasses.dataclass(frozen=True)
+class ScheduleWorkload:
+    """One decode token through a whole layer schedule with several caches.
+
+    modes[l] is "swa" (attention over the layer's own window only), "full" (writes
+    its own cache, scores and selects), "reindex" (scores and selects on the cache
+    of the latest Full layer) or "reuse" (attends with the latest indices on that
+    cache).  m[l] is the tokens per entry of the cache layer l reads.  Each Full
+    layer's cache has its own seeded rows (cache_workload); the query-side inputs of
+    every layer come from query_workload().layer_inputs(l).  npool > 0: Reindex
+    layers score and select inside the candidate pool built from their Full
+    layer's scores.
+    """
+
+    name: str
+    cfg_id: int
+    ctx: int
+    H: int
+    Hi: int
+    K: int
+    W: int = 128
+    modes: tuple = ()
+    m: tuple = ()
+    npool: int = 0
+    seed: int = 0
+    kind: str = "schedule"
+    B: int = 1
+
+    @property
+    def layers(self) -> tuple:
+        return self.modes
+
+    def writers(self) -> list:
+        return [i for i, md in enumerate(self.modes) if md == "full"]
+
+    def source(self, layer: int):
+        """The Full layer whose cache `layer` reads (None for a window-only layer)."""
+        if self.modes[layer] == "swa":
+            return None
+        w = [i for i in self.writers() if i <= layer]
+        if not w:
+            raise ValueError(f"layer {layer} reads a cache before any Full layer")
+        return w[-1]
+
+    def cache_workload(self, writer: int) -> Workload:
+        """The single-cache workload that lays out and seeds the cache of Full layer
+        `writer` (config id 100 * cfg_id + writer)."""
+        return Workload(f"{self.name}_cache{writer}", 100 * self.cfg_id + writer, "decode", B=1, ctx=(self.ctx,),
+                        H=self.H, Hi=self.Hi, K=self.K, W=self.W, m=self.m[writer], layers=("full",), seed=self.seed)
+
+    def query_workload(self) -> Workload:
+        """Per-layer query-side inputs (q, q_idx, w, window), keyed by layer."""
+        return Workload(self.name, self.cfg_id, "decode", B=1, ctx=(self.ctx,), H=self.H, Hi=self.Hi, K=self.K,
+                        W=self.W, m=2, layers=self.modes, seed=self.seed)
+
+
+def published_schedule():
+    """The published 40-layer allocation ("DeepSeek-V4.1-Flash, expliqué pas à pas",
+    CSA2 mode table; "Résumé exécutif", CSA2 section): encoder layers 0-1 window
+    only, then 3 groups of [Full + 5 Reuse] with m = 2 (writers 2, 8, 14); decoder 5
+    groups of 4 with m = 1: [Full + 3 Reuse] (writer 20), then 4 x [Reindex + 3 Reuse].
+    Returns (modes, m) per layer."""
+    modes = ["swa", "swa"] + ["full"] + ["reuse"] * 5 + ["full"] + ["reuse"] * 5 + ["full"] + ["reuse"] * 5
+    m = [0, 0] + [2] * 18
+    modes += ["full"] + ["reuse"] * 3
+    for _ in range(4):
+        modes += ["reindex"] + ["reuse"] * 3
+    m += [1] * 20
+    return tuple(modes), tuple(m)
+
+
 C4_LAYERS = ("full", "reuse", "reindex", "reuse", "reindex", "reuse", "reindex", "reuse", "reindex", "reuse")
 
 WORKLOADS = {
@@ -210,6 +281,11 @@ WORKLOADS = {
                                    chunk=4096),
     # bounded replay of the last 128 tokens of a 1,048,576-token prompt: every query
     # has its causal top-K over the whole cache; the window restarts at the replay
+    # one token through all 40 layers at 1,048,576 tokens: three m = 2 encoder
+    # caches (524,288 entries each) and the m = 1 decoder cache (1,048,576 entries),
+    # 0.87 GiB in all; the decoder's Reindex layers select inside 2048-block pools
+    "decode_1m_schedule": ScheduleWorkload("decode_1m_schedule", 7, 1048576, H=64, Hi=64, K=2048,
+                                           modes=published_schedule()[0], m=published_schedule()[1], npool=2048),
     "replay_128_1m": Workload("replay_128_1m", 6, "prefill", B=1, ctx=(1048576 - 128,), H=64, Hi=64, K=2048,
                               chunk=128, swa_replay=True),
 }

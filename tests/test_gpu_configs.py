@@ -17,7 +17,7 @@ import torch
 
 import oracle
 from sparse_attention_fp4_cache_amd import lib
-from sparse_attention_fp4_cache_amd.step import DecodeStep, PrefillStep
+from sparse_attention_fp4_cache_amd.step import DecodeStep, PrefillStep, ScheduleDecodeStep
 from sparse_attention_fp4_cache_amd.workloads import WORKLOADS
 from _helpers import attn_close, say
 
@@ -142,6 +142,62 @@ def test_config_decode_1m_10layer_pool_and_graph_replay():
     graph_replays_equal_eager(st)
 
 
+@pytest.mark.timeout(1500)
+def test_config_decode_1m_whole_schedule():
+    """One token through all 40 layers: three m = 2 encoder caches, the m = 1 decoder
+    cache (1,048,576 entries), window-only layers, pooled decoder Reindex layers."""
+    sw = WORKLOADS["decode_1m_schedule"]
+    say(f"case: {sw.name} ({len(sw.modes)} layers, writers {sw.writers()}, pool {sw.npool} blocks)")
+    st = ScheduleDecodeStep(sw, "cuda")
+    st.build_cache()
+    st.run(keep_scores=True)
+    torch.cuda.synchronize()
+    qw = sw.query_workload()
+    refs = {}
+    for w in sw.writers():
+        cw = sw.cache_workload(w)
+        o = oracle_cache(cw)
+        C = st.caches[w]
+        for name in ("main_codes", "main_scales", "idx_codes", "idx_scales"):
+            nbad = int(np.count_nonzero(getattr(C["cache"], name).cpu().numpy() != getattr(o, name)))
+            assert nbad == 0, f"cache of layer {w}: {name} differs in {nbad} bytes"
+        refs[w] = (o, cw.block_table(), cw.n_visible())
+        say(f"  cache of layer {w} (m = {cw.m}, {int(cw.n_entries[0])} entries): bytes equal")
+    latest, pools = {}, {}
+    for li, L in enumerate(st.layers):
+        d = qw.layer_inputs(li)
+        mode, src = L["mode"], L["src"]
+        if mode == "swa":
+            o, bt, nv = next(iter(refs.values()))
+            ro, rl = oracle.sparse_attn_decode(o, d["q"], np.zeros((1, 0), np.int32), bt, d["swa"], d["swa_len"],
+                                               st.scale)
+            attn_close(L["out"].cpu().numpy(), ro, L["lse"].cpu().numpy(), rl, f"layer {li} (window only)")
+            continue
+        o, bt, nv = refs[src]
+        if mode == "reindex" and sw.npool > 0:
+            ref_ps, not_fp32, _ = oracle.index_score_pool(o, d["q_idx"], d["w"], nv, pools[src], bt)
+            assert not_fp32 == 0
+            npv = np.count_nonzero(~np.isnan(ref_ps), axis=1)
+            scores_equal(L["scores"].cpu().numpy(), ref_ps, npv, f"layer {li} pool scores")
+            latest[src] = oracle.topk_pool(ref_ps, pools[src], nv, sw.K)
+            topk_equal(L["topk"].cpu().numpy(), latest[src], f"layer {li} pool top-k")
+            say(f"  layer {li} (reindex over the pool): scores and top-k bit-exact")
+        elif mode in ("full", "reindex"):
+            ref_s, not_fp32, _ = oracle.index_score(o, d["q_idx"], d["w"], nv, bt, ld=st.caches[src]["ld"])
+            assert not_fp32 == 0
+            scores_equal(L["scores"].cpu().numpy(), ref_s, nv, f"layer {li} scores")
+            latest[src] = oracle.topk_select(ref_s, nv, sw.K)
+            topk_equal(L["topk"].cpu().numpy(), latest[src], f"layer {li} top-k")
+            say(f"  layer {li} ({mode}): scores and top-k bit-exact")
+            if mode == "full" and st.caches[src]["pooled"]:
+                pools[src] = oracle.pool_build(ref_s, nv, sw.npool)
+                topk_equal(L["pool"].cpu().numpy(), pools[src], f"layer {li} candidate pool")
+        ro, rl = oracle.sparse_attn_decode(o, d["q"], latest[src], bt, d["swa"], d["swa_len"], st.scale)
+        attn_close(L["out"].cpu().numpy(), ro, L["lse"].cpu().numpy(), rl, f"layer {li} ({mode}) attention")
+    say("  all 40 layers' attention within tolerance")
+    graph_replays_equal_eager(st)
+
+
 def graph_replays_equal_eager(st):
     # the benchmark replays the step as one HIP graph: every replay must equal the
     # eager step bit for bit, with eager work and synchronisations in between
@@ -160,8 +216,9 @@ def graph_replays_equal_eager(st):
             L["lse"].zero_()
             if "topk" in L:
                 L["topk"].fill_(-7)
-        if st.npool > 0:
-            st.pool.fill_(-7)
+        for P in ([st.pool] if getattr(st, "npool", 0) > 0 else
+                  [C["pool"] for C in getattr(st, "caches", {}).values() if C.get("pooled")]):
+            P.fill_(-7)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()

@@ -75,6 +75,9 @@ def lib():
                                                 ctypes.c_float, _I32, _P, _P]
         L.oracle_sparse_attn_prefill_chunk.argtypes = [_P, _P, _P, _I32, _P, _I32, _P, _I32, _I32, _I32, _P,
                                                        _I32, _I32, ctypes.c_float, _P, _I32, _P, _P]
+        L.oracle_swa_fp8_quant.argtypes = [_P, _I64, _P, _P]
+        L.oracle_swa_fp8_dequant.argtypes = [_P, _P, _I64, _P]
+        L.oracle_swa_fp8_dequant.restype = _I64
         L.oracle_entry_bytes.argtypes = [_I64, _I64]
         L.oracle_entry_bytes.restype = _I64
         L.oracle_bits_per_channel.argtypes = [_I64]
@@ -284,6 +287,46 @@ def sparse_attn_prefill_chunk(cache: Cache, q: np.ndarray, topk_idx: np.ndarray,
 
 
 # -------------------------------------------------------------- footprint --
+def swa_fp8_quant(x_bf16: np.ndarray):
+    """Window rows [..., 512] bf16 bits -> (E4M3FN codes [..., 512], E8M0 scales [...])."""
+    x = _arr(x_bf16, np.uint16)
+    assert x.shape[-1] == LATENT_DIM
+    rows = x.size // LATENT_DIM
+    codes = np.zeros(x.shape, np.uint8)
+    scales = np.zeros(x.shape[:-1], np.uint8)
+    lib().oracle_swa_fp8_quant(_ptr(x), rows, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def swa_fp8_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """FP8 window rows -> bf16 bits of their exact values (raises if bf16 cannot hold
+    one exactly)."""
+    codes = _arr(codes, np.uint8)
+    scales = _arr(scales, np.uint8)
+    assert codes.shape[-1] == LATENT_DIM and codes.shape[:-1] == scales.shape
+    out = np.zeros(codes.shape, np.uint16)
+    bad = lib().oracle_swa_fp8_dequant(_ptr(codes), _ptr(scales), scales.size, _ptr(out))
+    if bad:
+        raise ValueError(f"{bad} FP8 window values are not exact in bf16")
+    return out
+
+
+def sparse_attn_decode_fp8win(cache: Cache, q: np.ndarray, topk_idx: np.ndarray, block_table: np.ndarray,
+                              swa_codes: np.ndarray, swa_scales: np.ndarray, swa_len: np.ndarray,
+                              softmax_scale: float):
+    """Decode attention with an FP8 window: the window rows' exact values, then the
+    same attention as sparse_attn_decode."""
+    return sparse_attn_decode(cache, q, topk_idx, block_table, swa_fp8_dequant(swa_codes, swa_scales), swa_len,
+                              softmax_scale)
+
+
+def sparse_attn_prefill_chunk_fp8win(cache: Cache, q: np.ndarray, topk_idx: np.ndarray, block_table: np.ndarray,
+                                     swa_codes: np.ndarray, swa_scales: np.ndarray, swa_first_valid: int,
+                                     window: int, softmax_scale: float, which: np.ndarray | None = None):
+    return sparse_attn_prefill_chunk(cache, q, topk_idx, block_table, swa_fp8_dequant(swa_codes, swa_scales),
+                                     swa_first_valid, window, softmax_scale, which=which)
+
+
 def entry_bytes(dim: int, block: int) -> int:
     return int(lib().oracle_entry_bytes(dim, block))
 

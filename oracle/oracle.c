@@ -34,6 +34,10 @@
  *     by index, -1 padded when fewer than k entries are visible.
  *   - attention: every selected latent row and every window row is both key and
  *     value for all heads; one softmax over the union; fp64 arithmetic.
+ *   - FP8 window ([EXP] FP4 KV cache section: the SWA KV stays in FP8): E4M3FN codes
+ *     and one E8M0 scale per 512-channel window row, X = the smallest power of two
+ *     with amax <= 448 X (no code saturates); code = E4M3FN nearest to x / X, ties
+ *     to the even byte, sign copied; amax = 0 -> X = 2^-127.
  */
 #include <math.h>
 #include <stdint.h>
@@ -514,6 +518,62 @@ void oracle_sparse_attn_prefill_chunk(const uint8_t* main_codes, const uint8_t* 
                 out + (int64_t)i * H * LATENT_DIM, lse + (int64_t)i * H);
     free(X);
   }
+}
+
+/* ------------------------------------------------------------- FP8 window -- */
+
+/* Non-negative E4M3FN byte nearest to a (0 <= a <= 448), ties to the even byte,
+ * searched over every finite non-negative byte (values and differences exact in
+ * double: a has at most 8 significant bits, each candidate 4). */
+static uint8_t e4m3_nearest(double a) {
+  uint8_t best = 0;
+  double bestd = INFINITY;
+  for (int b = 0; b <= 0x7E; ++b) {
+    double d = fabs(oracle_e4m3_value((uint8_t)b) - a);
+    if (d < bestd || (d == bestd && !(b & 1) && (best & 1))) {
+      bestd = d;
+      best = (uint8_t)b;
+    }
+  }
+  return best;
+}
+
+/* Window rows in FP8 ([EXP] FP4 KV cache section: the window KV is kept in FP8 as it
+ * is the more quantisation-sensitive part; the format below is the reading stated in
+ * the header).  rows x [rows][512] bf16 -> codes [rows][512] E4M3FN, scales [rows]
+ * E8M0. */
+void oracle_swa_fp8_quant(const uint16_t* x, int64_t rows, uint8_t* codes, uint8_t* scales) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint16_t* xr = x + r * LATENT_DIM;
+    double amax = 0.0;
+    for (int c = 0; c < LATENT_DIM; ++c) amax = fmax(amax, fabs(oracle_bf16_value(xr[c])));
+    int e = -127;
+    while (ldexp(448.0, e) < amax) ++e;
+    scales[r] = (uint8_t)(e + 127);
+    for (int c = 0; c < LATENT_DIM; ++c) {
+      double v = oracle_bf16_value(xr[c]);
+      codes[r * LATENT_DIM + c] = (uint8_t)((signbit(v) ? 0x80 : 0) | e4m3_nearest(ldexp(fabs(v), -e)));
+    }
+  }
+}
+
+/* FP8 window rows -> bf16 bit patterns of their exact values (E4M3FN x E8M0).
+ * Returns the number of values that bf16 cannot hold exactly (0 for any row whose
+ * scale is at least 2^-124). */
+int64_t oracle_swa_fp8_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows, uint16_t* out) {
+  int64_t bad = 0;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int c = 0; c < LATENT_DIM; ++c) {
+      double v = oracle_e4m3_value(codes[r * LATENT_DIM + c]) * oracle_e8m0_value(scales[r]);
+      float f = (float)v;
+      uint32_t u;
+      memcpy(&u, &f, 4);
+      uint16_t b = (uint16_t)(u >> 16);
+      if ((double)f != v || oracle_bf16_value(b) != v) ++bad;
+      out[r * LATENT_DIM + c] = b;
+    }
+  return bad;
 }
 
 /* -------------------------------------------------------------- footprint -- */

@@ -55,6 +55,9 @@ MUTATIONS = [
     ("pool scores one entry past the visible end", "j >= n_visible[q]) continue;\n      int64_t s = slot_of",
      "j > n_visible[q]) continue;\n      int64_t s = slot_of"),
     ("pool top-k reports pool positions", "all[m].j = j;", "all[m].j = p;"),
+    ("fp8 window scale twice too large", "while (ldexp(448.0, e) < amax) ++e;", "while (ldexp(224.0, e) < amax) ++e;"),
+    ("fp8 window ties to the odd byte", "(d == bestd && !(b & 1) && (best & 1))", "(d == bestd)"),
+    ("fp8 window drops the sign", "(uint8_t)((signbit(v) ? 0x80 : 0) | e4m3_nearest(", "(uint8_t)((0) | e4m3_nearest("),
 ]
 
 
@@ -76,7 +79,8 @@ def test_pins_catch_planted_mistake(tmp_path, label, old, new):
     so = _build_mutant(str(tmp_path), old, new)
     env = dict(os.environ, CSA2_ORACLE_LIB=so, OMP_NUM_THREADS="4")
     r = subprocess.run([sys.executable, "-m", "pytest", os.path.join(HERE, "test_oracle_pins.py"),
-                        os.path.join(HERE, "test_oracle_pool.py"), "-x", "-q",
+                        os.path.join(HERE, "test_oracle_pool.py"), os.path.join(HERE, "test_oracle_fp8win.py"),
+                        "-x", "-q",
                         "-p", "no:cacheprovider", "-m", "not gpu"], cwd=ROOT, env=env, capture_output=True,
                        text=True, timeout=600)
     assert r.returncode == 1, f"mistake '{label}' was not caught by any pin:\n{r.stdout[-1500:]}"

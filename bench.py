@@ -360,9 +360,15 @@ def main():
                                            for s in steps for L in idx_layers])[0] * 1e3
         calls_us["topk_select"] = burst_ms([functools.partial(lib.topk_select, st.scores, st.n_visible, wl.K,
                                                               L["topk"], st.ws_topk) for L in idx_layers])[0] * 1e3
-        calls_us["sparse_attn_decode"] = burst_ms([functools.partial(
-            lib.sparse_attn_decode, s.cache, L["q"], st.layers[0]["topk"], s.block_table, L["swa"], L["swa_len"],
-            st.scale, L["out"], L["lse"], s.ws_attn) for s in steps for L in st.layers])[0] * 1e3
+        if wl.fp8_window:
+            calls_us["sparse_attn_decode_fp8win"] = burst_ms([functools.partial(
+                lib.sparse_attn_decode_fp8win, s.cache, L["q"], st.layers[0]["topk"], s.block_table, L["swa8"],
+                L["swa8_scale"], L["swa_len"], st.scale, L["out"], L["lse"], s.ws_attn)
+                for s in steps for L in st.layers])[0] * 1e3
+        else:
+            calls_us["sparse_attn_decode"] = burst_ms([functools.partial(
+                lib.sparse_attn_decode, s.cache, L["q"], st.layers[0]["topk"], s.block_table, L["swa"], L["swa_len"],
+                st.scale, L["out"], L["lse"], s.ws_attn) for s in steps for L in st.layers])[0] * 1e3
         idx_bytes = sum(int(x) for x in wl.n_entries) * IDX_ENTRY_BYTES
         tokens = wl.B
     else:

@@ -234,6 +234,37 @@ int sparse_attn_prefill_chunk(const csa2_fp4_cache* cache, const uint16_t* q, in
                               const uint16_t* swa, int32_t swa_first_valid, int32_t window, float softmax_scale,
                               float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* FP8 window.  "DeepSeek-V4.1-Flash, expliqué pas à pas", FP4 KV cache section: the
+ * sliding-window KV stays in FP8 because it is more sensitive to quantisation.  The
+ * pages give no format; the one used here: E4M3FN codes and one E8M0 scale per
+ * 512-channel row, X = the smallest power of two with amax <= 448 X (no code
+ * saturates), code = the E4M3FN value nearest to x / X (ties to even, sign copied);
+ * an all-zero row gets X = 2^-127.  Every dequantised value is exact in bf16, so the
+ * attention over an FP8 window equals the attention over the bf16 rows holding those
+ * values.
+ *
+ * swa_fp8_write -- quantise n window rows.
+ *   rows bf16 [n][512]; codes u8 [n][512] out; scales u8 [n] out (E8M0 byte e + 127).
+ *   Rows are independent (any n >= 0).  NULL pointers with n > 0: CSA2_ERR_NULL. */
+int swa_fp8_write(const uint16_t* rows, int64_t n, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+/* sparse_attn_decode_fp8win / sparse_attn_prefill_chunk_fp8win -- the attention calls
+ * above with the window as FP8 rows: swa_codes u8 and swa_scales u8 in place of swa,
+ * laid out as swa's rows ([B][window] rows for decode, [window-1+T] rows for the
+ * prefill chunk).  Everything else, the workspaces included
+ * (sparse_attn_decode_workspace_size, sparse_attn_prefill_chunk_workspace_size), is as
+ * for the bf16 calls.  window > 0 with a NULL codes or scales pointer: CSA2_ERR_NULL. */
+int sparse_attn_decode_fp8win(const csa2_fp4_cache* cache, const uint16_t* q, int32_t H, const int32_t* topk_idx,
+                              int32_t k, const int32_t* block_table, int32_t max_pages, const uint8_t* swa_codes,
+                              const uint8_t* swa_scales, const int32_t* swa_len, int32_t window, float softmax_scale,
+                              int32_t B, float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+int sparse_attn_prefill_chunk_fp8win(const csa2_fp4_cache* cache, const uint16_t* q, int32_t H,
+                                     const int32_t* topk_idx, int32_t k, const int32_t* block_table,
+                                     int32_t max_pages, int64_t chunk_start, int32_t T, const uint8_t* swa_codes,
+                                     const uint8_t* swa_scales, int32_t swa_first_valid, int32_t window,
+                                     float softmax_scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -63,7 +63,9 @@ struct AttnArgs {
   int k;
   const int32_t* block_table;
   int max_pages;
-  const uint16_t* swa;
+  const uint16_t* swa;       // bf16 window rows [.][512], or
+  const uint8_t* swa8;       // FP8 window rows: E4M3FN codes [.][512] ...
+  const uint8_t* swa8_scale; // ... and one E8M0 scale per row
   const int32_t* swa_len;    // decode: valid window rows per query
   int window;
   int prefill;               // 1: window rows of query i are swa rows i .. i+window-1
@@ -122,10 +124,32 @@ CSA2_DEV int xchunk(int c) { return c ^ ((c >> 3) & 7); }
 struct TileRegs {
   uint4 code[2];  // FP4 entry: 32 code bytes (64 channels)
   uint32_t sc;    // FP4 entry: the E4M3 scale bytes of channels 16j .. 16j+15, j = 0..3
-  uint4 win[8];   // window row: 64 bf16
+  uint4 win[8];   // window row: 64 bf16 (FP8 window: 64 code bytes in win[0..3])
+  uint32_t wsc;   // FP8 window row: its E8M0 scale byte
   int kind;       // 1: FP4 entry, 2: window row, 0: no row
 };
 
+// 8 E4M3FN codes (two dwords) times a power-of-two scale as 8 bf16, exact (4
+// significant bits times 2^e), via V_CVT_PK_F32_FP8 (OCP E4M3FN on gfx950).
+CSA2_DEV uint4 dequant_fp8x8(uint32_t lo, uint32_t hi, float X) {
+  const v2f a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+  const v2f c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+  return make_uint4(pack_bf16(a[0] * X, a[1] * X), pack_bf16(b[0] * X, b[1] * X), pack_bf16(c[0] * X, c[1] * X),
+                    pack_bf16(d[0] * X, d[1] * X));
+}
+
+// Channels 8i .. 8i+7 of a thread's window share as bf16: loaded bf16, or dequantised
+// from the FP8 codes (byte 8i of the share is in win[i / 2]).
+template <bool W8>
+CSA2_DEV uint4 win_chunk(const uint4* win, int i, float X) {
+  if (!W8) return win[i];
+  const uint4 v = win[i >> 1];
+  return (i & 1) ? dequant_fp8x8(v.z, v.w, X) : dequant_fp8x8(v.x, v.y, X);
+}
+
+CSA2_DEV float e8m0_scale(uint32_t u) { return ldexpf(1.0f, (int)(u & 0xFFu) - 127); }
+
+template <bool W8>
 CSA2_DEV void issue_tile(const AttnArgs& a, const int* src_rows, int tid, int tile_row0, bool has_main, bool has_win,
                          TileRegs& t) {
   const int row = tid >> 3, c8 = tid & 7;
@@ -141,7 +165,16 @@ CSA2_DEV void issue_tile(const AttnArgs& a, const int* src_rows, int tid, int ti
     t.code[0] = t.code[1] = make_uint4(0u, 0u, 0u, 0u);
     t.sc = 0u;
   }
-  if (has_win) {
+  t.wsc = 0u;
+  if (has_win && W8) {
+    const int64_t wrow = src <= -2 ? (int64_t)(-2 - src) : 0;
+    const uint4* wp = reinterpret_cast<const uint4*>(a.swa8 + wrow * kLatentDim) + 4 * c8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t.win[i] = wp[i];
+#pragma unroll
+    for (int i = 4; i < 8; ++i) t.win[i] = make_uint4(0u, 0u, 0u, 0u);
+    t.wsc = a.swa8_scale[wrow];
+  } else if (has_win) {
     const int64_t wrow = src <= -2 ? (int64_t)(-2 - src) : 0;
     const uint4* wp = reinterpret_cast<const uint4*>(a.swa + wrow * kLatentDim) + 8 * c8;
 #pragma unroll
@@ -169,10 +202,12 @@ CSA2_DEV uint4 dequant8(uint32_t c, float s) {
 // Branch-free within a tile: E4M3 scale via V_CVT_F32_FP8 (OCP E4M3FN on gfx950),
 // E2M1 pairs via V_CVT_SCALEF32_PK_F32_FP4 with a unit scale, product exact in
 // fp32 and in bf16.
+template <bool W8>
 CSA2_DEV void store_tile(HalfSmem& sm, int tid, const TileRegs& t, bool has_main) {
   const int row = tid >> 3, c8 = tid & 7;
   uint4* xr = reinterpret_cast<uint4*>(sm.x + row * kXStride);
   const uint32_t wmask = t.kind == 2 ? ~0u : 0u;
+  const float X = W8 ? e8m0_scale(t.wsc) : 1.0f;
   if (has_main) {
     const uint32_t mmask = t.kind == 1 ? ~0u : 0u;
     const uint32_t cw[8] = {t.code[0].x, t.code[0].y, t.code[0].z, t.code[0].w,
@@ -181,10 +216,10 @@ CSA2_DEV void store_tile(HalfSmem& sm, int tid, const TileRegs& t, bool has_main
                          __builtin_amdgcn_cvt_f32_fp8((int)t.sc, 2), __builtin_amdgcn_cvt_f32_fp8((int)t.sc, 3)};
 #pragma unroll
     for (int i = 0; i < 8; ++i)  // chunk i (8 channels) of this thread's 64 uses scale byte i / 2
-      xr[xchunk(8 * c8 + i)] = or4(and4(dequant8(cw[i], sc[i >> 1]), mmask), and4(t.win[i], wmask));
+      xr[xchunk(8 * c8 + i)] = or4(and4(dequant8(cw[i], sc[i >> 1]), mmask), and4(win_chunk<W8>(t.win, i, X), wmask));
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xr[xchunk(8 * c8 + i)] = and4(t.win[i], wmask);
+    for (int i = 0; i < 8; ++i) xr[xchunk(8 * c8 + i)] = and4(win_chunk<W8>(t.win, i, X), wmask);
   }
 }
 
@@ -194,6 +229,7 @@ CSA2_DEV bf16x8 as_bf16x8(uint4 v) {
   return r;
 }
 
+template <bool W8>
 __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a) {
   __shared__ AttnSmem smem;
   const int half = threadIdx.x >> 8;
@@ -250,13 +286,13 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a) {
   auto has_main = [&](int rl0) { return r_begin + seg0 + rl0 < a.k; };
   auto has_win = [&](int rl0) { return a.window > 0 && r_begin + seg0 + rl0 + kRT > a.k; };
   TileRegs cur;
-  issue_tile(a, smem.src, tid, half * kRT, has_main(half * kRT), has_win(half * kRT), cur);
+  issue_tile<W8>(a, smem.src, tid, half * kRT, has_main(half * kRT), has_win(half * kRT), cur);
   for (int pair0 = 0; pair0 < seg_n; pair0 += 2 * kRT) {
     const int row0 = pair0 + half * kRT;  // may lie past seg_n: an empty tile
     lds_barrier();  // previous tile fully consumed
-    store_tile(sm, tid, cur, has_main(row0));
+    store_tile<W8>(sm, tid, cur, has_main(row0));
     const int next0 = row0 + 2 * kRT;  // inside the padded sources whenever another pair follows
-    if (pair0 + 2 * kRT < seg_n) issue_tile(a, smem.src, tid, next0, has_main(next0), has_win(next0), cur);
+    if (pair0 + 2 * kRT < seg_n) issue_tile<W8>(a, smem.src, tid, next0, has_main(next0), has_win(next0), cur);
     lds_barrier();
     // ---- partial logits over this wavefront's 128 channels, two 16-row M-tiles
     v4f s[2];
@@ -411,10 +447,12 @@ static_assert(sizeof(WideSmem) <= 160 * 1024, "attention LDS exceeds 160 KB");
 struct WideRegs {
   uint4 code;     // FP4 entry: 16 code bytes (32 channels)
   uint32_t sc;    // FP4 entry: the two E4M3 scale bytes of those channels
-  uint4 win[4];   // window row: 32 bf16
+  uint4 win[4];   // window row: 32 bf16 (FP8 window: 32 code bytes in win[0..1])
+  uint32_t wsc;   // FP8 window row: its E8M0 scale byte
   int kind;       // 1: FP4 entry, 2: window row, 0: no row
 };
 
+template <bool W8>
 CSA2_DEV void issue_wide(const AttnArgs& a, const int* src_rows, int tid, int tile_row0, bool has_main, bool has_win,
                          WideRegs& t) {
   const int row = tid >> 4, c16 = tid & 15;
@@ -428,7 +466,15 @@ CSA2_DEV void issue_wide(const AttnArgs& a, const int* src_rows, int tid, int ti
     t.code = make_uint4(0u, 0u, 0u, 0u);
     t.sc = 0u;
   }
-  if (has_win) {
+  t.wsc = 0u;
+  if (has_win && W8) {
+    const int64_t wrow = src <= -2 ? (int64_t)(-2 - src) : 0;
+    const uint4* wp = reinterpret_cast<const uint4*>(a.swa8 + wrow * kLatentDim) + 2 * c16;
+    t.win[0] = wp[0];
+    t.win[1] = wp[1];
+    t.win[2] = t.win[3] = make_uint4(0u, 0u, 0u, 0u);
+    t.wsc = a.swa8_scale[wrow];
+  } else if (has_win) {
     const int64_t wrow = src <= -2 ? (int64_t)(-2 - src) : 0;
     const uint4* wp = reinterpret_cast<const uint4*>(a.swa + wrow * kLatentDim) + 4 * c16;
 #pragma unroll
@@ -439,10 +485,12 @@ CSA2_DEV void issue_wide(const AttnArgs& a, const int* src_rows, int tid, int ti
   }
 }
 
+template <bool W8>
 CSA2_DEV void store_wide(uint16_t* x, int tid, const WideRegs& t, bool has_main, bool has_win) {
   const int row = tid >> 4, c16 = tid & 15;
   uint4* xr = reinterpret_cast<uint4*>(x + row * kXStride);
   const uint32_t wmask = t.kind == 2 ? ~0u : 0u;
+  const float X = W8 ? e8m0_scale(t.wsc) : 1.0f;
   if (has_main && !has_win) {
     // FP4 rows only: a row that is not an entry dequantises code 0 with scale 0 (the
     // loaded bytes of its stand-in slot are not used), which is +0 in every channel
@@ -458,13 +506,15 @@ CSA2_DEV void store_wide(uint16_t* x, int tid, const WideRegs& t, bool has_main,
     const uint32_t cw[4] = {t.code.x, t.code.y, t.code.z, t.code.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i)  // chunk i (8 channels) of this thread's 32 uses scale byte i / 2
-      xr[xchunk(4 * c16 + i)] = or4(and4(dequant8(cw[i], i < 2 ? s0 : s1), mmask), and4(t.win[i], wmask));
+      xr[xchunk(4 * c16 + i)] =
+          or4(and4(dequant8(cw[i], i < 2 ? s0 : s1), mmask), and4(win_chunk<W8>(t.win, i, X), wmask));
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xr[xchunk(4 * c16 + i)] = and4(t.win[i], wmask);
+    for (int i = 0; i < 4; ++i) xr[xchunk(4 * c16 + i)] = and4(win_chunk<W8>(t.win, i, X), wmask);
   }
 }
 
+template <bool W8>
 __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) {
   __shared__ WideSmem smem;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -516,9 +566,9 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
   // buffer written in iteration t was last read in iteration t-2, and red[t%2] in
   // iteration t-2, both before the barrier of iteration t-1.
   WideRegs cur;
-  issue_wide(a, smem.src, tid, 0, has_main(0), has_win(0), cur);
-  store_wide(smem.x[0], tid, cur, has_main(0), has_win(0));
-  if (ntiles > 1) issue_wide(a, smem.src, tid, kRT, has_main(kRT), has_win(kRT), cur);
+  issue_wide<W8>(a, smem.src, tid, 0, has_main(0), has_win(0), cur);
+  store_wide<W8>(smem.x[0], tid, cur, has_main(0), has_win(0));
+  if (ntiles > 1) issue_wide<W8>(a, smem.src, tid, kRT, has_main(kRT), has_win(kRT), cur);
   lds_barrier();
   for (int t = 0; t < ntiles; ++t) {
     const int row0 = t * kRT;
@@ -537,9 +587,9 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
 #pragma unroll
       for (int r = 0; r < 4; ++r) red[hg][kh][tt][r][lane] = sl[r];
     }
-    if (t + 1 < ntiles) store_wide(smem.x[(t + 1) % 3], tid, cur, has_main(row0 + kRT), has_win(row0 + kRT));
+    if (t + 1 < ntiles) store_wide<W8>(smem.x[(t + 1) % 3], tid, cur, has_main(row0 + kRT), has_win(row0 + kRT));
     if (t + 2 < ntiles)
-      issue_wide(a, smem.src, tid, row0 + 2 * kRT, has_main(row0 + 2 * kRT), has_win(row0 + 2 * kRT), cur);
+      issue_wide<W8>(a, smem.src, tid, row0 + 2 * kRT, has_main(row0 + 2 * kRT), has_win(row0 + 2 * kRT), cur);
     lds_barrier();
     float z[2][4];
     float tmax = -INFINITY;
@@ -702,13 +752,16 @@ static int run_attention(AttnArgs a, void* ws, size_t ws_bytes, hipStream_t stre
     a.part_o = reinterpret_cast<float*>(ws);
     a.part_ml = a.part_o + (size_t)a.nq * a.nsplit * a.H * kLatentDim;
   }
+  const bool w8 = a.swa8 != nullptr;
   if (a.nsplit == 1 && a.H % kWideHeads == 0) {  // many queries: a workgroup takes 64 heads
-    hipLaunchKernelGGL(sparse_attn_wide_kernel, dim3((unsigned)a.nq, (unsigned)(a.H / kWideHeads)), dim3(kThreads), 0,
-                       stream, a);
+    const dim3 grid((unsigned)a.nq, (unsigned)(a.H / kWideHeads));
+    if (w8) hipLaunchKernelGGL(sparse_attn_wide_kernel<true>, grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL(sparse_attn_wide_kernel<false>, grid, dim3(kThreads), 0, stream, a);
     return launch_status();
   }
   const dim3 grid((unsigned)a.nsplit, (unsigned)(a.H / 16), (unsigned)a.nq);
-  hipLaunchKernelGGL(sparse_attn_kernel, grid, dim3(kThreads), 0, stream, a);
+  if (w8) hipLaunchKernelGGL(sparse_attn_kernel<true>, grid, dim3(kThreads), 0, stream, a);
+  else hipLaunchKernelGGL(sparse_attn_kernel<false>, grid, dim3(kThreads), 0, stream, a);
   if (a.nsplit > 1) launch_merge(a, stream);
   return launch_status();
 }
@@ -721,8 +774,10 @@ static size_t attn_ws_size(int nq, int H, int k, int window) {
   return b > 0 ? b : 256;
 }
 
+// swa: the window rows' storage (bf16 rows, or the FP8 codes; the FP8 scales are
+// checked by the caller)
 static int check_common(const csa2_fp4_cache* cache, const uint16_t* q, int32_t H, const int32_t* topk_idx, int32_t k,
-                        const int32_t* block_table, int32_t max_pages, const uint16_t* swa, int32_t window,
+                        const int32_t* block_table, int32_t max_pages, const void* swa, int32_t window,
                         float scale, float* out, float* lse) {
   if (!cache_ok(cache)) return CSA2_ERR_NULL;
   if (!cache_shape_ok(cache)) return CSA2_ERR_SHAPE;
@@ -747,14 +802,17 @@ extern "C" size_t sparse_attn_prefill_chunk_workspace_size(int32_t T, int32_t H,
   return attn_ws_size(T, H, k, window);
 }
 
-extern "C" int sparse_attn_decode(const csa2_fp4_cache* cache, const uint16_t* q, int32_t H, const int32_t* topk_idx,
-                                  int32_t k, const int32_t* block_table, int32_t max_pages, const uint16_t* swa,
-                                  const int32_t* swa_len, int32_t window, float softmax_scale, int32_t B, float* out,
-                                  float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+namespace csa2 {
+
+static int decode_impl(const csa2_fp4_cache* cache, const uint16_t* q, int32_t H, const int32_t* topk_idx, int32_t k,
+                       const int32_t* block_table, int32_t max_pages, const uint16_t* swa, const uint8_t* swa8,
+                       const uint8_t* swa8_scale, const int32_t* swa_len, int32_t window, float softmax_scale,
+                       int32_t B, float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (B < 0) return CSA2_ERR_SHAPE;
-  const int st = check_common(cache, q, H, topk_idx, k, block_table, max_pages, swa, window, softmax_scale, out, lse);
+  const void* win = swa8 ? static_cast<const void*>(swa8) : static_cast<const void*>(swa);
+  const int st = check_common(cache, q, H, topk_idx, k, block_table, max_pages, win, window, softmax_scale, out, lse);
   if (st != CSA2_OK) return st;
-  if (window > 0 && !swa_len) return CSA2_ERR_NULL;
+  if (window > 0 && (!swa_len || (swa8 && !swa8_scale))) return CSA2_ERR_NULL;
   if (B == 0) return CSA2_OK;
   AttnArgs a{};
   a.main_codes = cache->main_codes;
@@ -765,7 +823,9 @@ extern "C" int sparse_attn_decode(const csa2_fp4_cache* cache, const uint16_t* q
   a.k = k;
   a.block_table = block_table;
   a.max_pages = max_pages;
-  a.swa = swa;
+  a.swa = swa8 ? nullptr : swa;
+  a.swa8 = window > 0 ? swa8 : nullptr;
+  a.swa8_scale = swa8_scale;
   a.swa_len = swa_len;
   a.window = window;
   a.prefill = 0;
@@ -777,14 +837,16 @@ extern "C" int sparse_attn_decode(const csa2_fp4_cache* cache, const uint16_t* q
   return run_attention(a, ws, ws_bytes, stream);
 }
 
-extern "C" int sparse_attn_prefill_chunk(const csa2_fp4_cache* cache, const uint16_t* q, int32_t H,
-                                         const int32_t* topk_idx, int32_t k, const int32_t* block_table,
-                                         int32_t max_pages, int64_t chunk_start, int32_t T, const uint16_t* swa,
-                                         int32_t swa_first_valid, int32_t window, float softmax_scale, float* out,
-                                         float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+static int prefill_impl(const csa2_fp4_cache* cache, const uint16_t* q, int32_t H, const int32_t* topk_idx, int32_t k,
+                        const int32_t* block_table, int32_t max_pages, int64_t chunk_start, int32_t T,
+                        const uint16_t* swa, const uint8_t* swa8, const uint8_t* swa8_scale, int32_t swa_first_valid,
+                        int32_t window, float softmax_scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
   if (T < 0 || chunk_start < 0 || swa_first_valid < 0) return CSA2_ERR_SHAPE;
-  const int st = check_common(cache, q, H, topk_idx, k, block_table, max_pages, swa, window, softmax_scale, out, lse);
+  const void* win = swa8 ? static_cast<const void*>(swa8) : static_cast<const void*>(swa);
+  const int st = check_common(cache, q, H, topk_idx, k, block_table, max_pages, win, window, softmax_scale, out, lse);
   if (st != CSA2_OK) return st;
+  if (window > 0 && swa8 && !swa8_scale) return CSA2_ERR_NULL;
   if (T == 0) return CSA2_OK;
   AttnArgs a{};
   a.main_codes = cache->main_codes;
@@ -795,7 +857,9 @@ extern "C" int sparse_attn_prefill_chunk(const csa2_fp4_cache* cache, const uint
   a.k = k;
   a.block_table = block_table;
   a.max_pages = max_pages;
-  a.swa = swa;
+  a.swa = swa8 ? nullptr : swa;
+  a.swa8 = window > 0 ? swa8 : nullptr;
+  a.swa8_scale = swa8_scale;
   a.swa_len = nullptr;
   a.window = window;
   a.prefill = 1;
@@ -805,4 +869,43 @@ extern "C" int sparse_attn_prefill_chunk(const csa2_fp4_cache* cache, const uint
   a.out = out;
   a.lse = lse;
   return run_attention(a, ws, ws_bytes, stream);
+}
+
+}  // namespace csa2
+
+extern "C" int sparse_attn_decode(const csa2_fp4_cache* cache, const uint16_t* q, int32_t H, const int32_t* topk_idx,
+                                  int32_t k, const int32_t* block_table, int32_t max_pages, const uint16_t* swa,
+                                  const int32_t* swa_len, int32_t window, float softmax_scale, int32_t B, float* out,
+                                  float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_impl(cache, q, H, topk_idx, k, block_table, max_pages, swa, nullptr, nullptr, swa_len, window,
+                     softmax_scale, B, out, lse, ws, ws_bytes, stream);
+}
+
+extern "C" int sparse_attn_decode_fp8win(const csa2_fp4_cache* cache, const uint16_t* q, int32_t H,
+                                         const int32_t* topk_idx, int32_t k, const int32_t* block_table,
+                                         int32_t max_pages, const uint8_t* swa_codes, const uint8_t* swa_scales,
+                                         const int32_t* swa_len, int32_t window, float softmax_scale, int32_t B,
+                                         float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_impl(cache, q, H, topk_idx, k, block_table, max_pages, nullptr, swa_codes, swa_scales, swa_len,
+                     window, softmax_scale, B, out, lse, ws, ws_bytes, stream);
+}
+
+extern "C" int sparse_attn_prefill_chunk(const csa2_fp4_cache* cache, const uint16_t* q, int32_t H,
+                                         const int32_t* topk_idx, int32_t k, const int32_t* block_table,
+                                         int32_t max_pages, int64_t chunk_start, int32_t T, const uint16_t* swa,
+                                         int32_t swa_first_valid, int32_t window, float softmax_scale, float* out,
+                                         float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return prefill_impl(cache, q, H, topk_idx, k, block_table, max_pages, chunk_start, T, swa, nullptr, nullptr,
+                      swa_first_valid, window, softmax_scale, out, lse, ws, ws_bytes, stream);
+}
+
+extern "C" int sparse_attn_prefill_chunk_fp8win(const csa2_fp4_cache* cache, const uint16_t* q, int32_t H,
+                                                const int32_t* topk_idx, int32_t k, const int32_t* block_table,
+                                                int32_t max_pages, int64_t chunk_start, int32_t T,
+                                                const uint8_t* swa_codes, const uint8_t* swa_scales,
+                                                int32_t swa_first_valid, int32_t window, float softmax_scale,
+                                                float* out, float* lse, void* ws, size_t ws_bytes,
+                                                hipStream_t stream) {
+  return prefill_impl(cache, q, H, topk_idx, k, block_table, max_pages, chunk_start, T, nullptr, swa_codes,
+                      swa_scales, swa_first_valid, window, softmax_scale, out, lse, ws, ws_bytes, stream);
 }

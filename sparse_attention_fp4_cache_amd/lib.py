@@ -37,6 +37,9 @@ EXPORTS = (
     "sparse_attn_decode",
     "sparse_attn_prefill_chunk_workspace_size",
     "sparse_attn_prefill_chunk",
+    "swa_fp8_write",
+    "sparse_attn_decode_fp8win",
+    "sparse_attn_prefill_chunk_fp8win",
 )
 
 
@@ -95,6 +98,12 @@ def load() -> ctypes.CDLL:
         L.sparse_attn_prefill_chunk_workspace_size.restype = _SZ
         L.sparse_attn_prefill_chunk.argtypes = [ctypes.POINTER(_CacheStruct), _P, _I32, _P, _I32, _P, _I32, _I64,
                                                 _I32, _P, _I32, _I32, ctypes.c_float, _P, _P, _P, _SZ, _P]
+        L.swa_fp8_write.argtypes = [_P, _I64, _P, _P, _P]
+        L.sparse_attn_decode_fp8win.argtypes = [ctypes.POINTER(_CacheStruct), _P, _I32, _P, _I32, _P, _I32, _P, _P,
+                                                _P, _I32, ctypes.c_float, _I32, _P, _P, _P, _SZ, _P]
+        L.sparse_attn_prefill_chunk_fp8win.argtypes = [ctypes.POINTER(_CacheStruct), _P, _I32, _P, _I32, _P, _I32,
+                                                       _I64, _I32, _P, _P, _I32, _I32, ctypes.c_float, _P, _P, _P,
+                                                       _SZ, _P]
         for name in EXPORTS:
             if name not in ("csa2_status_string",) and not name.endswith("_size"):
                 getattr(L, name).restype = ctypes.c_int
@@ -308,6 +317,54 @@ def sparse_attn_prefill_chunk(cache: Cache, q: torch.Tensor, topk_idx: torch.Ten
         _bits16(swa, "swa"), int(swa_first_valid), int(window), float(softmax_scale),
         _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"), _ptr(ws, torch.uint8, "ws"),
         ws.numel(), _stream(stream)))
+
+
+def swa_fp8_write(rows: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stream=None):
+    """Window rows [..., 512] bf16 -> FP8 codes [..., 512] uint8 and one E8M0 scale per
+    row [...] uint8."""
+    if rows.shape[-1] != LATENT_DIM or codes.shape != rows.shape or scales.shape != rows.shape[:-1]:
+        raise ValueError("shape mismatch in swa_fp8_write arguments")
+    n = rows.numel() // LATENT_DIM
+    _check("swa_fp8_write", load().swa_fp8_write(_bits16(rows, "rows"), n, _ptr(codes, torch.uint8, "codes"),
+                                                 _ptr(scales, torch.uint8, "scales"), _stream(stream)))
+
+
+def sparse_attn_decode_fp8win(cache: Cache, q: torch.Tensor, topk_idx: torch.Tensor, block_table: torch.Tensor,
+                              swa_codes: torch.Tensor, swa_scales: torch.Tensor, swa_len: torch.Tensor,
+                              softmax_scale: float, out: torch.Tensor, lse: torch.Tensor, ws: torch.Tensor,
+                              stream=None):
+    B, H, d = q.shape
+    k = topk_idx.shape[1]
+    window = swa_codes.shape[1]
+    if d != LATENT_DIM or topk_idx.shape[0] != B or swa_codes.shape != (B, window, LATENT_DIM) \
+            or swa_scales.shape != (B, window) or out.shape != (B, H, d) or lse.shape != (B, H) \
+            or swa_len.shape != (B,):
+        raise ValueError("shape mismatch in sparse_attn_decode_fp8win arguments")
+    _check("sparse_attn_decode_fp8win", load().sparse_attn_decode_fp8win(
+        cache.struct, _bits16(q, "q"), H, _ptr(topk_idx, torch.int32, "topk_idx"), k,
+        _ptr(block_table, torch.int32, "block_table"), block_table.shape[1], _ptr(swa_codes, torch.uint8, "swa_codes"),
+        _ptr(swa_scales, torch.uint8, "swa_scales"), _ptr(swa_len, torch.int32, "swa_len"), window,
+        float(softmax_scale), B, _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"),
+        _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+
+
+def sparse_attn_prefill_chunk_fp8win(cache: Cache, q: torch.Tensor, topk_idx: torch.Tensor,
+                                     block_table: torch.Tensor, chunk_start: int, swa_codes: torch.Tensor,
+                                     swa_scales: torch.Tensor, swa_first_valid: int, window: int,
+                                     softmax_scale: float, out: torch.Tensor, lse: torch.Tensor, ws: torch.Tensor,
+                                     stream=None):
+    T, H, d = q.shape
+    k = topk_idx.shape[1]
+    if d != LATENT_DIM or topk_idx.shape[0] != T or swa_codes.shape != (window - 1 + T, LATENT_DIM) \
+            or swa_scales.shape != (window - 1 + T,) or out.shape != (T, H, d) or lse.shape != (T, H) \
+            or block_table.dim() != 1:
+        raise ValueError("shape mismatch in sparse_attn_prefill_chunk_fp8win arguments")
+    _check("sparse_attn_prefill_chunk_fp8win", load().sparse_attn_prefill_chunk_fp8win(
+        cache.struct, _bits16(q, "q"), H, _ptr(topk_idx, torch.int32, "topk_idx"), k,
+        _ptr(block_table, torch.int32, "block_table"), block_table.shape[0], int(chunk_start), T,
+        _ptr(swa_codes, torch.uint8, "swa_codes"), _ptr(swa_scales, torch.uint8, "swa_scales"),
+        int(swa_first_valid), int(window), float(softmax_scale), _ptr(out, torch.float32, "out"),
+        _ptr(lse, torch.float32, "lse"), _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
 
 
 def default_softmax_scale() -> float:

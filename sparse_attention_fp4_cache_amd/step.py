@@ -82,6 +82,10 @@ class DecodeStep:
                 L["w"] = torch.from_numpy(d["w"]).to(device)
                 L["topk"] = torch.full((B, K), -1, dtype=torch.int32, device=device)
                 L["scores"] = None
+            if wl.fp8_window:  # the window rows in FP8, quantised once on the device
+                L["swa8"] = torch.zeros((B, W, 512), dtype=torch.uint8, device=device)
+                L["swa8_scale"] = torch.zeros((B, W), dtype=torch.uint8, device=device)
+                lib.swa_fp8_write(L["swa"], L["swa8"], L["swa8_scale"])
             self.layers.append(L)
         self.new_latent = None
 
@@ -139,8 +143,13 @@ class DecodeStep:
                         L["pool"] = self.pool.clone()
             if latest is None:
                 raise ValueError("a reuse layer needs an earlier full or reindex layer")
-            call("sparse_attn_decode", lib.sparse_attn_decode, self.cache, L["q"], latest, self.block_table,
-                 L["swa"], L["swa_len"], self.scale, L["out"], L["lse"], self.ws_attn)
+            if self.wl.fp8_window:
+                call("sparse_attn_decode_fp8win", lib.sparse_attn_decode_fp8win, self.cache, L["q"], latest,
+                     self.block_table, L["swa8"], L["swa8_scale"], L["swa_len"], self.scale, L["out"], L["lse"],
+                     self.ws_attn)
+            else:
+                call("sparse_attn_decode", lib.sparse_attn_decode, self.cache, L["q"], latest, self.block_table,
+                     L["swa"], L["swa_len"], self.scale, L["out"], L["lse"], self.ws_attn)
 
 
 def _write_decode_cache(cache, wl: Workload, device, rows_per_call: int):

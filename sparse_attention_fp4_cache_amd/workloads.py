@@ -50,6 +50,9 @@ class Workload:
               Flash, expliqué pas à pas", bounded SWA replay in the on-disk cache
               chapter; the interval's formula is lost there, this is its plain
               reading).
+    fp8_window decode only: every layer's window rows are stored in FP8 ("DeepSeek-
+              V4.1-Flash, expliqué pas à pas", FP4 KV cache section) and attended
+              from there; the rows are the same seeded bf16 rows, quantised once.
     """
 
     name: str
@@ -69,6 +72,7 @@ class Workload:
     seed: int = 0
     npool: int = 0  # decode: >0 -> Reindex layers scan a candidate pool of npool blocks of 8 entries
     swa_replay: bool = False  # prefill: the window starts at the chunk's first token (bounded replay)
+    fp8_window: bool = False  # decode: window rows kept in FP8 (E4M3FN, one E8M0 scale per row)
 
     # ------------------------------------------------------------ geometry --
     @property
@@ -281,6 +285,9 @@ WORKLOADS = {
                                    chunk=4096),
     # bounded replay of the last 128 tokens of a 1,048,576-token prompt: every query
     # has its causal top-K over the whole cache; the window restarts at the replay
+    # the same inputs as decode_1m_10layer with every layer's window in FP8
+    "decode_1m_10layer_fp8win": Workload("decode_1m_10layer_fp8win", 4, "decode", B=1, ctx=(1048576,), H=64,
+                                         Hi=64, K=2048, layers=C4_LAYERS, fp8_window=True),
     # one token through all 40 layers at 1,048,576 tokens: three m = 2 encoder
     # caches (524,288 entries each) and the m = 1 decoder cache (1,048,576 entries),
     # 0.87 GiB in all; the decoder's Reindex layers select inside 2048-block pools

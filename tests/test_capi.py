@@ -178,3 +178,33 @@ def test_attention_validation(L):
                                        FAKE, pws, None) == -2
     assert L.sparse_attn_prefill_chunk(c, FAKE, 64, FAKE, 2048, FAKE, 64, 0, 0, FAKE, 0, 128, 0.04, FAKE, FAKE,
                                        FAKE, pws, None) == 0
+
+
+def test_fp8_window_validation(L):
+    assert L.swa_fp8_write(FAKE, -1, FAKE, FAKE, None) == -2
+    assert L.swa_fp8_write(FAKE, 0, None, None, None) == 0
+    assert L.swa_fp8_write(None, 4, FAKE, FAKE, None) == -1
+    assert L.swa_fp8_write(FAKE, 4, FAKE, None, None) == -1
+    c = _cache()
+    ws = L.sparse_attn_decode_workspace_size(1, 64, 2048, 128)
+
+    def dec(codes=FAKE, scales=FAKE, window=128, H=64, B=1):
+        return L.sparse_attn_decode_fp8win(c, FAKE, H, FAKE, 2048, FAKE, 64, codes, scales, FAKE, window, 0.04, B,
+                                           FAKE, FAKE, FAKE, ws, None)
+
+    assert dec(codes=None) == -1
+    assert dec(scales=None) == -1
+    assert dec(H=8) == -2
+    assert dec(window=129) == -2
+    assert dec(codes=None, scales=None, window=0, B=0) == 0
+    assert dec(B=0) == 0
+    pws = L.sparse_attn_prefill_chunk_workspace_size(16, 64, 2048, 128)
+
+    def pre(codes=FAKE, scales=FAKE, T=16, start=0):
+        return L.sparse_attn_prefill_chunk_fp8win(c, FAKE, 64, FAKE, 2048, FAKE, 64, start, T, codes, scales, 0, 128,
+                                                  0.04, FAKE, FAKE, FAKE, pws, None)
+
+    assert pre(codes=None) == -1
+    assert pre(scales=None) == -1
+    assert pre(start=-1) == -2
+    assert pre(T=0) == 0

@@ -99,8 +99,15 @@ def run_decode_case(name, attn_rows=None, wl=None):
                 topk_equal(L["pool"].cpu().numpy(), ref_pool, f"{name} layer {li} candidate pool")
                 say(f"  layer {li}: candidate pool of {wl.npool} blocks bit-exact")
         rows = np.arange(wl.B) if attn_rows is None else np.asarray(attn_rows)
-        ro, rl = oracle.sparse_attn_decode(o, d["q"][rows], latest[rows], bt[rows], d["swa"][rows],
-                                           d["swa_len"][rows], st.scale)
+        if wl.fp8_window:
+            codes, scales = oracle.swa_fp8_quant(d["swa"][rows])
+            assert np.array_equal(L["swa8"].cpu().numpy()[rows], codes), f"layer {li}: FP8 window codes differ"
+            assert np.array_equal(L["swa8_scale"].cpu().numpy()[rows], scales), f"layer {li}: FP8 scales differ"
+            ro, rl = oracle.sparse_attn_decode_fp8win(o, d["q"][rows], latest[rows], bt[rows], codes, scales,
+                                                      d["swa_len"][rows], st.scale)
+        else:
+            ro, rl = oracle.sparse_attn_decode(o, d["q"][rows], latest[rows], bt[rows], d["swa"][rows],
+                                               d["swa_len"][rows], st.scale)
         attn_close(L["out"].cpu().numpy()[rows], ro, L["lse"].cpu().numpy()[rows], rl,
                    f"{name} layer {li} ({L['mode']}) attention")
     return st
@@ -124,6 +131,13 @@ def test_config_ragged_decode_32_paged():
 @pytest.mark.timeout(1200)
 def test_config_decode_1m_10layer_and_graph_replay():
     st = run_decode_case("decode_1m_10layer")
+    graph_replays_equal_eager(st)
+
+
+@pytest.mark.timeout(1200)
+def test_config_decode_1m_10layer_fp8_window():
+    # every layer's window in FP8: codes and scales bit-exact, attention within tolerance
+    st = run_decode_case("decode_1m_10layer_fp8win")
     graph_replays_equal_eager(st)
 
 

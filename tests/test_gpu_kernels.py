@@ -661,3 +661,108 @@ def test_pool_with_tied_keys():
 
     say("case: pool with 2000 tied entries (ties to the lower block and entry)")
     _pool_case(np.random.default_rng(402), [6000], 16, 300, 500, key_fn=keys)
+
+
+# -------------------------------------------------------------- FP8 window --------
+def _fp8_rows(rng, n):
+    """Window rows with the cases the FP8 format has: ties between E4M3 neighbours,
+    zero and -0 rows, bf16 subnormal and huge rows, outlier channels."""
+    x = (rng.standard_normal((n, 512)) * np.exp(rng.uniform(-20, 20, (n, 1)))).astype(np.float32)
+    x[:, 7] *= 8.0
+    x[1] = 0.0
+    x[2] = -0.0
+    x[3] = rng.standard_normal(512).astype(np.float32) * np.float32(1e-39)  # bf16 subnormals
+    x[4] = rng.standard_normal(512).astype(np.float32) * np.float32(1e37)
+    # row 5: scale 2^0 (amax 448) and E4M3 midpoints
+    e4 = np.array([oracle.e4m3_value(b) for b in range(0x7F)])
+    mids = (e4[8:-1] + e4[9:]) / 2
+    x[5] = 0.0
+    x[5, 0] = 448.0
+    x[5, 1:1 + len(mids)] = mids * np.where(np.arange(len(mids)) % 2, -1, 1)
+    return bits(x)
+
+
+def test_swa_fp8_write_bit_exact():
+    rng = np.random.default_rng(500)
+    rows = _fp8_rows(rng, 3001)
+    say("case: FP8 window rows, 3001 rows with ties, zero, subnormal and huge rows")
+    codes = torch.full((3001, 512), 0x55, dtype=torch.uint8, device="cuda")
+    scales = torch.full((3001,), 0x55, dtype=torch.uint8, device="cuda")
+    lib.swa_fp8_write(dev_bits(rows), codes, scales)
+    rc, rs = oracle.swa_fp8_quant(rows)
+    assert np.array_equal(scales.cpu().numpy(), rs), "FP8 window scales differ"
+    got = codes.cpu().numpy()
+    bad = np.argwhere(got != rc)
+    assert len(bad) == 0, f"{len(bad)} FP8 codes differ, first {bad[:4].tolist()}"
+
+
+def _fp8_window(rng, shape):
+    x = rng.standard_normal(shape).astype(np.float32)
+    x[..., [3, 200]] *= 8.0
+    return bits(x)
+
+
+@pytest.mark.parametrize("H", [16, 64])
+def test_attention_decode_fp8_window(H):
+    rng = np.random.default_rng(510 + H)
+    n, B, k, W = 3000, 3, 300, 128
+    g, o = _attn_cache(rng, n)
+    bt = np.tile(np.arange((n + 63) // 64, dtype=np.int32), (B, 1))
+    idx = np.stack([np.sort(rng.choice(n, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    idx[1, 250:] = -1
+    q = bits(rng.standard_normal((B, H, 512)))
+    rows = _fp8_window(rng, (B, W, 512))
+    codes = torch.zeros((B, W, 512), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((B, W), dtype=torch.uint8, device="cuda")
+    lib.swa_fp8_write(dev_bits(rows), codes, scales)
+    swa_len = np.array([128, 5, 0], np.int32)
+    scale = 1 / math.sqrt(512)
+    ws = torch.zeros(lib.sparse_attn_decode_workspace_size(B, H, k, W), dtype=torch.uint8, device="cuda")
+    say(f"case: attention decode, FP8 window, H={H}")
+    out = torch.zeros((B, H, 512), device="cuda")
+    lse = torch.zeros((B, H), device="cuda")
+    lib.sparse_attn_decode_fp8win(g, dev_bits(q), dev(idx), dev(bt), codes, scales, dev(swa_len), scale, out, lse, ws)
+    rc, rs = oracle.swa_fp8_quant(rows)
+    ro, rl = oracle.sparse_attn_decode_fp8win(o, q, idx, bt, rc, rs, swa_len, scale)
+    attn_close(out.cpu().numpy(), ro, lse.cpu().numpy(), rl, f"decode FP8 window H={H}")
+    # the same kernel fed the bf16 rows of the window's exact values: identical bits
+    out2 = torch.zeros_like(out)
+    lse2 = torch.zeros_like(lse)
+    lib.sparse_attn_decode(g, dev_bits(q), dev(idx), dev(bt), dev_bits(oracle.swa_fp8_dequant(rc, rs)), dev(swa_len),
+                           scale, out2, lse2, ws)
+    assert torch.equal(out.view(torch.int32), out2.view(torch.int32))
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+
+
+@pytest.mark.parametrize("T", [40, 160])
+def test_attention_prefill_fp8_window(T):
+    # T = 40: several row ranges per query; T = 160: one workgroup per query (64 heads)
+    rng = np.random.default_rng(520 + T)
+    n, H, k, W = 2500, 64, 200, 128
+    g, o = _attn_cache(rng, n)
+    bt = np.arange((n + 63) // 64, dtype=np.int32)
+    idx = np.stack([np.sort(rng.choice(n, k, replace=False)) for _ in range(T)]).astype(np.int32)
+    idx[5, 150:] = -1
+    q = bits(rng.standard_normal((T, H, 512)))
+    rows = _fp8_window(rng, (W - 1 + T, 512))
+    codes = torch.zeros((W - 1 + T, 512), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((W - 1 + T,), dtype=torch.uint8, device="cuda")
+    lib.swa_fp8_write(dev_bits(rows), codes, scales)
+    first_valid = 100
+    scale = 1 / math.sqrt(512)
+    ws = torch.zeros(max(256, lib.sparse_attn_prefill_chunk_workspace_size(T, H, k, W)), dtype=torch.uint8,
+                     device="cuda")
+    say(f"case: attention prefill, FP8 window, T={T}")
+    out = torch.zeros((T, H, 512), device="cuda")
+    lse = torch.zeros((T, H), device="cuda")
+    lib.sparse_attn_prefill_chunk_fp8win(g, dev_bits(q), dev(idx), dev(bt), 5000, codes, scales, first_valid, W, scale,
+                                         out, lse, ws)
+    rc, rs = oracle.swa_fp8_quant(rows)
+    ro, rl = oracle.sparse_attn_prefill_chunk_fp8win(o, q, idx, bt, rc, rs, first_valid, W, scale)
+    attn_close(out.cpu().numpy(), ro, lse.cpu().numpy(), rl, f"prefill FP8 window T={T}")
+    out2 = torch.zeros_like(out)
+    lse2 = torch.zeros_like(lse)
+    lib.sparse_attn_prefill_chunk(g, dev_bits(q), dev(idx), dev(bt), 5000, dev_bits(oracle.swa_fp8_dequant(rc, rs)),
+                                  first_valid, W, scale, out2, lse2, ws)
+    assert torch.equal(out.view(torch.int32), out2.view(torch.int32))
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))

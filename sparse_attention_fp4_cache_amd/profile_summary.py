@@ -22,7 +22,7 @@ import glob
 import os
 import sys
 
-SCAN_KERNEL = "index_score_kernel<4, 1, false>"  # the standalone scan (index_score, 64 heads, one query)
+SCAN_KERNEL = "index_score_kernel<4, 1, false, false>"  # the standalone scan (index_score, 64 heads, one query)
 COPY_KERNEL = "MulFunctor"  # torch's elementwise multiply, used as a read-N/write-N copy
 
 

@@ -369,30 +369,30 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
   const int npg_all = max(min(gend - gfirst, kMaxPagesPerWave), 1);
   auto page_of = [&](int k) { return gfirst < gend ? bt_row[min(k, npg_all - 1)] : 0; };
 
-  // the wavefront's first four pages, unconditionally (past its last page -- or
-  // with no page at all -- it re-reads a valid page and ignores the data)
-  KeyTile t0, t1, t2, t3;
+  // the wavefront's pages, unconditionally (past its last page -- or with no page at
+  // all -- it re-reads a valid page and ignores the data), two in flight at a time:
+  // pages 0 and 1 now, page 2 into t0 once page 0 is scored, page 3 into t1 once
+  // page 1 is.  Two pages per wavefront keep about 17 MB in flight over the chip at
+  // batch 1, enough for the HBM rate, while the query blocks that every workgroup
+  // stages first do not queue behind the whole scan's bytes.
+  KeyTile t0, t1;
   // the four page numbers are read now.  Wavefronts that stage query blocks request
   // their pages after the staging, so the staging's query loads do not queue behind
-  // the key burst; the others request theirs at once.
+  // their own key loads; the others request theirs at once.
   const int pg0 = POOL ? 0 : page_of(0), pg1 = POOL ? 0 : page_of(1), pg2 = POOL ? 0 : page_of(2),
             pg3 = POOL ? 0 : page_of(3);
   const bool stager = wid * 64 < items;  // uniform
   const int32_t* __restrict__ pool_row = POOL ? pool + (int64_t)q0 * npool : nullptr;
   const int32_t* __restrict__ bt_seq = block_table + (int64_t)first_row * max_pages;
   auto vpage = [&](int k) { return gfirst + min(k, npg_all - 1); };  // pools: virtual page of the k-th
-  auto request_pages = [&]() {
-    if (POOL) {
-      load_keys_pool(t0, idx_codes, idx_scales, pool_row, npool, bt_seq, vpage(0), lane);
-      load_keys_pool(t1, idx_codes, idx_scales, pool_row, npool, bt_seq, vpage(1), lane);
-      load_keys_pool(t2, idx_codes, idx_scales, pool_row, npool, bt_seq, vpage(2), lane);
-      load_keys_pool(t3, idx_codes, idx_scales, pool_row, npool, bt_seq, vpage(3), lane);
-    } else {
-      load_keys(t0, idx_codes, idx_scales, pg0, lane);
-      load_keys(t1, idx_codes, idx_scales, pg1, lane);
-      load_keys(t2, idx_codes, idx_scales, pg2, lane);
-      load_keys(t3, idx_codes, idx_scales, pg3, lane);
-    }
+  // page k of the wavefront into t (k = 0 .. 3)
+  auto request_page = [&](KeyTile& t, int k, int pg) __attribute__((always_inline)) {
+    if (POOL) load_keys_pool(t, idx_codes, idx_scales, pool_row, npool, bt_seq, vpage(k), lane);
+    else load_keys(t, idx_codes, idx_scales, pg, lane);
+  };
+  auto request_pages = [&]() __attribute__((always_inline)) {
+    request_page(t0, 0, pg0);
+    request_page(t1, 1, pg1);
   };
   if (!stager) request_pages();
 
@@ -465,9 +465,11 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
     // straight-line code: the wait for page k leaves pages k+1.. in flight (a loop
     // here would make the compiler wait for every outstanding load at its head)
     page_all(t0, 0);
+    request_page(t0, 2, pg2);
     if (npg > 1) page_all(t1, 1);
-    if (npg > 2) page_all(t2, 2);
-    if (npg > 3) page_all(t3, 3);
+    request_page(t1, 3, pg3);
+    if (npg > 2) page_all(t0, 2);
+    if (npg > 3) page_all(t1, 3);
     // rare: entries whose blocks fall outside the exact window of the MFMA
     while (exact_bits != 0ull) {
       const int b = __builtin_ctzll(exact_bits);

@@ -325,6 +325,26 @@ def test_topk_many_rows_one_workgroup_per_row():
     _topk_case(s, nvis, 300, "rows k=300")
 
 
+def test_topk_many_long_rows_one_workgroup_per_row():
+    """260 rows of 70,000 scores (enough rows for one workgroup per row, rows longer
+    than a workgroup's lists): rows whose best entries come first, last or in a few
+    huge values, all-equal, tied and short rows."""
+    rng = np.random.default_rng(332)
+    nq, ld = 260, 70_000
+    s = rng.standard_normal((nq, ld)).astype(np.float32)
+    nvis = rng.integers(60_000, ld + 1, nq).astype(np.int32)
+    nvis[:3] = [2048, 100, 0]
+    s[3, -5000:] += 50.0                    # the best entries last
+    s[4, :1100] = 1000.0 + rng.standard_normal(1100).astype(np.float32) * 1e-3  # a few huge values first
+    s[5] = 2.5                              # all equal
+    s[6] = rng.integers(0, 300, ld).astype(np.float32)  # many ties
+    s[7, :8192] += 50.0                     # the first 8192 far above the rest
+    nvis[3:8] = ld
+    say("case: top-k 260 rows of 70,000 (one workgroup per row)")
+    _topk_case(s, nvis, 2048, "long rows k=2048")
+    _topk_case(s, nvis, 64, "long rows k=64")
+
+
 def test_topk_few_long_rows_take_chunks():
     """130 rows of 70,000 scores (too few rows to fill the chip with one workgroup
     each): the chunked path with many rows, ragged, tied and short rows included."""

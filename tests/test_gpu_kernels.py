@@ -674,6 +674,56 @@ def test_pool_covering_every_block_and_short_pools():
     assert np.all(pool[3] == -1), "a query with no visible entry has an empty pool"
 
 
+def test_pool_queries_sharing_sequences():
+    """Pools for several queries per sequence (a prefill chunk's causal rows): the
+    full scan, the pools and the pooled scan address each sequence's pages through
+    seq_of_query."""
+    rng = np.random.default_rng(403)
+    n_per_seq = [9000, 3000]
+    pages = [(n + 63) // 64 for n in n_per_seq]
+    phys = rng.permutation(sum(pages))
+    bt = np.zeros((2, max(pages)), np.int32)
+    bt[0, :pages[0]] = phys[:pages[0]]
+    bt[1, :pages[1]] = phys[pages[0]:]
+    lat, key, slots = [], [], []
+    for b, n in enumerate(n_per_seq):
+        j = np.arange(n)
+        slots.append(bt[b, j // 64].astype(np.int64) * 64 + j % 64)
+        key.append(bits(rng.standard_normal((n, 128)).astype(np.float32)))
+        lat.append(bits(np.zeros((n, 512), np.float32)))
+    g, o = both_caches(np.concatenate(lat), np.concatenate(key), np.concatenate(slots), sum(pages) * 64)
+    soq = np.array([0, 0, 0, 1, 1, 1, 1], np.int32)
+    nvis = np.array([9000, 8999, 4321, 3000, 2999, 17, 0], np.int32)
+    nq, Hi, npool, k = len(soq), 16, 200, 300
+    ld = ((int(nvis.max()) + 63) // 64) * 64
+    q0 = bits(rng.standard_normal((nq, Hi, 128)).astype(np.float32))
+    q1 = bits(rng.standard_normal((nq, Hi, 128)).astype(np.float32))
+    w0 = rng.random((nq, Hi), dtype=np.float32)
+    w1 = rng.random((nq, Hi), dtype=np.float32)
+    say("case: pools for 7 queries on 2 sequences (seq_of_query)")
+    dnv, dbt, dsoq = dev(nvis), dev(bt), dev(soq)
+    s_full = torch.full((nq, ld), float("nan"), device="cuda")
+    lib.index_score(g, dev_bits(q0), dev(w0), dnv, dbt, s_full, seq_of_query=dsoq)
+    ref_full, _, _ = oracle.index_score(o, q0, w0, nvis, bt, seq_of_query=soq, ld=ld)
+    ref_pool = oracle.pool_build(ref_full, nvis, npool)
+    ref_ps, _, _ = oracle.index_score_pool(o, q1, w1, nvis, ref_pool, bt, seq_of_query=soq)
+    ref_top = oracle.topk_pool(ref_ps, ref_pool, nvis, k)
+    pool = torch.full((nq, npool), -7, dtype=torch.int32, device="cuda")
+    ws_b = torch.zeros(lib.index_pool_build_workspace_size(nq, ld, npool), dtype=torch.uint8, device="cuda")
+    lib.index_pool_build(s_full, dnv, npool, pool, ws_b)
+    ps = torch.full((nq, npool * 8), float("nan"), device="cuda")
+    top = torch.full((nq, k), -7, dtype=torch.int32, device="cuda")
+    ws_t = torch.zeros(lib.index_topk_pool_workspace_size(nq, npool, k), dtype=torch.uint8, device="cuda")
+    lib.index_topk_pool(g, dev_bits(q1), dev(w1), dnv, pool, dbt, ps, k, top, ws_t, seq_of_query=dsoq)
+    torch.cuda.synchronize()
+    assert np.array_equal(pool.cpu().numpy(), ref_pool), "pool differs"
+    got_ps = ps.cpu().numpy()
+    for r in range(nq):
+        npv = int((~np.isnan(ref_ps[r])).sum())
+        assert same_bits_f32(got_ps[r, :npv], ref_ps[r, :npv]), f"row {r}: pool scores differ"
+    assert np.array_equal(top.cpu().numpy(), ref_top), "pool top-k differs"
+
+
 def test_pool_with_tied_keys():
     def keys(k):
         k[1000:3000] = k[1000]  # 2000 entries with one key: tied scores across many blocks

@@ -664,6 +664,8 @@ def test_pool_build_and_topk_inside_pool():
     _pool_case(rng, [20001, 3005, 777], 64, 256, 300)
     say("case: pool of 2048 blocks over one 70,000-entry sequence, k = 2048, Hi = 16")
     _pool_case(rng, [70000], 16, 2048, 2048)
+    say("case: pool of 300 blocks over 2 sequences, k = 500, Hi = 128")
+    _pool_case(rng, [5003, 2999], 128, 300, 500)
 
 
 def test_pool_covering_every_block_and_short_pools():

@@ -278,6 +278,9 @@ WORKLOADS = {
                                  H=64, Hi=64, K=2048, paged_random=True),
     "decode_1m_10layer": Workload("decode_1m_10layer", 4, "decode", B=1, ctx=(1048576,), H=64, Hi=64, K=2048,
                                   layers=C4_LAYERS),
+    # eight 1M-token sessions decoding together: the 10-layer step at batch 8
+    "decode_1m_10layer_b8": Workload("decode_1m_10layer_b8", 8, "decode", B=8, ctx=(1048576,) * 8, H=64, Hi=64,
+                                     K=2048, layers=C4_LAYERS),
     # the same inputs as decode_1m_10layer; the four Reindex layers use the pool
     "decode_1m_10layer_pool": Workload("decode_1m_10layer_pool", 4, "decode", B=1, ctx=(1048576,), H=64, Hi=64,
                                        K=2048, layers=C4_LAYERS, npool=2048),

@@ -46,6 +46,11 @@ template <int MT>
 struct QStage {
   uint4 codes[MT][64];            // A operand of M-tile mt for lane l
   uint32_t scale[(MT + 3) / 4][64];  // byte (mt%4) of word mt/4: E8M0 of lane l in tile mt
+  // the same blocks as A operands of the 32x32x64 form (Hi a multiple of 32): 32-head
+  // tile m, K-step s, lane l = head row (l%32) and block 2s + l/32; E8M0 in byte
+  // (2m+s)%4 of word (2m+s)/4
+  uint4 codes32[(MT + 1) / 2][2][64];
+  uint32_t scale32[(MT + 3) / 4][64];
   uint8_t u[16 * MT][4];          // E8M0 of head h, block b (plain order, exact path)
   uint32_t stat[MT];  // heads of M-tile mt: largest block-exponent span | min u << 8 | max u << 16
   int row;
@@ -153,9 +158,35 @@ CSA2_DEV void transpose4(float& r0, float& r1, float& r2, float& r3) {
 
 struct KeyTile {
   uint4 codes[4];   // N-tile nt: 16 bytes of key (16nt + lane%16), block lane/16
+                    // (32x32x64 form: [2n + s] = key (32n + lane%32), block 2s + lane/32)
   uint32_t sc[4];   // its E8M0 byte
   uint32_t own;     // the 4 E8M0 bytes of entry `lane` of the page
 };
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+template <int OA>
+CSA2_DEV v16f mfma32_fp4(const uint4& a, const uint4& b, const v16f& c, int asc, int bsc) {
+  const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, OA, asc, 0, bsc);
+}
+
+// One page of keys as B operands of the 32x32x64 form.
+CSA2_DEV void load_keys32(KeyTile& t, const uint8_t* __restrict__ idx_codes, const uint8_t* __restrict__ idx_scales,
+                          int page, int lane) {
+  const int64_t slot0 = (int64_t)__builtin_amdgcn_readfirstlane(page) * kPage;  // uniform
+  const uint32_t hf = (uint32_t)lane >> 5, n = (uint32_t)lane & 31u;
+  const uint8_t* __restrict__ cb = idx_codes + slot0 * kIdxRowBytes;
+  const uint8_t* __restrict__ sb = idx_scales + slot0 * kIdxScaleBytes;
+#pragma unroll
+  for (uint32_t i = 0; i < 4; ++i) {
+    const uint32_t e = 32u * (i >> 1) + n, blk = 2u * (i & 1u) + hf;
+    t.codes[i] = *reinterpret_cast<const uint4*>(cb + (e * (uint32_t)kIdxRowBytes + 16u * blk));
+    t.sc[i] = sb[e * (uint32_t)kIdxScaleBytes + blk];
+  }
+  t.own = *reinterpret_cast<const uint32_t*>(sb + (uint32_t)lane * kIdxScaleBytes);
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // One page of keys: a wavefront-uniform page base plus fixed 32-bit lane offsets,
 // so every load takes the scalar-base + vector-offset form.
@@ -202,6 +233,25 @@ CSA2_DEV void load_keys_pool(KeyTile& t, const uint8_t* __restrict__ idx_codes,
   for (int nt = 0; nt < 4; ++nt) {
     t.codes[nt] = *reinterpret_cast<const uint4*>(idx_codes + sl[nt] * kIdxRowBytes + 16u * g);
     t.sc[nt] = idx_scales[sl[nt] * kIdxScaleBytes + g];
+  }
+  t.own = *reinterpret_cast<const uint32_t*>(idx_scales + so * kIdxScaleBytes);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The same as B operands of the 32x32x64 form.
+CSA2_DEV void load_keys_pool32(KeyTile& t, const uint8_t* __restrict__ idx_codes,
+                               const uint8_t* __restrict__ idx_scales, const int32_t* __restrict__ pool_row,
+                               int npool, const int32_t* __restrict__ bt_seq, int G, int lane) {
+  const uint32_t hf = (uint32_t)lane >> 5, n = (uint32_t)lane & 31u;
+  int64_t sl[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) sl[nt] = pool_slot(pool_row, npool, bt_seq, G, 32 * nt + (int)n);
+  const int64_t so = pool_slot(pool_row, npool, bt_seq, G, lane);
+#pragma unroll
+  for (uint32_t i = 0; i < 4; ++i) {
+    const uint32_t blk = 2u * (i & 1u) + hf;
+    t.codes[i] = *reinterpret_cast<const uint4*>(idx_codes + sl[i >> 1] * kIdxRowBytes + 16u * blk);
+    t.sc[i] = idx_scales[sl[i >> 1] * kIdxScaleBytes + blk];
   }
   t.own = *reinterpret_cast<const uint32_t*>(idx_scales + so * kIdxScaleBytes);
   __builtin_amdgcn_sched_barrier(0);
@@ -286,6 +336,108 @@ __device__ __attribute__((always_inline)) inline bool score_page(const QStage<MT
   if (visible) srow[j] = acc;
   if (lh != nullptr && visible && !exact_needed) atomicAdd(&lh[score_key(acc) >> kTopkBinShift], 1u);
   return exact_needed;
+}
+
+// score_page with the 32x32x64 form, for Hi a multiple of 32: per 32-head tile m and
+// 32-entry tile n, two chained MFMAs (K = 64 each) give D[head row][entry], lane l
+// holding entry l%32 and rows 8q + 4(l/32) + i (register 4q + i).  One
+// v_permlane32_swap per register pair of the two entry tiles then leaves lane l with
+// entry l of the page: rows 8q + i in the first register of the pair and 8q + 4 + i in
+// the second, so the fma chain reads every head in ascending order.  The exactness
+// window is the one of score_page (the two K halves add exactly inside it).
+template <int MT>
+__device__ __attribute__((always_inline)) inline bool score_page32(const QStage<MT>& s, const KeyTile& cur, int G,
+                                                                   const float* __restrict__ wq,
+                                                                   float* __restrict__ srow, int lane, uint32_t* lh) {
+  static_assert(MT % 2 == 0, "the 32x32x64 form needs Hi a multiple of 32");
+  constexpr int M32 = MT / 2;
+  int q_span = 0, q_umin = 255, q_umax = 0;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const uint32_t sv = s.stat[mt];
+    q_span = max(q_span, (int)(sv & 0xFFu));
+    q_umin = min(q_umin, (int)((sv >> 8) & 0xFFu));
+    q_umax = max(q_umax, (int)((sv >> 16) & 0xFFu));
+  }
+  const int j = G * kPage + lane;
+  const uint32_t own = cur.own;
+  int kmin = 255, kmax = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int u = (int)((own >> (8 * b)) & 0xFFu);
+    kmin = u < kmin ? u : kmin;
+    kmax = u > kmax ? u : kmax;
+  }
+  const bool visible = j < s.nvis;
+  const bool exact_needed = visible & (((kmax - kmin) + q_span > kMaxSpread) | (q_umin + kmin < kMinExpSum) |
+                                       (q_umax + kmax > kMaxExpSum));
+  // one 32-head tile at a time (its 32 dots per lane, then its part of the chain):
+  // fewer live registers than holding every tile's dots
+  const v16f zero = {};
+  float acc = 0.0f;
+#pragma unroll
+  for (int m = 0; m < M32; ++m) {
+    float d[2][16];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      v16f t = zero;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int p = 2 * m + k;
+        const uint4 a = s.codes32[m][k][lane];
+        const int asc = (int)s.scale32[p >> 2][lane];
+        const int bsc = (int)cur.sc[2 * n + k];
+        switch (p & 3) {
+          case 0: t = mfma32_fp4<0>(a, cur.codes[2 * n + k], t, asc, bsc); break;
+          case 1: t = mfma32_fp4<1>(a, cur.codes[2 * n + k], t, asc, bsc); break;
+          case 2: t = mfma32_fp4<2>(a, cur.codes[2 * n + k], t, asc, bsc); break;
+          default: t = mfma32_fp4<3>(a, cur.codes[2 * n + k], t, asc, bsc); break;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) d[n][r] = t[r];
+    }
+    // lane l <- entry l: rows 8q + i in d[0][4q + i], rows 8q + 4 + i in d[1][4q + i]
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const auto v = __builtin_amdgcn_permlane32_swap(u_of(d[0][r]), u_of(d[1][r]), false, false);
+      d[0][r] = f_of(v[0]);
+      d[1][r] = f_of(v[1]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc = fmaf(wq[32 * m + 8 * q + i], relu(d[0][4 * q + i]), acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc = fmaf(wq[32 * m + 8 * q + 4 + i], relu(d[1][4 * q + i]), acc);
+    }
+  }
+  if (visible) srow[j] = acc;
+  if (lh != nullptr && visible && !exact_needed) atomicAdd(&lh[score_key(acc) >> kTopkBinShift], 1u);
+  return exact_needed;
+}
+
+// Page loads and scores in the form the head count takes: 32x32x64 when Hi is a
+// multiple of 32, 16x16x128 otherwise.
+template <int MT>
+CSA2_DEV void load_page(KeyTile& t, const uint8_t* __restrict__ idx_codes, const uint8_t* __restrict__ idx_scales,
+                        int page, int lane) {
+  if constexpr (MT % 2 == 0) load_keys32(t, idx_codes, idx_scales, page, lane);
+  else load_keys(t, idx_codes, idx_scales, page, lane);
+}
+template <int MT>
+CSA2_DEV void load_page_pool(KeyTile& t, const uint8_t* __restrict__ idx_codes, const uint8_t* __restrict__ idx_scales,
+                             const int32_t* __restrict__ pool_row, int npool, const int32_t* __restrict__ bt_seq,
+                             int G, int lane) {
+  if constexpr (MT % 2 == 0) load_keys_pool32(t, idx_codes, idx_scales, pool_row, npool, bt_seq, G, lane);
+  else load_keys_pool(t, idx_codes, idx_scales, pool_row, npool, bt_seq, G, lane);
+}
+template <int MT>
+__device__ __attribute__((always_inline)) inline bool score_any(const QStage<MT>& s, const KeyTile& cur, int G,
+                                                                const float* __restrict__ wq,
+                                                                float* __restrict__ srow, int lane, uint32_t* lh) {
+  if constexpr (MT % 2 == 0) return score_page32<MT>(s, cur, G, wq, srow, lane, lh);
+  else return score_page<MT>(s, cur, G, wq, srow, lane, lh);
 }
 
 // The definition itself for one entry (integer block sums, one rounding per head,
@@ -387,8 +539,8 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
   auto vpage = [&](int k) { return gfirst + min(k, npg_all - 1); };  // pools: virtual page of the k-th
   // page k of the wavefront into t (k = 0 .. 3)
   auto request_page = [&](KeyTile& t, int k, int pg) __attribute__((always_inline)) {
-    if (POOL) load_keys_pool(t, idx_codes, idx_scales, pool_row, npool, bt_seq, vpage(k), lane);
-    else load_keys(t, idx_codes, idx_scales, pg, lane);
+    if (POOL) load_page_pool<MT>(t, idx_codes, idx_scales, pool_row, npool, bt_seq, vpage(k), lane);
+    else load_page<MT>(t, idx_codes, idx_scales, pg, lane);
   };
   auto request_pages = [&]() __attribute__((always_inline)) {
     request_page(t0, 0, pg0);
@@ -426,6 +578,11 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
       st[qi].codes[mt][l] = codes;
       st[qi].u[h][g] = (uint8_t)u;
       reinterpret_cast<uint8_t*>(&st[qi].scale[mt >> 2][l])[mt & 3] = (uint8_t)u;
+      if (MT % 2 == 0) {  // head h, block g -> tile h/32, step g/2, lane h%32 + 32 (g%2)
+        const int l32 = (h & 31) + 32 * (g & 1), p32 = 2 * (h >> 5) + (g >> 1);
+        st[qi].codes32[h >> 5][g >> 1][l32] = codes;
+        reinterpret_cast<uint8_t*>(&st[qi].scale32[p32 >> 2][l32])[p32 & 3] = (uint8_t)u;
+      }
       if (l == 0) st[qi].stat[mt] = (uint32_t)span | ((uint32_t)lo << 8) | ((uint32_t)hi << 16);
     }
   }
@@ -454,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
     for (int qi = 0; qi < qt; ++qi) {
       const QStage<MT>& sq = st[qi];
       if (G * kPage >= sq.nvis) continue;  // uniform
-      const bool ex = score_page<MT>(sq, t, G, w + (int64_t)(q0 + qi) * HI, scores + (int64_t)(q0 + qi) * ld,
+      const bool ex = score_any<MT>(sq, t, G, w + (int64_t)(q0 + qi) * HI, scores + (int64_t)(q0 + qi) * ld,
                                      lane, hist_on ? lh : nullptr);
       exact_bits |= (unsigned long long)ex << (i * qt + qi);
     }
@@ -491,8 +648,8 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
         const int page = block_table[(int64_t)sq.row * max_pages + G];
         const int64_t slot0 = (int64_t)page * kPage;
         KeyTile t;
-        load_keys(t, idx_codes, idx_scales, page, lane);
-        if (score_page<MT>(sq, t, G, w + (int64_t)(q0 + qi) * HI, scores + (int64_t)(q0 + qi) * ld, lane,
+        load_page<MT>(t, idx_codes, idx_scales, page, lane);
+        if (score_any<MT>(sq, t, G, w + (int64_t)(q0 + qi) * HI, scores + (int64_t)(q0 + qi) * ld, lane,
                            nullptr))
           exact_entry<MT>(sq, idx_codes, idx_scales, slot0 + lane, w + (int64_t)(q0 + qi) * HI,
                           scores + (int64_t)(q0 + qi) * ld + (int64_t)G * kPage + lane);
@@ -654,14 +811,7 @@ CSA2_DEV float q4_exact(const uint16_t* __restrict__ qrow, const float* __restri
   return acc;
 }
 
-typedef float v16f __attribute__((ext_vector_type(16)));
 
-template <int OA>
-CSA2_DEV v16f mfma32_fp4(const uint4& a, const uint4& b, const v16f& c, int asc, int bsc) {
-  const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-  const v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, OA, asc, 0, bsc);
-}
 
 // NM = Hi / 16 M-tiles; Hi <= 64 keeps a wavefront's operands and weights in registers.
 template <int NM>

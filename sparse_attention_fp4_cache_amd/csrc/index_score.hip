@@ -7,8 +7,10 @@
 // score[q][j] = fma-chain over h = 0..Hi-1 of w[q][h] * max(d_h, 0), starting at +0,
 // d_h = exact dot(qhat_h, khat_j) rounded once to fp32.
 //
-// Layout of the work.  A wavefront takes one page (64 consecutive entries) at a time
-// and, for each query of its tile, issues Hi/16 x 4 MFMAs
+// Layout of the work.  A wavefront takes one page (64 consecutive entries) at a time.
+// With Hi a multiple of 32 it issues, per 32-head tile and 32-entry tile, two chained
+//   V_MFMA_SCALE_F32_32X32X64_F8F6F4 (A = 32 query heads, B = 32 keys, K = 64 each)
+// (score_page32 below); otherwise Hi/16 x 4 MFMAs
 //   V_MFMA_SCALE_F32_16X16X128_F8F6F4 (A = 16 query heads, B = 16 keys, K = 128)
 // with E8M0 block scales, so one instruction produces 16x16 complete dot products.
 // Operand lane l holds row l%16 and the 32-channel block l/16: that is exactly one

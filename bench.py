@@ -6,9 +6,12 @@ entries, m = 2), batch 1, 64 heads, top-k 2048, 128-row bf16 window, and the
 selections + 10 attentions + the Full layer's cache write per step).  Inputs are
 seeded synthetic data already resident in HBM when timing starts.
 
-Cold mode is the headline: the step rotates over R copies of the cache whose
-total exceeds twice the 256 MB last-level (MALL) cache, so each step starts with
-its cache out of the MALL.  Warm mode (one copy, replayed) is reported beside it.
+Cold mode is the headline: the step rotates over R copies of the cache, with R
+chosen so that the bytes the other R - 1 copies' steps touch (indexer keys plus
+gathered rows) exceed twice the 256 MB last-level (MALL) cache: when a copy comes
+round again its bytes have been pushed out of the MALL.  Warm mode (one copy,
+replayed) is reported beside it, and so are the median and 10th / 90th percentile
+of single cold steps timed one by one with HIP events.
 
 Prints ONE JSON line: tokens/s (sequences / step time), the FP4 cache bytes read
 per step and their rate, a roofline record for the indexer scan (the kernel that
@@ -55,7 +58,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", type=int, default=1, help="replay the step as one HIP graph (1) or launch eagerly (0)")
     p.add_argument("--replicas", type=int, default=0,
-                   help="cache copies rotated in cold mode (0: enough to exceed twice the MALL)")
+                   help="cache copies rotated in cold mode (0: enough that the other copies' touched bytes "
+                        "exceed twice the MALL)")
+    p.add_argument("--dist-steps", type=int, default=200,
+                   help="single cold steps timed one by one for the median and p10 / p90")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="after timing, run one plain device copy of this size (counter calibration)")
     return p.parse_args()
@@ -112,6 +118,39 @@ def fp4_bytes_per_step(wl):
         b = sum(1 for m in wl.layers if m in ("full", "reindex")) * sum(n) * IDX_ENTRY_BYTES
     b += len(wl.layers) * sum(min(wl.K, x) for x in n) * MAIN_ENTRY_BYTES
     return b
+
+
+def touched_bytes_per_step(wl):
+    """Cache bytes one step reads from one cache copy: the indexer keys every index
+    layer scans (each layer scans the same keys, so they count once) plus the main
+    rows the attentions gather (at most k per index layer and sequence)."""
+    if wl.kind == "schedule":
+        b = 0
+        for w in wl.writers():
+            n = int(wl.cache_workload(w).n_entries[0])
+            layers = [li for li in range(len(wl.modes)) if wl.source(li) == w]
+            idx_layers = sum(1 for li in layers if wl.modes[li] in ("full", "reindex"))
+            b += n * IDX_ENTRY_BYTES + idx_layers * min(wl.K, n) * MAIN_ENTRY_BYTES
+        return b
+    if wl.kind == "prefill":
+        n = int(wl.n_entries[0]) + wl.n_chunk_entries
+        return n * (IDX_ENTRY_BYTES + MAIN_ENTRY_BYTES)
+    n = [int(x) for x in wl.n_entries]
+    idx_layers = sum(1 for m in wl.layers if m in ("full", "reindex"))
+    return sum(n) * IDX_ENTRY_BYTES + idx_layers * sum(min(wl.K, x) for x in n) * MAIN_ENTRY_BYTES
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(wl):
@@ -238,8 +277,10 @@ def main():
     st = Step(wl, dev)
     st.build_cache()
     torch.cuda.synchronize()
-    R = args.replicas if args.replicas > 0 else 1 + math.ceil(2 * MALL_BYTES / st.cache_bytes())
-    R = max(1, min(R, 16))
+    touched = touched_bytes_per_step(wl)
+    R = args.replicas if args.replicas > 0 else 1 + math.ceil(2 * MALL_BYTES / touched)
+    # copies of the whole cache: at most 32 and 64 GB of HBM
+    R = max(1, min(R, 32, (64 << 30) // max(1, st.cache_bytes())))
     steps = [st] + [st.replica() for _ in range(R - 1)]
     torch.cuda.synchronize()
 
@@ -280,6 +321,23 @@ def main():
     # ---- timed region: K whole steps, cold (rotating cache copies), then warm
     ms_per_step = timed(args.steps, rotate=True)
     warm_ms = timed(args.steps, rotate=False)
+
+    # ---- single cold steps, each between two HIP events on the step's stream
+    def step_dist(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            evs[0].record(stream)
+            for i in range(n):
+                one_step(i, i % R)
+                evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        t = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(n))
+        pick = lambda f: t[min(n - 1, int(round(f * (n - 1))))]
+        return {"n": n, "median_ms": pick(0.5), "p10_ms": pick(0.1), "p90_ms": pick(0.9), "min_ms": t[0],
+                "max_ms": t[-1]}
+
+    dist = step_dist(max(1, args.dist_steps)) if args.dist_steps > 0 else None
 
     # ---- each library call alone: back-to-back launches over the same inputs as the
     # step (every layer, every cache copy), captured in a graph and timed with HIP
@@ -353,11 +411,13 @@ def main():
                 lib.index_topk_pool, s.cache, L["q_idx"], L["w"], s.n_visible, st.pool, s.block_table,
                 st.scores_pool, wl.K, L["topk"], st.ws_topk_pool)
                 for s in steps for L in st.layers if L["mode"] == "reindex"])[0] * 1e3
+        # layer-major over the copies: consecutive calls never read the same copy, so
+        # each call finds its keys out of the MALL (cold), as in the step
         scan = [functools.partial(lib.index_score, s.cache, L["q_idx"], L["w"], s.n_visible, s.block_table, s.scores)
-                for s in steps for L in idx_layers]
+                for L in idx_layers for s in steps]
         calls_us["index_topk"] = burst_ms([functools.partial(lib.index_topk, s.cache, L["q_idx"], L["w"], s.n_visible,
                                                              s.block_table, s.scores, wl.K, L["topk"], s.ws_topk)
-                                           for s in steps for L in idx_layers])[0] * 1e3
+                                           for L in idx_layers for s in steps])[0] * 1e3
         calls_us["topk_select"] = burst_ms([functools.partial(lib.topk_select, st.scores, st.n_visible, wl.K,
                                                               L["topk"], st.ws_topk) for L in idx_layers])[0] * 1e3
         if wl.fp8_window:
@@ -418,7 +478,9 @@ def main():
                    "batch": wl.B, "heads": wl.H, "index_heads": wl.Hi, "topk": wl.K, "window": wl.W,
                    "layers": (",".join(wl.layers) if wl.kind in ("decode", "schedule")
                               else f"prefill chunk {wl.chunk}"),
-                   "hip_graph": bool(args.graph), "cache_copies_rotated": R},
+                   "hip_graph": bool(args.graph), "cache_copies_rotated": R,
+                   "touched_bytes_per_copy_step": touched},
+        "cold_step_distribution": dist,
         "warm_ms_per_step": warm_ms,
         "warm_tokens_per_s": tokens / (warm_ms * 1e-3),
         "fp4_bytes_per_step": step_bytes,
@@ -452,6 +514,7 @@ def main():
                                       "flop_per_launch": attn_flop}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)
+        res["cpu_baseline"]["cpu_model"] = cpu_model()
     print(json.dumps(res), flush=True)
 
 

@@ -20,8 +20,9 @@
  * Conventions for every entry point:
  *   - Array arguments and every pointer inside csa2_fp4_cache are DEVICE pointers,
  *     allocated and owned by the caller.  The cache descriptor struct itself is a
- *     host struct.  The library allocates no memory, keeps no global state and
- *     never synchronises; work is enqueued on `stream` in order.
+ *     host struct.  The library allocates no memory and never synchronises; work
+ *     is enqueued on `stream` in order.  Its only global state is one diagnostic
+ *     counter per device (csa2_exact_path_count below).
  *   - Arguments are validated on the host before anything is enqueued, so a bad
  *     argument returns a negative csa2_status and enqueues nothing.  A failed
  *     launch returns CSA2_ERR_LAUNCH (work enqueued before it may have run).
@@ -264,6 +265,19 @@ int sparse_attn_prefill_chunk_fp8win(const csa2_fp4_cache* cache, const uint16_t
                                      const uint8_t* swa_scales, int32_t swa_first_valid, int32_t window,
                                      float softmax_scale, float* out, float* lse, void* ws, size_t ws_bytes,
                                      hipStream_t stream);
+
+/* Diagnostic: the number of (query, entry) index scores that were recomputed on the
+ * exact integer path since the last csa2_exact_path_reset(), on the current device.
+ * index_score, index_topk and index_topk_pool take an entry's score from the FP4
+ * matrix unit only when every partial sum of each head's dot is exactly
+ * representable in fp32 (the per-block exponent sums span at most 10 and stay in
+ * fp32's normal range, so the result is the exact dot); other entries are
+ * recomputed from the definition, with identical results either way.  Both calls
+ * are synchronous with respect to the device; the count covers work enqueued and
+ * finished before the call.  count NULL: CSA2_ERR_NULL; a HIP failure:
+ * CSA2_ERR_LAUNCH. */
+int csa2_exact_path_count(unsigned long long* count);
+int csa2_exact_path_reset(void);
 
 #ifdef __cplusplus
 }

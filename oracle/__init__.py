@@ -85,6 +85,7 @@ def lib():
         L.oracle_global_bytes_per_token.argtypes = [_P, _P, _I32]
         L.oracle_global_bytes_per_token.restype = ctypes.c_double
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_causal_n_visible.argtypes = [_P, _I64, _I32, _P]
         _lib = L
     return _lib
 
@@ -139,6 +140,26 @@ def quant_mx32(x_bf16: np.ndarray):
     scales = np.zeros(x.shape[:-1], np.uint8)
     lib().oracle_quant_mx32(_ptr(x), nblk, _ptr(codes), _ptr(scales))
     return codes, scales
+
+
+# ------------------------------------------------------- causal visibility --
+def causal_n_visible(tokens, m: int) -> np.ndarray:
+    """Entries visible to a query at each token position: entry j (tokens m*j ..
+    m*j+m-1) is visible once its last token is at or before the query's."""
+    tok = _arr(tokens, np.int64).reshape(-1)
+    out = np.zeros(tok.shape[0], np.int32)
+    lib().oracle_causal_n_visible(_ptr(tok), tok.shape[0], int(m), _ptr(out))
+    return out
+
+
+def decode_n_visible(ctx, m: int) -> np.ndarray:
+    """A decode query is the last token of its context (token ctx - 1)."""
+    return causal_n_visible(np.asarray(ctx, np.int64) - 1, m)
+
+
+def prefill_n_visible(prefix_tokens: int, T: int, m: int) -> np.ndarray:
+    """Query i of a chunk after `prefix_tokens` tokens sits at token prefix_tokens + i."""
+    return causal_n_visible(int(prefix_tokens) + np.arange(T, dtype=np.int64), m)
 
 
 # ------------------------------------------------------------------ cache --

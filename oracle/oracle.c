@@ -211,6 +211,24 @@ static int64_t slot_of(const int32_t* block_table, int32_t max_pages, int32_t pa
   return (int64_t)block_table[(int64_t)row * max_pages + j / page_size] * page_size + j % page_size;
 }
 
+/* ------------------------------------------------------- causal visibility -- */
+
+/* Entries a query at token t may read ([EXP] CSA2 section: an entry compresses a
+ * disjoint group of m consecutive tokens; intro: a token attends only to tokens at or
+ * before it).  Entry j covers tokens m*j .. m*j + m - 1, so it exists for the query
+ * at t once its last token m*j + m - 1 is at or before t.  The visible entries are
+ * the prefix j = 0 .. J - 1 with J the number of j >= 0 satisfying
+ *   m*j + m - 1 <= t   <=>   j <= (t + 1)/m - 1   <=>   j < floor((t + 1)/m),
+ * so J = floor((t + 1)/m) (0 for t < m - 1).  A decode query is the context's last
+ * token (t = ctx - 1); query i of a prefill chunk after a prefix of P tokens is at
+ * t = P + i.  out[i] = J for token tok[i] (tok[i] >= -1). */
+void oracle_causal_n_visible(const int64_t* tok, int64_t n, int32_t m, int32_t* out) {
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t t = tok[i];
+    out[i] = (int32_t)((t + 1) / m);
+  }
+}
+
 /* ------------------------------------------------------------ index score -- */
 
 /* Signed E2M1 value times 2, an integer in [-12, 12]. */

@@ -16,11 +16,17 @@
 // Operand lane l holds row l%16 and the 32-channel block l/16: that is exactly one
 // 16-byte slice of a packed key row plus its E8M0 byte, so each key row is fetched
 // with four coalesced 16-byte loads per lane group.
-// Measured on MI355X: the instruction returns the round-once exact dot whenever the
-// four per-block exponent sums (u_q + u_k) span at most 14; it loses low bits beyond
-// that.  Entries whose scales could exceed a span of 12 (or reach the fp32 subnormal
-// or overflow range) take an exact integer/fp64 path instead, so results are always
-// bit-identical to the definition.
+// Exactness.  A block of 32 products contributes S_b * 2^E_b with S_b an integer,
+// |S_b| <= 32 * 12 * 12 = 4608 (products of twice-E2M1 values), and E_b the block's
+// exponent sum u_q + u_k - 256.  When the four E_b span at most s, one block sits at
+// the lowest exponent E and every partial sum of the dot is an integer multiple of
+// 2^E below 4608 * (1 + 3 * 2^s) * 2^E in magnitude, which is under 2^24 * 2^E for
+// s <= 10: every partial sum is then exactly representable in fp32, so the matrix
+// unit's result is the exact dot whatever order or width it accumulates in (also
+// for the two chained K = 64 instructions of the 32x32x64 form), and the one
+// rounding of the definition is the identity.  Entries outside that window (or
+// near the fp32 subnormal or overflow range) take an exact integer/fp64 path, so
+// results are always bit-identical to the definition.
 // The query heads are permuted across MFMA rows so that lane group g ends up holding
 // a contiguous run of Hi/4 heads; a 4x4 transpose across lane groups with
 // v_permlane32_swap / v_permlane16_swap then leaves every lane with one entry and
@@ -36,9 +42,14 @@ namespace csa2 {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kMaxSpread = 12;   // exponent-sum span accepted on the MFMA path
+constexpr int kMaxSpread = 10;   // exponent-sum span accepted on the MFMA path (every partial sum exact)
 constexpr int kMinExpSum = 130;  // keeps every nonzero dot >= 2^-126 (fp32 normal)
 constexpr int kMaxExpSum = 360;  // keeps every dot far below fp32 overflow
+// (query, entry) scores recomputed on the exact path since the last reset, on this
+// device (a diagnostic: the exact path is rare, so the atomics cost nothing measurable)
+__device__ unsigned long long g_exact_path_count = 0ull;
+CSA2_DEV void count_exact_path() { atomicAdd(&g_exact_path_count, 1ull); }
+
 constexpr int kMaxPagesPerWave = 4;  // pages (of 64 entries) one wavefront scans, all prefetched
 constexpr int kWaves = 8;             // wavefronts per workgroup (they share one query staging)
 constexpr int kThreads = 64 * kWaves;
@@ -346,7 +357,7 @@ __device__ __attribute__((always_inline)) inline bool score_page(const QStage<MT
 // v_permlane32_swap per register pair of the two entry tiles then leaves lane l with
 // entry l of the page: rows 8q + i in the first register of the pair and 8q + 4 + i in
 // the second, so the fma chain reads every head in ascending order.  The exactness
-// window is the one of score_page (the two K halves add exactly inside it).
+// window is the one of score_page: inside it both K halves and their sum are exact.
 template <int MT>
 __device__ __attribute__((always_inline)) inline bool score_page32(const QStage<MT>& s, const KeyTile& cur, int G,
                                                                    const float* __restrict__ wq,
@@ -638,6 +649,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
                                 : (int64_t)page_of(i) * kPage + lane;
       const float e = exact_entry<MT>(st[qi], idx_codes, idx_scales, slot, w + (int64_t)(q0 + qi) * HI,
                                       scores + (int64_t)(q0 + qi) * ld + (int64_t)(gfirst + i) * kPage + lane);
+      count_exact_path();
       if (HIST && hist_on) atomicAdd(&lh[score_key(e) >> kTopkBinShift], 1u);
     }
   } else {
@@ -652,9 +664,11 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
         KeyTile t;
         load_page<MT>(t, idx_codes, idx_scales, page, lane);
         if (score_any<MT>(sq, t, G, w + (int64_t)(q0 + qi) * HI, scores + (int64_t)(q0 + qi) * ld, lane,
-                           nullptr))
+                           nullptr)) {
           exact_entry<MT>(sq, idx_codes, idx_scales, slot0 + lane, w + (int64_t)(q0 + qi) * HI,
                           scores + (int64_t)(q0 + qi) * ld + (int64_t)G * kPage + lane);
+          count_exact_path();
+        }
       }
     }
   }
@@ -1024,6 +1038,7 @@ __global__ __launch_bounds__(kThreads) void index_score_q2_kernel(
           const int64_t slot = (int64_t)bt[Gp] * kPage + e;
           srow[Gp * kPage + e] = q4_exact(qrow, w + (int64_t)qo * HI, HI, idx_codes + slot * kIdxRowBytes,
                                           *reinterpret_cast<const uint32_t*>(idx_scales + slot * kIdxScaleBytes));
+          count_exact_path();
         }
         // nothing of this rare branch stays in flight, so the waits after it count only
         // the staging loads and score stores of the common path
@@ -1054,9 +1069,12 @@ __global__ __launch_bounds__(kThreads) void index_score_q2_kernel(
   }
 }
 
-// Queries per workgroup of the scan (1 when every query reads its own sequence).
+// Queries per workgroup of the scan (1 when every query reads its own sequence, or
+// when four staged queries would not fit in 64 KB of LDS).
 static int query_tile(const int32_t* soq, int32_t nq, size_t stage_bytes) {
-  return (soq == nullptr || nq < 64) ? 1 : (stage_bytes * 8 <= 64 * 1024 ? 8 : 4);
+  if (soq == nullptr || nq < 64) return 1;
+  if (stage_bytes * 8 <= 64 * 1024) return 8;
+  return stage_bytes * 4 <= 64 * 1024 ? 4 : 1;
 }
 
 // Pool scans (pool != nullptr) take one query per workgroup over virtual pages of
@@ -1109,7 +1127,7 @@ static int launch_mt(const csa2_fp4_cache* c, const uint16_t* q_idx, const float
     hipLaunchKernelGGL((index_score_kernel<MT, 4, false>), grid, block, lds, stream, c->idx_codes, c->idx_scales,
                        q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k, ncopies,
                        nullptr, 0, nullptr);
-  } else if ((long long)gx * qtiles > 256) {
+  } else if ((long long)gx * qtiles > device_cu_count()) {
     // one query per workgroup, more workgroups than CUs: the counting kernel with its
     // counts switched off (no histogram, k past every row), whose register allocation
     // leaves room for two workgroups per CU where the plain variant's does not
@@ -1193,6 +1211,22 @@ static int check_args(const csa2_fp4_cache* cache, const uint16_t* q_idx, const 
 }  // namespace csa2
 
 using namespace csa2;
+
+extern "C" int csa2_exact_path_count(unsigned long long* count) {
+  if (count == nullptr) return CSA2_ERR_NULL;
+  return hipMemcpyFromSymbol(count, HIP_SYMBOL(g_exact_path_count), sizeof(*count), 0, hipMemcpyDeviceToHost) ==
+                 hipSuccess
+             ? CSA2_OK
+             : CSA2_ERR_LAUNCH;
+}
+
+extern "C" int csa2_exact_path_reset(void) {
+  const unsigned long long zero = 0ull;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_exact_path_count), &zero, sizeof(zero), 0, hipMemcpyHostToDevice) ==
+                 hipSuccess
+             ? CSA2_OK
+             : CSA2_ERR_LAUNCH;
+}
 
 extern "C" int index_score(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
                            const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* block_table,

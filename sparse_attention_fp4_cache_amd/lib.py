@@ -40,6 +40,8 @@ EXPORTS = (
     "swa_fp8_write",
     "sparse_attn_decode_fp8win",
     "sparse_attn_prefill_chunk_fp8win",
+    "csa2_exact_path_count",
+    "csa2_exact_path_reset",
 )
 
 
@@ -104,6 +106,8 @@ def load() -> ctypes.CDLL:
         L.sparse_attn_prefill_chunk_fp8win.argtypes = [ctypes.POINTER(_CacheStruct), _P, _I32, _P, _I32, _P, _I32,
                                                        _I64, _I32, _P, _P, _I32, _I32, ctypes.c_float, _P, _P, _P,
                                                        _SZ, _P]
+        L.csa2_exact_path_count.argtypes = [ctypes.POINTER(ctypes.c_ulonglong)]
+        L.csa2_exact_path_reset.argtypes = []
         for name in EXPORTS:
             if name not in ("csa2_status_string",) and not name.endswith("_size"):
                 getattr(L, name).restype = ctypes.c_int
@@ -365,6 +369,18 @@ def sparse_attn_prefill_chunk_fp8win(cache: Cache, q: torch.Tensor, topk_idx: to
         _ptr(swa_codes, torch.uint8, "swa_codes"), _ptr(swa_scales, torch.uint8, "swa_scales"),
         int(swa_first_valid), int(window), float(softmax_scale), _ptr(out, torch.float32, "out"),
         _ptr(lse, torch.float32, "lse"), _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+
+
+def exact_path_count() -> int:
+    """Index scores recomputed on the exact integer path since the last reset (current
+    device; synchronous)."""
+    n = ctypes.c_ulonglong(0)
+    _check("csa2_exact_path_count", load().csa2_exact_path_count(ctypes.byref(n)))
+    return int(n.value)
+
+
+def exact_path_reset() -> None:
+    _check("csa2_exact_path_reset", load().csa2_exact_path_reset())
 
 
 def default_softmax_scale() -> float:

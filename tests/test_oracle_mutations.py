@@ -57,6 +57,8 @@ MUTATIONS = [
     ("pool top-k reports pool positions", "all[m].j = j;", "all[m].j = p;"),
     ("fp8 window scale twice too large", "while (ldexp(448.0, e) < amax) ++e;", "while (ldexp(224.0, e) < amax) ++e;"),
     ("fp8 window ties to the odd byte", "(d == bestd && !(b & 1) && (best & 1))", "(d == bestd)"),
+    ("visibility from t // m", "out[i] = (int32_t)((t + 1) / m);", "out[i] = (int32_t)(t / m);"),
+    ("visibility one entry early", "out[i] = (int32_t)((t + 1) / m);", "out[i] = (int32_t)((t + m) / m);"),
     ("fp8 window drops the sign", "(uint8_t)((signbit(v) ? 0x80 : 0) | e4m3_nearest(", "(uint8_t)((0) | e4m3_nearest("),
 ]
 

@@ -511,3 +511,92 @@ def test_bounded_replay_window_is_the_replayed_segment():
         o, l = oracle.sparse_attn_decode(c, q[i:i + 1], idx[i:i + 1], bt[None, :], win,
                                          np.array([len(rows)], np.int32), 0.04)
         assert np.array_equal(o[0], out[i]) and np.array_equal(l[0], lse[i])
+
+
+# ------------------------------------------------- causal visibility -------
+def test_causal_visibility_brute_force_in_token_coordinates():
+    """Entry j compresses the disjoint group of tokens m*j .. m*j+m-1 and a query at
+    token t may read an entry only once every token of its group is at or before t
+    ("DeepSeek-V4.1-Flash, expliqué pas à pas": CSA2 section, disjoint groups of m
+    tokens; intro, causal attention).  Built here from the token sets themselves."""
+    for m in (1, 2, 3, 4, 7):
+        n_tokens = 64 * m + 5
+        groups = [set(range(m * j, m * j + m)) for j in range(n_tokens // m + 2)]
+        toks = np.arange(-1, n_tokens, dtype=np.int64)
+        got = oracle.causal_n_visible(toks, m)
+        for t, g in zip(toks, got):
+            visible = [j for j, grp in enumerate(groups) if max(grp) <= t]
+            # the visible entries are a prefix 0 .. J-1 of the entry order
+            assert visible == list(range(len(visible))), (m, t)
+            assert int(g) == len(visible), (m, int(t), int(g), len(visible))
+
+
+def test_causal_visibility_of_the_workload_positions():
+    # decode: the query is the context's last token, so every complete group is read;
+    # a prefill query at t = P + i reads one more entry each time t + 1 is a multiple of m
+    assert np.array_equal(oracle.decode_n_visible([4096, 131072, 4097], 2), [2048, 65536, 2048])
+    nv = oracle.prefill_n_visible(262144, 6, 2)
+    assert np.array_equal(nv, [131072, 131073, 131073, 131074, 131074, 131075])
+    assert np.array_equal(oracle.prefill_n_visible(10, 5, 1), [11, 12, 13, 14, 15])
+    # the chunk's first token completes no group of m = 2 on an even prefix
+    assert oracle.prefill_n_visible(8, 1, 2)[0] == 4
+
+
+# --------------------------------------- exhaustive element rounding -------
+def _exact_nearest_codes(vals_f32: np.ndarray, scale: Fraction) -> np.ndarray:
+    """Exact-rational nearest E2M1 magnitude of |v| / scale (ties to the even index,
+    clipping at 6), sign bit copied: written from the definition with Fractions."""
+    out = np.zeros(vals_f32.size, np.uint8)
+    mags = [Fraction(m) for m in E2M1]
+    for i, v in enumerate(vals_f32.tolist()):
+        r = abs(Fraction(v)) / scale
+        best, bestd = 0, None
+        for c, mg in enumerate(mags):
+            d = abs(mg - r)
+            if bestd is None or d < bestd or (d == bestd and c % 2 == 0 and best % 2 == 1):
+                best, bestd = c, d
+        out[i] = best | (8 if math.copysign(1.0, v) < 0 else 0)
+    return out
+
+
+def _all_finite_bf16_up_to(limit: float) -> np.ndarray:
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = bf16_bits_to_f32(allb)
+    return allb[np.isfinite(f) & (np.abs(f) <= limit)]
+
+
+@pytest.mark.parametrize("block_max,scale_byte,scale", [
+    (6.0, 0x38, Fraction(1)),                # E4M3 1.0
+    (6.75, 0x39, Fraction(9, 8)),            # E4M3 1.125: thresholds t*s off the power-of-two grid
+    (6.0 * 2.0 ** -6, 0x08, Fraction(1, 64)),  # the smallest normal E4M3 scale
+    (6.0 * 3 * 2.0 ** -9, 0x03, Fraction(3, 512)),  # a subnormal E4M3 scale
+])
+def test_exhaustive_bf16_nv16_element_rule(block_max, scale_byte, scale):
+    """Every finite bf16 value v with |v| <= 6 s, as a non-max element of an NV16 block
+    whose scale is s, against the exact-rational rule."""
+    vals = _all_finite_bf16_up_to(float(6 * scale))
+    blocks = np.zeros((vals.size, 16), np.uint16)
+    blocks[:, 0] = to_bf16_bits(np.float32([block_max]))[0]
+    blocks[:, 1] = vals
+    codes, sc = oracle.quant_nv16(blocks)
+    assert np.all(sc == scale_byte)
+    want = _exact_nearest_codes(bf16_bits_to_f32(vals), scale)
+    bad = np.flatnonzero(codes[:, 1] != want)
+    assert len(bad) == 0, (len(bad), float(bf16_bits_to_f32(vals[bad[0]])), codes[bad[0], 1], want[bad[0]])
+
+
+@pytest.mark.parametrize("block_max,u", [(7.5, 127), (-4.0, 127), (7.5 * 2.0 ** -100, 27), (6.0 * 2.0 ** 100, 227)])
+def test_exhaustive_bf16_mx32_element_rule(block_max, u):
+    """Every finite bf16 value v with |v| <= |block max| as a non-max element of an MX32
+    block with X = 2^(u - 127), against the exact-rational rule (values in (6X, 8X)
+    clip to 6)."""
+    X = Fraction(2) ** (u - 127)
+    vals = _all_finite_bf16_up_to(abs(block_max))
+    blocks = np.zeros((vals.size, 32), np.uint16)
+    blocks[:, 0] = to_bf16_bits(np.float32([block_max]))[0]
+    blocks[:, 1] = vals
+    codes, sc = oracle.quant_mx32(blocks)
+    assert np.all(sc == u)
+    want = _exact_nearest_codes(bf16_bits_to_f32(vals), X)
+    bad = np.flatnonzero(codes[:, 1] != want)
+    assert len(bad) == 0, (len(bad), float(bf16_bits_to_f32(vals[bad[0]])), codes[bad[0], 1], want[bad[0]])

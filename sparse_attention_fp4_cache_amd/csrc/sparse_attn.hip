@@ -658,35 +658,34 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
 }
 
 // Combine the row ranges of one (query, head): out = sum_s 2^(m_s-M) O_s / L.
-// Four wavefronts per (query, head), each owning 128 channels (two per lane).  With
-// at most B <= 64 ranges a wavefront issues the loads of every range's O_s at once
-// (unconditional: addresses past the last range are clamped to it, weight 0)
-// together with lane s's (m_s, l_s), takes M and L with wave reductions, and sums
-// the ranges in index order with one fma chain per channel: one round of loads, no
-// LDS, no barrier.  More ranges take rounds of 64.
-constexpr int kMergeThreads = 256;
+// One wavefront per workgroup, kMergeSlices workgroups per (query, head), each owning
+// 64 channels (one per lane): a workgroup then reads ns * 256 bytes of partials, where
+// one per (query, head) read ns * 2 KB and was held back by how many loads one
+// compute unit keeps in flight.  With at most B <= 64 ranges the wavefront issues the
+// loads of every range's O_s at once (unconditional: addresses past the last range
+// are clamped to it, weight 0) together with lane s's (m_s, l_s), takes M and L with
+// wave reductions, and sums the ranges in index order with one fma chain per channel:
+// one round of loads, no LDS, no barrier.  More ranges take rounds of B.
+constexpr int kMergeThreads = 64;
+constexpr int kMergeSlices = kLatentDim / kMergeThreads;
 template <int B>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
-  const int head = blockIdx.x, qrow = blockIdx.y;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int head = blockIdx.x / kMergeSlices, slice = blockIdx.x % kMergeSlices, qrow = blockIdx.y;
+  const int lane = threadIdx.x;
   const int ns = a.nsplit;
   const int64_t base = (int64_t)qrow * ns * a.H + head;  // + s * H
-  const float2* po = reinterpret_cast<const float2*>(a.part_o) + 64 * wv + lane;  // + pidx * 256
+  const float* po = a.part_o + kMergeThreads * slice + lane;  // + pidx * 512
   auto ml_of = [&](int s) { return *reinterpret_cast<const float2*>(a.part_ml + 2 * (base + (int64_t)s * a.H)); };
-  float2 o = make_float2(0.f, 0.f);
+  float o = 0.0f;
   float M, L = 0.0f;
-  auto accumulate = [&](const float2 (&v)[B], float w) {
+  auto accumulate = [&](const float (&v)[B], float w) {
 #pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
-      o.x = fmaf(v[u].x, wu, o.x);
-      o.y = fmaf(v[u].y, wu, o.y);
-    }
+    for (int u = 0; u < B; ++u) o = fmaf(v[u], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u)), o);
   };
   if (ns <= B) {
-    float2 v[B];
+    float v[B];
 #pragma unroll
-    for (int u = 0; u < B; ++u) v[u] = po[(base + (int64_t)min(u, ns - 1) * a.H) * (kLatentDim / 2)];
+    for (int u = 0; u < B; ++u) v[u] = po[(base + (int64_t)min(u, ns - 1) * a.H) * kLatentDim];
     const float2 ml = lane < ns ? ml_of(lane) : make_float2(-INFINITY, 0.0f);
     M = wave_max(ml.x);
     const float w = (ml.x == -INFINITY) ? 0.0f : fast_exp2(ml.x - M);
@@ -698,9 +697,9 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
       if (s0 + lane < ns) M = fmaxf(M, ml_of(s0 + lane).x);
     M = wave_max(M);
     for (int s0 = 0; s0 < ns; s0 += B) {
-      float2 v[B];
+      float v[B];
 #pragma unroll
-      for (int u = 0; u < B; ++u) v[u] = po[(base + (int64_t)min(s0 + u, ns - 1) * a.H) * (kLatentDim / 2)];
+      for (int u = 0; u < B; ++u) v[u] = po[(base + (int64_t)min(s0 + u, ns - 1) * a.H) * kLatentDim];
       const float2 ml = (lane < B && s0 + lane < ns) ? ml_of(s0 + lane) : make_float2(-INFINITY, 0.0f);
       const float w = (ml.x == -INFINITY) ? 0.0f : fast_exp2(ml.x - M);
       L += wave_sum(ml.y * w);
@@ -708,13 +707,13 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     }
   }
   const float inv = (L > 0.0f) ? __builtin_amdgcn_rcpf(L) : 0.0f;
-  reinterpret_cast<float2*>(a.out + ((int64_t)qrow * a.H + head) * kLatentDim)[64 * wv + lane] =
-      make_float2(o.x * inv, o.y * inv);
-  if (threadIdx.x == 0) a.lse[(int64_t)qrow * a.H + head] = (L > 0.0f) ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
+  a.out[((int64_t)qrow * a.H + head) * kLatentDim + kMergeThreads * slice + lane] = o * inv;
+  if (slice == 0 && lane == 0)
+    a.lse[(int64_t)qrow * a.H + head] = (L > 0.0f) ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
 }
 
 static void launch_merge(const AttnArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.H, (unsigned)a.nq), block(kMergeThreads);
+  const dim3 grid((unsigned)(a.H * kMergeSlices), (unsigned)a.nq), block(kMergeThreads);
   const int ns = a.nsplit;
   if (ns <= 8) hipLaunchKernelGGL(attn_merge_kernel<8>, grid, block, 0, stream, a);
   else if (ns <= 16) hipLaunchKernelGGL(attn_merge_kernel<16>, grid, block, 0, stream, a);

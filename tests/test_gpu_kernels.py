@@ -595,6 +595,68 @@ def test_index_topk_fused_exact_path_entries():
     _fused_vs_separate(np.random.default_rng(301), [6000], 16, 512, key_fn=keys)
 
 
+def test_index_topk_best_entries_crowd_one_range():
+    """The best 3000 entries first, then last, in a row of 300,000: one range of the
+    row holds the whole top k (every other chunk of the selection lists nothing)."""
+    def first(k):
+        k[:3000] *= 3.0
+        return k
+
+    def last(k):
+        k[-3000:] *= 3.0
+        return k
+
+    say("case: index_topk, best entries crowded at the start of a 300K row")
+    _fused_vs_separate(np.random.default_rng(303), [300000], 64, 2048, key_fn=first, reps=1)
+    say("case: index_topk, best entries crowded at the end of a 300K row")
+    _fused_vs_separate(np.random.default_rng(304), [300000], 64, 2048, key_fn=last, reps=1)
+
+
+def test_index_topk_all_scores_tied():
+    """Every key equal, so every score ties: the threshold bin holds every entry and
+    overflows the candidate lists; ties go to the lower index."""
+    def same(k):
+        k[:] = k[0]
+        return k
+
+    say("case: index_topk, all scores tied in a 100K row and a 5K row")
+    _fused_vs_separate(np.random.default_rng(305), [100000, 5000], 64, 2048, key_fn=same, reps=1)
+
+
+def test_index_topk_long_rows_of_different_lengths():
+    """Rows of up to 1.1M entries (538 scan workgroups and 269 selection chunks per
+    query), eight queries of different lengths (two at or below k); keys drawn on the
+    device.  index_topk against index_score then topk_select, bit for bit."""
+    n_max, Hi, k = 1_100_000, 64, 2048
+    n = [n_max, 900_000, 524_288, 70_000, 2048, 1000, 300_001, 4097]
+    pages = (n_max + 63) // 64
+    g = lib.Cache(pages * 64)
+    gen = torch.Generator(device="cuda").manual_seed(306)
+    key = torch.randn((pages * 64, 128), device="cuda", generator=gen).to(torch.bfloat16).view(torch.int16)
+    lat = torch.zeros((pages * 64, 512), dtype=torch.int16, device="cuda")
+    lib.fp4_cache_write(g, lat, key, torch.arange(pages * 64, dtype=torch.int64, device="cuda"))
+    del lat, key
+    nq = len(n)
+    q = torch.randn((nq, Hi, 128), device="cuda", generator=gen).to(torch.bfloat16).view(torch.int16)
+    w = torch.rand((nq, Hi), device="cuda", generator=gen)
+    nvis = torch.tensor(n, dtype=torch.int32, device="cuda")
+    bt = torch.arange(pages, dtype=torch.int32, device="cuda").repeat(nq, 1)
+    ld = pages * 64
+    ws = torch.zeros(lib.topk_select_workspace_size(nq, ld, k), dtype=torch.uint8, device="cuda")
+    s_sep = torch.full((nq, ld), float("nan"), device="cuda")
+    i_sep = torch.full((nq, k), -7, dtype=torch.int32, device="cuda")
+    say(f"case: index_topk over rows of up to {n_max} entries ({nq} queries)")
+    lib.index_score(g, q, w, nvis, bt, s_sep)
+    lib.topk_select(s_sep, nvis, k, i_sep, ws)
+    s_f = torch.full((nq, ld), float("nan"), device="cuda")
+    i_f = torch.full((nq, k), -7, dtype=torch.int32, device="cuda")
+    lib.index_topk(g, q, w, nvis, bt, s_f, k, i_f, ws)
+    torch.cuda.synchronize()
+    for r in range(nq):
+        assert torch.equal(s_f[r, :n[r]].view(torch.int32), s_sep[r, :n[r]].view(torch.int32)), f"row {r} scores"
+    assert torch.equal(i_f, i_sep), "top-k differs"
+
+
 def test_index_topk_query_tiles_fall_back():
     say("case: index_topk with a sequence map and 70 queries (tiles of queries, separate counting pass)")
     _fused_vs_separate(np.random.default_rng(302), [5000, 3000], 32, 128, seq_of_query=[0] * 40 + [1] * 30)

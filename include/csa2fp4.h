@@ -22,7 +22,8 @@
  *     allocated and owned by the caller.  The cache descriptor struct itself is a
  *     host struct.  The library allocates no memory and never synchronises; work
  *     is enqueued on `stream` in order.  Its only global state is one diagnostic
- *     counter per device (csa2_exact_path_count below).
+ *     counter per device (csa2_exact_path_count below) and the static workspace of
+ *     index_topk_noalloc.
  *   - Arguments are validated on the host before anything is enqueued, so a bad
  *     argument returns a negative csa2_status and enqueues nothing.  A failed
  *     launch returns CSA2_ERR_LAUNCH (work enqueued before it may have run).
@@ -148,6 +149,25 @@ int index_topk(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* 
                const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* block_table, int32_t max_pages,
                int32_t nq, float* scores, int64_t ld, int32_t k, int32_t* topk_idx, void* ws, size_t ws_bytes,
                hipStream_t stream);
+
+/* index_topk_noalloc -- index_topk for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid it.  The
+ * same arguments without ws / ws_bytes and the same results (bit for bit): the
+ * selection's workspace is a static array of CSA2_NOALLOC_SCRATCH_BYTES in device
+ * memory, one per device, held until the process ends.  Calls that need more
+ * (topk_select_workspace_size(nq, ld, k) > CSA2_NOALLOC_SCRATCH_BYTES; 1M-entry rows
+ * take about 0.37 MB per query) return CSA2_ERR_WORKSPACE and enqueue nothing.  The
+ * call allocates nothing (no hipMalloc, no library allocation); it clears the array's
+ * counters with a kernel (no memset node, so it may be captured into a graph).  All
+ * calls on one device share the array: calls that overlap on one device (different
+ * streams, not ordered) race and give undefined results; calls on one stream are
+ * safe.  The array's device address is looked up on the first call on each device.
+ * A HIP failure in that lookup returns CSA2_ERR_LAUNCH. */
+#define CSA2_NOALLOC_SCRATCH_BYTES (32u << 20)
+int index_topk_noalloc(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
+                       const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* block_table,
+                       int32_t max_pages, int32_t nq, float* scores, int64_t ld, int32_t k, int32_t* topk_idx,
+                       hipStream_t stream);
 
 /* Hierarchical candidate pool.
  * Source: "DeepSeek V4.1 Flash et le cerveau divisé", memory section (the first

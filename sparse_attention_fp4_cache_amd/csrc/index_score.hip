@@ -36,6 +36,7 @@
 #include "topk_internal.hpp"
 
 #include <algorithm>
+#include <mutex>
 
 namespace csa2 {
 
@@ -1257,6 +1258,49 @@ extern "C" int index_topk(const csa2_fp4_cache* cache, const uint16_t* q_idx, co
     if (st != CSA2_OK) return st;
   }
   return topk_enqueue(scores, ld, n_visible, nq, k, topk_idx, ws, stream, fuse, copies, nullptr, 0);
+}
+
+// ---- index_topk without allocation: the workspace in a static device array --------
+// For callers that cannot allocate (code under graph capture, serving loops).  Each
+// device holds its own copy of `scratch` for the life of the process; its device
+// address comes from hipGetSymbolAddress, once per device, and only that address is
+// handed to kernels (the array's name in host code is a host-side stand-in).
+static __device__ __align__(256) unsigned char scratch[CSA2_NOALLOC_SCRATCH_BYTES];
+
+static int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return CSA2_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return CSA2_ERR_LAUNCH;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return CSA2_OK;
+}
+
+extern "C" int index_topk_noalloc(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
+                                  const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* block_table,
+                                  int32_t max_pages, int32_t nq, float* scores, int64_t ld, int32_t k,
+                                  int32_t* topk_idx, hipStream_t stream) {
+  int st = check_args(cache, q_idx, w, Hi, n_visible, block_table, max_pages, nq, scores, ld);
+  if (st != CSA2_OK) return st;
+  if (k < 1 || k > CSA2_MAX_K || ld >= ((int64_t)1 << 31)) return CSA2_ERR_SHAPE;
+  if (nq == 0) return CSA2_OK;
+  if (!topk_idx) return CSA2_ERR_NULL;
+  const size_t need = topk_select_workspace_size(nq, ld, k);
+  if (need > (size_t)CSA2_NOALLOC_SCRATCH_BYTES) return CSA2_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != CSA2_OK) return st;
+  // the array keeps the last call's bytes: its counters and histograms start at zero
+  st = zero_fill(ws, topk_zero_bytes(nq, ld), stream);
+  if (st != CSA2_OK) return st;
+  return index_topk(cache, q_idx, w, Hi, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, k,
+                    topk_idx, ws, need, stream);
 }
 
 // the pool workspace: visible pool positions per query, then the selection's workspace

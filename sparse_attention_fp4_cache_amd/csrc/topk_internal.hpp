@@ -29,4 +29,11 @@ int topk_enqueue(const float* scores, int64_t ld, const int32_t* n_visible, int3
                  int32_t* topk_idx, void* ws, hipStream_t stream, bool hist_done, int copies, const int32_t* pool,
                  int npool);
 
+// Bytes at the start of a top-k workspace for (nq, ld) that must be zero before a
+// call (its counters and histograms; a multiple of 256); the rest is scratch that
+// every call writes before reading.
+size_t topk_zero_bytes(int32_t nq, int64_t ld);
+// Enqueue a kernel that zeroes `bytes` (a multiple of 16) at p.
+int zero_fill(void* p, size_t bytes, hipStream_t stream);
+
 }  // namespace csa2

@@ -803,6 +803,26 @@ extern "C" size_t topk_select_workspace_size(int32_t nq, int64_t ld, int32_t k) 
 
 namespace csa2 {
 
+size_t topk_zero_bytes(int32_t nq, int64_t ld) {
+  (void)ld;  // the zeroed part (control words, digit-1 and digit-2 histograms) comes first in carve()
+  return align_up(sizeof(TopkCtl) * (size_t)nq) + align_up(sizeof(uint32_t) * kBins * kTopkHistCopies * (size_t)nq) +
+         align_up(sizeof(uint32_t) * kBins * (size_t)nq);
+}
+
+// Zero n16 16-byte words (a kernel, not a memset: it may be captured into a graph).
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* __restrict__ p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+int zero_fill(void* p, size_t bytes, hipStream_t stream) {
+  const size_t n16 = bytes / 16;  // callers pass multiples of 256 bytes
+  if (n16 == 0) return CSA2_OK;
+  const unsigned blocks = (unsigned)std::min<size_t>((n16 + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_fill_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<uint4*>(p), n16);
+  return launch_status();
+}
+
 uint32_t* topk_digit1_hist(void* ws, int32_t nq, int64_t ld) {
   const long long nchunk = ld > 0 ? (ld + kChunk - 1) / kChunk : 1;
   return carve(ws, nq, nchunk).hist;

@@ -40,6 +40,7 @@ EXPORTS = (
     "swa_fp8_write",
     "sparse_attn_decode_fp8win",
     "sparse_attn_prefill_chunk_fp8win",
+    "index_topk_noalloc",
     "csa2_exact_path_count",
     "csa2_exact_path_reset",
 )
@@ -106,6 +107,8 @@ def load() -> ctypes.CDLL:
         L.sparse_attn_prefill_chunk_fp8win.argtypes = [ctypes.POINTER(_CacheStruct), _P, _I32, _P, _I32, _P, _I32,
                                                        _I64, _I32, _P, _P, _I32, _I32, ctypes.c_float, _P, _P, _P,
                                                        _SZ, _P]
+        L.index_topk_noalloc.argtypes = [ctypes.POINTER(_CacheStruct), _P, _P, _I32, _P, _P, _P, _I32, _I32, _P,
+                                         _I64, _I32, _P, _P]
         L.csa2_exact_path_count.argtypes = [ctypes.POINTER(ctypes.c_ulonglong)]
         L.csa2_exact_path_reset.argtypes = []
         for name in EXPORTS:
@@ -237,6 +240,28 @@ def index_topk(cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, n_visible: to
                                            _ptr(scores, torch.float32, "scores"), scores.shape[1], k,
                                            _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(ws, torch.uint8, "ws"),
                                            ws.numel(), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # CSA2_NOALLOC_SCRATCH_BYTES
+
+
+def index_topk_noalloc(cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, n_visible: torch.Tensor,
+                       block_table: torch.Tensor, scores: torch.Tensor, k: int, topk_idx: torch.Tensor,
+                       seq_of_query: torch.Tensor | None = None, stream=None):
+    """index_topk with its workspace in the library's static per-device array (the call
+    allocates nothing); sizes past the array raise with CSA2_ERR_WORKSPACE."""
+    nq, Hi, d = q_idx.shape
+    if d != INDEX_DIM or w.shape != (nq, Hi) or n_visible.shape != (nq,) or scores.dim() != 2 or scores.shape[0] != nq:
+        raise ValueError("shape mismatch in index_topk_noalloc arguments")
+    if topk_idx.shape != (nq, k):
+        raise ValueError("topk_idx must be [nq, k]")
+    _check("index_topk_noalloc",
+           load().index_topk_noalloc(cache.struct, _bits16(q_idx, "q_idx"), _ptr(w, torch.float32, "w"), Hi,
+                                     _ptr(seq_of_query, torch.int32, "seq_of_query"),
+                                     _ptr(n_visible, torch.int32, "n_visible"),
+                                     _ptr(block_table, torch.int32, "block_table"), block_table.shape[1], nq,
+                                     _ptr(scores, torch.float32, "scores"), scores.shape[1], k,
+                                     _ptr(topk_idx, torch.int32, "topk_idx"), _stream(stream)))
 
 
 POOL_BLOCK = 8  # entries per candidate-pool block

@@ -208,3 +208,20 @@ def test_fp8_window_validation(L):
     assert pre(scales=None) == -1
     assert pre(start=-1) == -2
     assert pre(T=0) == 0
+
+
+def test_index_topk_noalloc_validation(L):
+    c = _cache(slots=1 << 20)
+
+    def call(nq=1, ld=128, k=16, Hi=64, q=FAKE, out=FAKE):
+        return L.index_topk_noalloc(c, q, FAKE, Hi, None, FAKE, FAKE, (ld + 63) // 64, nq, FAKE, ld, k, out, None)
+
+    assert call(Hi=24) == -2
+    assert call(k=0) == -2 and call(k=4097) == -2
+    assert call(q=None) == -1
+    assert call(out=None) == -1
+    # more than the static workspace holds: rejected before anything is enqueued
+    need = lib.load().topk_select_workspace_size(4096, 1 << 20, 2048)
+    assert need > lib.NOALLOC_SCRATCH_BYTES
+    assert call(nq=4096, ld=1 << 20, k=2048) == -4
+    assert call(nq=0) == 0

@@ -1128,19 +1128,16 @@ static int launch_mt(const csa2_fp4_cache* c, const uint16_t* q_idx, const float
     hipLaunchKernelGGL((index_score_kernel<MT, 4, false>), grid, block, lds, stream, c->idx_codes, c->idx_scales,
                        q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k, ncopies,
                        nullptr, 0, nullptr);
-  } else if ((long long)gx * qtiles > device_cu_count()) {
-    // one query per workgroup, more workgroups than CUs: the counting kernel with its
-    // counts switched off (no histogram, k past every row), whose register allocation
-    // leaves room for two workgroups per CU where the plain variant's does not
-    // (measured at batch 8: 63.7 against 73.2 us); with one workgroup per CU the
-    // plain variant is the faster one (10.5 against 10.9 us at batch 1)
+  } else {
+    // one query per workgroup: the kernel index_topk runs, with its counts switched off
+    // (no histogram, k past every row).  Its register allocation leaves room for two
+    // workgroups per CU where a variant without the counting code does not (batch 8:
+    // 63.7 against 73.2 us); with one workgroup per CU (batch 1) that variant was 0.4 us
+    // faster, but one kernel for both calls makes the standalone scan time the scan the
+    // indexer stage runs.
     hipLaunchKernelGGL((index_score_kernel<MT, 1, true>), grid, block, lds + kTopkBins * sizeof(uint32_t), stream,
                        c->idx_codes, c->idx_scales, q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw,
                        total_groups, nullptr, INT32_MAX, 1, nullptr, 0, nullptr);
-  } else {
-    hipLaunchKernelGGL((index_score_kernel<MT, 1, false>), grid, block, lds, stream, c->idx_codes, c->idx_scales,
-                       q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k, ncopies,
-                       nullptr, 0, nullptr);
   }
   return launch_status();
 }

@@ -220,3 +220,100 @@ def test_index_score_128_heads_causal_queries_of_one_sequence():
     for r in range(nq):
         m = int(nvis[r])
         assert np.array_equal(got[r, :m].view(np.int32), ref[r, :m].view(np.int32)), f"row {r}"
+
+
+def _exhaustive_query_heads():
+    """Query heads (4 MX32 blocks of 32) in which every finite bf16 pattern appears as
+    an element: a block whose largest exponent field is F holds 2^(F-127) at element 0
+    (so its shared exponent is F - 2), up to 30 patterns with exponent fields F-5 .. F
+    at elements 1..30 (every E2M1 region and midpoint relative to the block scale), and
+    0 at element 31.  The four blocks of a head share F."""
+    heads, fields_of_head = [], []
+    for F in range(1, 255):
+        pats = [(s << 15) | (f << 7) | m for f in range(max(0, F - 5), F + 1) for m in range(128) for s in (0, 1)]
+        blocks = []
+        for i in range(0, len(pats), 30):
+            chunk = pats[i:i + 30]
+            chunk += [0] * (30 - len(chunk))
+            blocks.append([F << 7] + chunk + [0])
+        while len(blocks) % 4:
+            blocks.append(blocks[0])
+        for i in range(0, len(blocks), 4):
+            heads.append(np.array(blocks[i:i + 4], np.uint16).reshape(128))
+            fields_of_head.append(F)
+    return np.stack(heads), np.array(fields_of_head)
+
+
+@pytest.mark.parametrize("shared", [False, True], ids=["one-query-per-workgroup", "queries-sharing-a-sequence"])
+def test_query_quantisation_every_bf16_pattern(shared):
+    """Every finite bf16 pattern through the MXFP4 query quantisation (on the hardware
+    convert where the block exponent allows it), read back exactly: keys are +-1 at one
+    channel c of block b and 1.0 at channel 31 of the other blocks (where every query is
+    0), so every key block has the same scale and, with one-hot head weights, the score
+    is ReLU(+-qhat[h][32b + c]).  The dequantised values come from the oracle's MX32
+    quantisation of the same blocks."""
+    Hi = 16
+    heads, fields = _exhaustive_query_heads()
+    ngroups = (len(heads) + Hi - 1) // Hi
+    pad = ngroups * Hi - len(heads)
+    heads = np.concatenate([heads, np.repeat(heads[:1], pad, axis=0)])
+    fields = np.concatenate([fields, np.repeat(fields[:1], pad)])
+    allpat = set(int(x) for x in heads.reshape(-1))
+    finite = [p for p in range(65536) if ((p >> 7) & 0xFF) != 0xFF]
+    assert set(finite) <= allpat  # every finite pattern is an element somewhere
+    q_groups = heads.reshape(ngroups, Hi, 128)
+    q = np.repeat(q_groups, Hi, axis=0)  # query g*Hi + h reads head h of group g
+    w = np.tile(np.eye(Hi, dtype=np.float32), (ngroups, 1))
+    nq = q.shape[0]
+    keys = []
+    for b in range(4):
+        for c in range(31):
+            for s in (1.0, -1.0):
+                k = np.zeros(128, np.float32)
+                k[[32 * bb + 31 for bb in range(4) if bb != b]] = 1.0
+                k[32 * b + c] = s
+                k[32 * b + 31] = 1.0
+                keys.append(k)
+    n = 256
+    keys = np.array(keys + [keys[0]] * (n - len(keys)), np.float32)
+    g = lib.Cache(n)
+    lib.fp4_cache_write(g, dev_bits(np.zeros((n, 512), np.uint16)), dev_bits(bits(keys)),
+                        dev(np.arange(n, dtype=np.int64)))
+    nvis = np.full(nq, n, np.int32)
+    scores = torch.full((nq, n), float("nan"), device="cuda")
+    soq = dev(np.zeros(nq, np.int32)) if shared else None
+    bt = dev(np.arange(4, dtype=np.int32)[None, :].repeat(1 if shared else nq, 0))
+    say(f"case: every finite bf16 pattern in {len(heads)} query heads ({nq} queries), shared={shared}")
+    torch.cuda.synchronize()
+    lib.exact_path_reset()
+    lib.index_score(g, dev_bits(q), dev(w), dev(nvis), bt, scores, seq_of_query=soq)
+    torch.cuda.synchronize()
+    counted = lib.exact_path_count()
+    got = scores.cpu().numpy()
+    # the oracle's dequantised query values
+    codes, u = oracle.quant_mx32(q_groups.reshape(-1, 32))
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+    deq = (np.where(codes & 8, -1.0, 1.0) * mags[codes & 7] * np.exp2(u.astype(np.float64) - 127)[:, None])
+    deq = deq.reshape(ngroups, Hi, 128)
+    want = np.zeros((nq, n), np.float32)
+    kinfo = [(b, c, s) for b in range(4) for c in range(31) for s in (1.0, -1.0)]
+    kinfo += [kinfo[0]] * (n - len(kinfo))
+    cols_ch = np.array([32 * b + c for b, c, _ in kinfo])
+    cols_s = np.array([s for _, _, s in kinfo])
+    for qi in range(nq):
+        gq, h = divmod(qi, Hi)
+        v = cols_s * deq[gq, h, cols_ch]
+        want[qi] = np.maximum(v, 0.0).astype(np.float32)
+    bad = np.argwhere(got.view(np.int32) != want.view(np.int32))
+    assert len(bad) == 0, (f"{len(bad)} differ, first (query, key) {bad[0].tolist()}: {got[tuple(bad[0])]!r} vs "
+                           f"{want[tuple(bad[0])]!r}")
+    # entries on the MFMA path: key blocks all at u = 125, every head's blocks share u,
+    # so a query takes the matrix unit unless its exponent sums leave fp32's range
+    uq = u.reshape(ngroups, Hi, 4).astype(np.int64)
+    lo = uq.min(axis=(1, 2)) + 125
+    hi = uq.max(axis=(1, 2)) + 125
+    exact_queries = int(np.count_nonzero((lo < 130) | (hi > 360))) * Hi
+    say(f"  all {nq * n} scores equal the oracle's quantisation; exact path {counted} "
+        f"(expected {exact_queries * n}), MFMA path for {nq - exact_queries} queries")
+    assert counted == exact_queries * n
+    assert nq - exact_queries > 2900

@@ -486,10 +486,18 @@ def main():
         "fp4_bytes_per_step": step_bytes,
         "fp4_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "fp4_frac_of_hbm_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "roofline": {"kernel": "index_score", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+        # the scan kernel of the indexer stage (index_score_kernel<Hi/16, 1, true>, the
+        # kernel index_topk launches), timed through index_score, which runs it with its
+        # digit counting off; in decode, bursts go layer-major over the cache copies, so
+        # every launch reads keys that are out of the MALL
+        "roofline": {"kernel": f"index_score_kernel<{wl.Hi // 16},1,true,false>" if wl.kind != "prefill"
+                     else f"index_score_q2_kernel<{wl.Hi // 16}>",
+                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_kind": "L2-miss (fabric) bytes per launch from FETCH_SIZE + WRITE_SIZE; MALL hits "
+                                     "count as misses",
                      "bytes_per_launch": idx_bytes, "avg_launch_ms": idx_ms,
-                     "launches_timed": idx_launches},
+                     "launches_timed": idx_launches, "cold": wl.kind != "prefill" and R > 1},
         "calls_us": calls_us,
     }
     if wl.kind == "prefill":
@@ -497,7 +505,7 @@ def main():
         # key, all index heads): its roofline is the FP4 MFMA peak, not HBM
         flop = int(wl.n_visible().astype("int64").sum()) * wl.Hi * INDEX_DIM * 2
         tflops = flop / (idx_ms * 1e-3) / 1e12
-        res["roofline"] = {"kernel": "index_score", "bound": "mfma", "achieved": tflops,
+        res["roofline"] = {"kernel": f"index_score_q2_kernel<{wl.Hi // 16}>", "bound": "mfma", "achieved": tflops,
                            "peak": MFMA_FP4_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tflops / MFMA_FP4_PEAK_TFLOPS,
                            "traffic": traffic, "flop_per_launch": flop, "avg_launch_ms": idx_ms,
                            "launches_timed": idx_launches}

@@ -542,12 +542,12 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
   // batch 1, enough for the HBM rate, while the query blocks that every workgroup
   // stages first do not queue behind the whole scan's bytes.
   KeyTile t0, t1;
-  // the four page numbers are read now.  Wavefronts that stage query blocks request
-  // their pages after the staging, so the staging's query loads do not queue behind
-  // their own key loads; the others request theirs at once.
+  // the four page numbers are read now.  Every wavefront requests its first pages
+  // after the staging: key loads issued earlier queue ahead of the staging's query
+  // loads in the compute unit's memory pipeline and delay the first page more than
+  // they save (measured at 1M entries, one query: 0.5 us per index_topk call).
   const int pg0 = POOL ? 0 : page_of(0), pg1 = POOL ? 0 : page_of(1), pg2 = POOL ? 0 : page_of(2),
             pg3 = POOL ? 0 : page_of(3);
-  const bool stager = wid * 64 < items;  // uniform
   const int32_t* __restrict__ pool_row = POOL ? pool + (int64_t)q0 * npool : nullptr;
   const int32_t* __restrict__ bt_seq = block_table + (int64_t)first_row * max_pages;
   auto vpage = [&](int k) { return gfirst + min(k, npg_all - 1); };  // pools: virtual page of the k-th
@@ -560,7 +560,6 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
     request_page(t0, 0, pg0);
     request_page(t1, 1, pg1);
   };
-  if (!stager) request_pages();
 
   // ---- stage the tile's queries: MXFP4 operands and scales.  Item = (query,
   // M-tile, lane); the 64 items of one (query, M-tile) are one wavefront, whose lanes
@@ -608,7 +607,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
   if (HIST)
 #pragma unroll
     for (int i = 0; i < kTopkBins / kThreads; ++i) lh[tid + i * kThreads] = 0u;
-  if (stager) request_pages();
+  request_pages();
   lds_barrier();
   const bool hist_on = HIST && q0 < nq && st[0].nvis > k;  // uniform (rows with n <= k need none)
   if (gfirst < gend) {

@@ -6,7 +6,8 @@
   python -m sparse_attention_fp4_cache_amd.profile_summary traffic \
         --fetch FETCH_DIR --write WRITE_DIR --copy-mib N --workload NAME \
         --bytes-per-launch B --command-fetch "..." --command-write "..."
-      HBM bytes per launch of the indexer scan from two counter passes
+      Bytes per launch of the indexer scan that missed the L2 (to the fabric: the
+      MALL or HBM; FETCH_SIZE cannot tell them apart), from two counter passes
       (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled by what the
       same counter reads for a plain copy kernel of known size run in the same
       process (it reads N bytes and writes N bytes).
@@ -22,7 +23,7 @@ import glob
 import os
 import sys
 
-SCAN_KERNEL = "index_score_kernel<4, 1, false, false>"  # the standalone scan (index_score, 64 heads, one query)
+SCAN_KERNEL = "index_score_kernel<4, 1, true, false>"  # the indexer stage's scan (64 heads, one query)
 COPY_KERNEL = "MulFunctor"  # torch's elementwise multiply, used as a read-N/write-N copy
 
 
@@ -81,14 +82,15 @@ def traffic(a) -> str:
     cw = _pick(write, COPY_KERNEL)
     f_fetch = copy_kib / max(cf)  # the largest multiply is the calibration copy
     f_write = copy_kib / max(cw)
-    sf = _pick(fetch, SCAN_KERNEL)
-    sw = _pick(write, SCAN_KERNEL)
+    sf = _pick(fetch, a.kernel)
+    sw = _pick(write, a.kernel)
     fetch_b = sum(sf) / len(sf) * 1024.0 * f_fetch
     write_b = sum(sw) / len(sw) * 1024.0 * f_write
     lines = [
-        f"# HBM traffic of the indexer scan ({SCAN_KERNEL}) on workload {a.workload}",
+        f"# L2-miss (fabric) traffic of the indexer scan ({a.kernel}) on workload {a.workload}",
         "# two rocprofv3 counter passes over the same benchmark command, FETCH_SIZE then WRITE_SIZE",
-        "# (KiB per dispatch), each scaled by the same counter on a plain copy of known size",
+        "# (KiB per dispatch), each scaled by the same counter on a plain copy of known size;",
+        "# bytes served by the MALL count here as well as bytes from HBM",
         f"command_fetch: {a.command_fetch}",
         f"command_write: {a.command_write}",
         f"kernel_source_sha256: {a.source_hash}",
@@ -124,6 +126,7 @@ def main(argv=None):
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
     t.add_argument("--source-hash", required=True)
+    t.add_argument("--kernel", default=SCAN_KERNEL)
     a = p.parse_args(argv)
     sys.stdout.write(stats(a.csv, a.command) if a.cmd == "stats" else traffic(a))
 

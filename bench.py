@@ -407,6 +407,10 @@ def main():
         if wl.npool > 0:
             calls_us["index_pool_build"] = burst_ms([functools.partial(
                 lib.index_pool_build, st.scores, st.n_visible, wl.npool, st.pool, st.ws_pool)])[0] * 1e3
+            L0 = st.layers[0]
+            calls_us["index_topk_pool_build"] = burst_ms([functools.partial(
+                lib.index_topk_pool_build, s.cache, L0["q_idx"], L0["w"], s.n_visible, s.block_table, st.scores,
+                wl.K, L0["topk"], wl.npool, st.pool, st.ws_gate) for s in steps])[0] * 1e3
             calls_us["index_topk_pool"] = burst_ms([functools.partial(
                 lib.index_topk_pool, s.cache, L["q_idx"], L["w"], s.n_visible, st.pool, s.block_table,
                 st.scores_pool, wl.K, L["topk"], st.ws_topk_pool)

@@ -192,6 +192,21 @@ size_t index_pool_build_workspace_size(int32_t nq, int64_t ld, int32_t npool);
 int index_pool_build(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq, int32_t npool,
                      int32_t* pool, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* index_topk_pool_build -- the gatekeeper layer's indexer stage in one call: index_topk
+ * and then index_pool_build on the same scores (the arguments of both; npool and pool
+ * as for index_pool_build).  scores, topk_idx and pool are bit-identical to the two
+ * calls.  With one query per workgroup (as for index_topk's folded counting) the scan
+ * also writes each 8-entry block's largest visible score and counts its first digit,
+ * so the pool's selection needs neither the block-maximum launch nor a counting
+ * launch.  ws, ws_bytes: at least index_topk_pool_build_workspace_size(nq, ld, k,
+ * npool) bytes, zero-filled before the first use (every call leaves its counters
+ * zero, as for topk_select). */
+size_t index_topk_pool_build_workspace_size(int32_t nq, int64_t ld, int32_t k, int32_t npool);
+int index_topk_pool_build(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
+                          const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* block_table,
+                          int32_t max_pages, int32_t nq, float* scores, int64_t ld, int32_t k, int32_t* topk_idx,
+                          int32_t npool, int32_t* pool, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* index_topk_pool -- index_topk restricted to each query's candidate pool: the
  * indexer stage of a Reindex layer behind a gatekeeper layer.
  *   pool int32 [nq][npool] : as written by index_pool_build (blocks ascending, -1 last)

@@ -290,7 +290,8 @@ CSA2_DEV int pool_visible(const int32_t* __restrict__ pool_row, int npool, int n
 template <int MT>
 __device__ __attribute__((always_inline)) inline bool score_page(const QStage<MT>& s, const KeyTile& cur, int G,
                                                                  const float* __restrict__ wq,
-                                                                 float* __restrict__ srow, int lane, uint32_t* lh) {
+                                                                 float* __restrict__ srow, int lane, uint32_t* lh,
+                                                                 float& score_out) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   int q_span = 0, q_umin = 255, q_umax = 0;
 #pragma unroll
@@ -349,6 +350,7 @@ __device__ __attribute__((always_inline)) inline bool score_page(const QStage<MT
       for (int r = 0; r < 4; ++r) acc = fmaf(wq[b * 4 * MT + 4 * mt + r], relu(d[mt][b][r]), acc);
   if (visible) srow[j] = acc;
   if (lh != nullptr && visible && !exact_needed) atomicAdd(&lh[score_key(acc) >> kTopkBinShift], 1u);
+  score_out = acc;
   return exact_needed;
 }
 
@@ -362,7 +364,8 @@ __device__ __attribute__((always_inline)) inline bool score_page(const QStage<MT
 template <int MT>
 __device__ __attribute__((always_inline)) inline bool score_page32(const QStage<MT>& s, const KeyTile& cur, int G,
                                                                    const float* __restrict__ wq,
-                                                                   float* __restrict__ srow, int lane, uint32_t* lh) {
+                                                                   float* __restrict__ srow, int lane, uint32_t* lh,
+                                                                   float& score_out) {
   static_assert(MT % 2 == 0, "the 32x32x64 form needs Hi a multiple of 32");
   constexpr int M32 = MT / 2;
   int q_span = 0, q_umin = 255, q_umax = 0;
@@ -428,6 +431,7 @@ __device__ __attribute__((always_inline)) inline bool score_page32(const QStage<
   }
   if (visible) srow[j] = acc;
   if (lh != nullptr && visible && !exact_needed) atomicAdd(&lh[score_key(acc) >> kTopkBinShift], 1u);
+  score_out = acc;
   return exact_needed;
 }
 
@@ -449,9 +453,10 @@ CSA2_DEV void load_page_pool(KeyTile& t, const uint8_t* __restrict__ idx_codes, 
 template <int MT>
 __device__ __attribute__((always_inline)) inline bool score_any(const QStage<MT>& s, const KeyTile& cur, int G,
                                                                 const float* __restrict__ wq,
-                                                                float* __restrict__ srow, int lane, uint32_t* lh) {
-  if constexpr (MT % 2 == 0) return score_page32<MT>(s, cur, G, wq, srow, lane, lh);
-  else return score_page<MT>(s, cur, G, wq, srow, lane, lh);
+                                                                float* __restrict__ srow, int lane, uint32_t* lh,
+                                                                float& score_out) {
+  if constexpr (MT % 2 == 0) return score_page32<MT>(s, cur, G, wq, srow, lane, lh, score_out);
+  else return score_page<MT>(s, cur, G, wq, srow, lane, lh, score_out);
 }
 
 // The definition itself for one entry (integer block sums, one rounding per head,
@@ -472,10 +477,16 @@ CSA2_DEV float exact_entry(const QStage<MT>& s, const uint8_t* __restrict__ idx_
 // HIST (one query per workgroup only): also fill the query's digit-1 histogram
 // (copy blockIdx.x % ncopies of hist[q]) of the selection that follows, when
 // n_visible[q] > k.
+// PB (with HIST, one query per workgroup): also the block maxima of the candidate
+// pool that index_pool_build derives from these scores: for each block of 8
+// consecutive entries with a visible member, bmax[q][block] = the largest score of its
+// visible members (the eight lanes of a page that hold the block, combined with
+// DPP), its digit-1 bin counted in copy blockIdx.x % bcopies of bhist[q] when the row
+// has more blocks than npool, and nblocks[q] = ceil(n_visible[q] / 8).
 // POOL: the row of each query is its candidate pool (pool [nq][npool] blocks of 8
 // entries, ld = 8 npool); position p scores member p % 8 of block pool[q][p / 8], and
 // workgroup 0 of each query writes the count of visible positions to pool_nvis[q].
-template <int MT, int QT, bool HIST, bool POOL = false>
+template <int MT, int QT, bool HIST, bool POOL = false, bool PB = false>
 __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __restrict__ idx_codes,
                                                           const uint8_t* __restrict__ idx_scales,
                                                           const uint16_t* __restrict__ q_idx,
@@ -487,8 +498,11 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
                                                           int groups_per_wave, int total_groups,
                                                           uint32_t* __restrict__ hist, int k, int ncopies,
                                                           const int32_t* __restrict__ pool, int npool,
-                                                          int32_t* __restrict__ pool_nvis) {
+                                                          int32_t* __restrict__ pool_nvis, float* __restrict__ bmax,
+                                                          int64_t ldb, uint32_t* __restrict__ bhist, int bcopies,
+                                                          int32_t* __restrict__ nblocks) {
   static_assert(!HIST || QT == 1, "the fused histogram serves one query per workgroup");
+  static_assert(!PB || (HIST && !POOL), "block maxima come from the fused scan of a whole row");
   static_assert(!POOL || QT == 1, "candidate pools are scanned one query per workgroup");
   constexpr int qt = QT;  // queries per workgroup
   constexpr int HI = 16 * MT;
@@ -604,12 +618,20 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
     st[tid].nvis = my_nvis;
   }
   uint32_t* lh = reinterpret_cast<uint32_t*>(smem + sizeof(QStage<MT>) * qt);  // HIST only
+  uint32_t* lhb = lh + kTopkBins;                                                 // PB only: block maxima
   if (HIST)
 #pragma unroll
     for (int i = 0; i < kTopkBins / kThreads; ++i) lh[tid + i * kThreads] = 0u;
+  if (PB)
+#pragma unroll
+    for (int i = 0; i < kTopkBins / kThreads; ++i) lhb[tid + i * kThreads] = 0u;
   request_pages();
   lds_barrier();
   const bool hist_on = HIST && q0 < nq && st[0].nvis > k;  // uniform (rows with n <= k need none)
+  // block maxima: a row with at most npool blocks keeps them all and needs no counts
+  const bool pb_on = PB && q0 < nq && (st[0].nvis + kPoolBlock - 1) / kPoolBlock > npool;
+  if (PB && tid == 0 && blockIdx.x == 0 && q0 < nq) nblocks[q0] = (st[0].nvis + kPoolBlock - 1) / kPoolBlock;
+  float ks0 = 0.0f, ks1 = 0.0f, ks2 = 0.0f, ks3 = 0.0f;  // this lane's score on each page (PB)
   if (gfirst < gend) {
   const int npg = gend - gfirst;
   bool same_row = true;  // every query of the tile reads the first query's sequence
@@ -618,14 +640,14 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
   // entries needing the exact path: bit (i * qt + qi) for page i, query qi
   unsigned long long exact_bits = 0ull;
   // all queries of the tile on one page whose keys are in t
-  auto page_all = [&](const KeyTile& t, int i) {
+  auto page_all = [&](const KeyTile& t, int i, float& ks) __attribute__((always_inline)) {
     const int G = gfirst + i;
 #pragma unroll 1
     for (int qi = 0; qi < qt; ++qi) {
       const QStage<MT>& sq = st[qi];
       if (G * kPage >= sq.nvis) continue;  // uniform
       const bool ex = score_any<MT>(sq, t, G, w + (int64_t)(q0 + qi) * HI, scores + (int64_t)(q0 + qi) * ld,
-                                     lane, hist_on ? lh : nullptr);
+                                     lane, hist_on ? lh : nullptr, ks);
       exact_bits |= (unsigned long long)ex << (i * qt + qi);
     }
   };
@@ -634,12 +656,12 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
     // the wavefront's (at most four) pages, all requested in the prologue, in
     // straight-line code: the wait for page k leaves pages k+1.. in flight (a loop
     // here would make the compiler wait for every outstanding load at its head)
-    page_all(t0, 0);
+    page_all(t0, 0, ks0);
     request_page(t0, 2, pg2);
-    if (npg > 1) page_all(t1, 1);
+    if (npg > 1) page_all(t1, 1, ks1);
     request_page(t1, 3, pg3);
-    if (npg > 2) page_all(t0, 2);
-    if (npg > 3) page_all(t1, 3);
+    if (npg > 2) page_all(t0, 2, ks2);
+    if (npg > 3) page_all(t1, 3, ks3);
     // rare: entries whose blocks fall outside the exact window of the MFMA
     while (exact_bits != 0ull) {
       const int b = __builtin_ctzll(exact_bits);
@@ -651,6 +673,32 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
                                       scores + (int64_t)(q0 + qi) * ld + (int64_t)(gfirst + i) * kPage + lane);
       count_exact_path();
       if (HIST && hist_on) atomicAdd(&lh[score_key(e) >> kTopkBinShift], 1u);
+      if (PB) {
+        if (i == 0) ks0 = e;
+        else if (i == 1) ks1 = e;
+        else if (i == 2) ks2 = e;
+        else ks3 = e;
+      }
+    }
+    if (PB && q0 < nq) {
+      // block maxima of this wavefront's pages: lanes 8b' .. 8b'+7 hold block b' of a
+      // page; quad swaps and the half-row mirror give each lane its block's maximum
+      const float ksv[kMaxPagesPerWave] = {ks0, ks1, ks2, ks3};
+      const int nvis = st[0].nvis;
+#pragma unroll
+      for (int i = 0; i < kMaxPagesPerWave; ++i) {
+        if (i < npg) {  // uniform
+          const int64_t j = (int64_t)(gfirst + i) * kPage + lane;
+          float v = j < nvis ? ksv[i] : -INFINITY;
+          v = fmaxf(v, dpp_f<0xB1>(v));
+          v = fmaxf(v, dpp_f<0x4E>(v));
+          v = fmaxf(v, dpp_f<0x141>(v));
+          if ((lane & 7) == 0 && j < nvis) {
+            bmax[(int64_t)q0 * ldb + (j >> 3)] = v;
+            if (pb_on) atomicAdd(&lhb[score_key(v) >> kTopkBinShift], 1u);
+          }
+        }
+      }
     }
   } else {
     // queries of several sequences share the tile: each query reads its own pages
@@ -663,8 +711,9 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
         const int64_t slot0 = (int64_t)page * kPage;
         KeyTile t;
         load_page<MT>(t, idx_codes, idx_scales, page, lane);
+        float unused;
         if (score_any<MT>(sq, t, G, w + (int64_t)(q0 + qi) * HI, scores + (int64_t)(q0 + qi) * ld, lane,
-                           nullptr)) {
+                           nullptr, unused)) {
           exact_entry<MT>(sq, idx_codes, idx_scales, slot0 + lane, w + (int64_t)(q0 + qi) * HI,
                           scores + (int64_t)(q0 + qi) * ld + (int64_t)G * kPage + lane);
           count_exact_path();
@@ -680,6 +729,15 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(const uint8_t* __
     for (int i = 0; i < kTopkBins / kThreads; ++i) {
       const uint32_t c = lh[tid + i * kThreads];
       if (c) atomicAdd(&gh[tid + i * kThreads], c);
+    }
+  }
+  if (PB && pb_on) {  // the block maxima's counts, into the pool selection's histogram
+    __syncthreads();
+    uint32_t* gb = bhist + ((size_t)q0 * kTopkHistCopies + blockIdx.x % bcopies) * kTopkBins;
+#pragma unroll
+    for (int i = 0; i < kTopkBins / kThreads; ++i) {
+      const uint32_t c = lhb[tid + i * kThreads];
+      if (c) atomicAdd(&gb[tid + i * kThreads], c);
     }
   }
 }
@@ -1085,10 +1143,20 @@ struct PoolArgs {
   int32_t* nvis = nullptr;  // [nq] out: visible pool positions
 };
 
+// Block maxima of the candidate pool built from the scores (index_topk_pool_build).
+struct PoolBuildArgs {
+  float* bmax = nullptr;  // [nq][ldb]
+  int64_t ldb = 0;
+  uint32_t* bhist = nullptr;  // the pool selection's digit-1 histograms
+  int32_t* nblocks = nullptr;
+  int npool = 0;
+};
+
 template <int MT>
 static int launch_mt(const csa2_fp4_cache* c, const uint16_t* q_idx, const float* w, const int32_t* soq,
                      const int32_t* nvis, const int32_t* bt, int32_t max_pages, int32_t nq, float* scores, int64_t ld,
-                     uint32_t* hist, int k, int* copies, const PoolArgs& pa, hipStream_t stream) {
+                     uint32_t* hist, int k, int* copies, const PoolArgs& pa, hipStream_t stream,
+                     const PoolBuildArgs* pb = nullptr) {
   const int total_groups = (int)ceil_div(ld, kPage);
   if (total_groups == 0 || nq == 0) return CSA2_OK;
   // queries per workgroup: several queries of one sequence share each loaded page
@@ -1106,27 +1174,32 @@ static int launch_mt(const csa2_fp4_cache* c, const uint16_t* q_idx, const float
   const size_t lds = sizeof(QStage<MT>) * qt;
   const int ncopies = topk_hist_copies(gx);
   if (copies != nullptr) *copies = ncopies;
-  if (pa.pool != nullptr) {
+  if (pb != nullptr) {  // one query per workgroup, with its digit-1 counts (the caller checked)
+    hipLaunchKernelGGL((index_score_kernel<MT, 1, true, false, true>), grid, block,
+                       lds + 2 * kTopkBins * sizeof(uint32_t), stream, c->idx_codes, c->idx_scales, q_idx, w, soq,
+                       nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k, ncopies, nullptr, pb->npool,
+                       nullptr, pb->bmax, pb->ldb, pb->bhist, ncopies, pb->nblocks);
+  } else if (pa.pool != nullptr) {
     if (hist != nullptr)
       hipLaunchKernelGGL((index_score_kernel<MT, 1, true, true>), grid, block, lds + kTopkBins * sizeof(uint32_t),
                          stream, c->idx_codes, c->idx_scales, q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw,
-                         total_groups, hist, k, ncopies, pa.pool, pa.npool, pa.nvis);
+                         total_groups, hist, k, ncopies, pa.pool, pa.npool, pa.nvis, nullptr, 0, nullptr, 0, nullptr);
     else
       hipLaunchKernelGGL((index_score_kernel<MT, 1, false, true>), grid, block, lds, stream, c->idx_codes,
                          c->idx_scales, q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist,
-                         k, ncopies, pa.pool, pa.npool, pa.nvis);
+                         k, ncopies, pa.pool, pa.npool, pa.nvis, nullptr, 0, nullptr, 0, nullptr);
   } else if (hist != nullptr) {  // one query per workgroup (the caller checked)
     hipLaunchKernelGGL((index_score_kernel<MT, 1, true>), grid, block, lds + kTopkBins * sizeof(uint32_t), stream,
                        c->idx_codes, c->idx_scales, q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw,
-                       total_groups, hist, k, ncopies, nullptr, 0, nullptr);
+                       total_groups, hist, k, ncopies, nullptr, 0, nullptr, nullptr, 0, nullptr, 0, nullptr);
   } else if (qt == 8) {
     hipLaunchKernelGGL((index_score_kernel<MT, 8, false>), grid, block, lds, stream, c->idx_codes, c->idx_scales,
                        q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k, ncopies,
-                       nullptr, 0, nullptr);
+                       nullptr, 0, nullptr, nullptr, 0, nullptr, 0, nullptr);
   } else if (qt == 4) {
     hipLaunchKernelGGL((index_score_kernel<MT, 4, false>), grid, block, lds, stream, c->idx_codes, c->idx_scales,
                        q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw, total_groups, hist, k, ncopies,
-                       nullptr, 0, nullptr);
+                       nullptr, 0, nullptr, nullptr, 0, nullptr, 0, nullptr);
   } else {
     // one query per workgroup: the kernel index_topk runs, with its counts switched off
     // (no histogram, k past every row).  Its register allocation leaves room for two
@@ -1136,7 +1209,7 @@ static int launch_mt(const csa2_fp4_cache* c, const uint16_t* q_idx, const float
     // indexer stage runs.
     hipLaunchKernelGGL((index_score_kernel<MT, 1, true>), grid, block, lds + kTopkBins * sizeof(uint32_t), stream,
                        c->idx_codes, c->idx_scales, q_idx, w, soq, nvis, bt, max_pages, nq, scores, ld, gpw,
-                       total_groups, nullptr, INT32_MAX, 1, nullptr, 0, nullptr);
+                       total_groups, nullptr, INT32_MAX, 1, nullptr, 0, nullptr, nullptr, 0, nullptr, 0, nullptr);
   }
   return launch_status();
 }
@@ -1161,7 +1234,8 @@ static int launch_q2(const csa2_fp4_cache* c, const uint16_t* q_idx, const float
 static int launch_hi(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
                      const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* block_table,
                      int32_t max_pages, int32_t nq, float* scores, int64_t ld, uint32_t* hist, int k,
-                     int* copies, hipStream_t stream, const PoolArgs& pa = PoolArgs()) {
+                     int* copies, hipStream_t stream, const PoolArgs& pa = PoolArgs(),
+                     const PoolBuildArgs* pb = nullptr) {
   // queries that share sequences, at most 64 heads: two queries per wavefront (two
   // score rows within one buffer resource's 2^31-byte range)
   if (pa.pool == nullptr && hist == nullptr && query_tile(seq_of_query, nq, 0) > 1 && Hi <= 64 &&
@@ -1178,7 +1252,7 @@ static int launch_hi(const csa2_fp4_cache* cache, const uint16_t* q_idx, const f
 #define CSA2_MT(m) \
   case m:          \
     return launch_mt<m>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, hist, k, \
-                        copies, pa, stream);
+                        copies, pa, stream, pb);
     CSA2_MT(1)
     CSA2_MT(2)
     CSA2_MT(3)
@@ -1187,7 +1261,7 @@ static int launch_hi(const csa2_fp4_cache* cache, const uint16_t* q_idx, const f
     CSA2_MT(6)
     CSA2_MT(7)
     default: return launch_mt<8>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld,
-                                 hist, k, copies, pa, stream);
+                                 hist, k, copies, pa, stream, pb);
 #undef CSA2_MT
   }
 }
@@ -1297,6 +1371,50 @@ extern "C" int index_topk_noalloc(const csa2_fp4_cache* cache, const uint16_t* q
   if (st != CSA2_OK) return st;
   return index_topk(cache, q_idx, w, Hi, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, k,
                     topk_idx, ws, need, stream);
+}
+
+extern "C" size_t index_topk_pool_build_workspace_size(int32_t nq, int64_t ld, int32_t k, int32_t npool) {
+  if (nq <= 0) return 256;
+  return ((topk_select_workspace_size(nq, ld, k) + 255) & ~(size_t)255) +
+         index_pool_build_workspace_size(nq, ld, npool);
+}
+
+extern "C" int index_topk_pool_build(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
+                                     const int32_t* seq_of_query, const int32_t* n_visible,
+                                     const int32_t* block_table, int32_t max_pages, int32_t nq, float* scores,
+                                     int64_t ld, int32_t k, int32_t* topk_idx, int32_t npool, int32_t* pool, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  int st = check_args(cache, q_idx, w, Hi, n_visible, block_table, max_pages, nq, scores, ld);
+  if (st != CSA2_OK) return st;
+  if (k < 1 || k > CSA2_MAX_K || npool < 1 || npool > CSA2_MAX_K || ld >= ((int64_t)1 << 31)) return CSA2_ERR_SHAPE;
+  if (nq == 0) return CSA2_OK;
+  if (!topk_idx || !pool) return CSA2_ERR_NULL;
+  if (!ws || ws_bytes < index_topk_pool_build_workspace_size(nq, ld, k, npool)) return CSA2_ERR_WORKSPACE;
+  const size_t topk_bytes = (topk_select_workspace_size(nq, ld, k) + 255) & ~(size_t)255;
+  void* ws_pool = static_cast<char*>(ws) + topk_bytes;
+  const size_t pool_bytes = ws_bytes - topk_bytes;
+  if (ld == 0 || query_tile(seq_of_query, nq, 0) != 1) {  // the two calls in turn
+    st = index_topk(cache, q_idx, w, Hi, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, k, topk_idx,
+                    ws, topk_bytes, stream);
+    if (st != CSA2_OK) return st;
+    return index_pool_build(scores, ld, n_visible, nq, npool, pool, ws_pool, pool_bytes, stream);
+  }
+  // one query per workgroup: the scan also writes the block maxima and counts their
+  // first digit, so neither selection needs a counting launch
+  const PoolWs pw = pool_ws_carve(ws_pool, nq, ld);
+  PoolBuildArgs pb;
+  pb.bmax = pw.bmax;
+  pb.ldb = pw.ldb;
+  pb.bhist = topk_digit1_hist(pw.ws_topk, nq, pw.ldb);
+  pb.nblocks = pw.nblocks;
+  pb.npool = npool;
+  int copies = 1;
+  st = launch_hi(cache, q_idx, w, Hi, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld,
+                 topk_digit1_hist(ws, nq, ld), k, &copies, stream, PoolArgs(), &pb);
+  if (st != CSA2_OK) return st;
+  st = topk_enqueue(scores, ld, n_visible, nq, k, topk_idx, ws, stream, true, copies, nullptr, 0);
+  if (st != CSA2_OK) return st;
+  return topk_enqueue(pw.bmax, pw.ldb, pw.nblocks, nq, npool, pool, pw.ws_topk, stream, true, copies, nullptr, 0);
 }
 
 // the pool workspace: visible pool positions per query, then the selection's workspace

@@ -29,6 +29,17 @@ int topk_enqueue(const float* scores, int64_t ld, const int32_t* n_visible, int3
                  int32_t* topk_idx, void* ws, hipStream_t stream, bool hist_done, int copies, const int32_t* pool,
                  int npool);
 
+// The candidate-pool workspace of index_pool_build (nq rows of ld scores): the block
+// maxima [nq][ldb] (ldb = ceil(ld / 8)), the blocks per row [nq], then the top-npool
+// selection's workspace over the block maxima.
+struct PoolWs {
+  int64_t ldb = 0;
+  float* bmax = nullptr;
+  int32_t* nblocks = nullptr;
+  void* ws_topk = nullptr;
+};
+PoolWs pool_ws_carve(void* ws, int32_t nq, int64_t ld);
+
 // Bytes at the start of a top-k workspace for (nq, ld) that must be zero before a
 // call (its counters and histograms; a multiple of 256); the rest is scratch that
 // every call writes before reading.

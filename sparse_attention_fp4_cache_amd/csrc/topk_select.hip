@@ -885,6 +885,16 @@ __global__ __launch_bounds__(kBmaxThreads) void pool_bmax_kernel(const float* __
 
 static int64_t pool_ldb(int64_t ld) { return (ld + 7) / 8; }
 
+PoolWs pool_ws_carve(void* ws, int32_t nq, int64_t ld) {
+  PoolWs p;
+  p.ldb = pool_ldb(ld);
+  p.bmax = reinterpret_cast<float*>(ws);
+  p.nblocks = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) +
+                                         align_up((size_t)nq * (size_t)p.ldb * sizeof(float)));
+  p.ws_topk = reinterpret_cast<char*>(p.nblocks) + align_up((size_t)nq * sizeof(int32_t));
+  return p;
+}
+
 }  // namespace csa2
 
 extern "C" size_t index_pool_build_workspace_size(int32_t nq, int64_t ld, int32_t npool) {
@@ -901,11 +911,11 @@ extern "C" int index_pool_build(const float* scores, int64_t ld, const int32_t* 
   if (nq == 0) return CSA2_OK;
   if (!n_visible || !pool || (ld > 0 && !scores)) return CSA2_ERR_NULL;
   if (!ws || ws_bytes < index_pool_build_workspace_size(nq, ld, npool)) return CSA2_ERR_WORKSPACE;
-  const int64_t ldb = pool_ldb(ld);
-  float* bmax = reinterpret_cast<float*>(ws);
-  int32_t* nb = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) +
-                                           align_up((size_t)nq * (size_t)ldb * sizeof(float)));
-  void* ws_topk = reinterpret_cast<char*>(nb) + align_up((size_t)nq * sizeof(int32_t));
+  const PoolWs pw = pool_ws_carve(ws, nq, ld);
+  const int64_t ldb = pw.ldb;
+  float* bmax = pw.bmax;
+  int32_t* nb = pw.nblocks;
+  void* ws_topk = pw.ws_topk;
   const dim3 grid((unsigned)std::max<int64_t>(1, (ldb + kBmaxThreads - 1) / kBmaxThreads), (unsigned)nq);
   hipLaunchKernelGGL(pool_bmax_kernel, grid, dim3(kBmaxThreads), 0, stream, scores, ld, n_visible, bmax, ldb, nb);
   if (launch_status() != CSA2_OK) return CSA2_ERR_LAUNCH;

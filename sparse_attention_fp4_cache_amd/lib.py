@@ -31,6 +31,8 @@ EXPORTS = (
     "index_topk",
     "index_pool_build_workspace_size",
     "index_pool_build",
+    "index_topk_pool_build_workspace_size",
+    "index_topk_pool_build",
     "index_topk_pool_workspace_size",
     "index_topk_pool",
     "sparse_attn_decode_workspace_size",
@@ -89,6 +91,10 @@ def load() -> ctypes.CDLL:
         L.index_pool_build_workspace_size.argtypes = [_I32, _I64, _I32]
         L.index_pool_build_workspace_size.restype = _SZ
         L.index_pool_build.argtypes = [_P, _I64, _P, _I32, _I32, _P, _P, _SZ, _P]
+        L.index_topk_pool_build_workspace_size.argtypes = [_I32, _I64, _I32, _I32]
+        L.index_topk_pool_build_workspace_size.restype = _SZ
+        L.index_topk_pool_build.argtypes = [ctypes.POINTER(_CacheStruct), _P, _P, _I32, _P, _P, _P, _I32, _I32, _P,
+                                            _I64, _I32, _P, _I32, _P, _P, _SZ, _P]
         L.index_topk_pool_workspace_size.argtypes = [_I32, _I32, _I32]
         L.index_topk_pool_workspace_size.restype = _SZ
         L.index_topk_pool.argtypes = [ctypes.POINTER(_CacheStruct), _P, _P, _I32, _P, _P, _P, _I32, _P, _I32, _I32,
@@ -282,6 +288,30 @@ def index_pool_build(scores: torch.Tensor, n_visible: torch.Tensor, npool: int, 
                                                        _ptr(n_visible, torch.int32, "n_visible"), nq, npool,
                                                        _ptr(pool, torch.int32, "pool"), _ptr(ws, torch.uint8, "ws"),
                                                        ws.numel(), _stream(stream)))
+
+
+def index_topk_pool_build_workspace_size(nq: int, ld: int, k: int, npool: int) -> int:
+    return int(load().index_topk_pool_build_workspace_size(nq, ld, k, npool))
+
+
+def index_topk_pool_build(cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, n_visible: torch.Tensor,
+                          block_table: torch.Tensor, scores: torch.Tensor, k: int, topk_idx: torch.Tensor, npool: int,
+                          pool: torch.Tensor, ws: torch.Tensor, seq_of_query: torch.Tensor | None = None, stream=None):
+    """index_topk then index_pool_build on the same scores, as one call (same results)."""
+    nq, Hi, d = q_idx.shape
+    if d != INDEX_DIM or w.shape != (nq, Hi) or n_visible.shape != (nq,) or scores.dim() != 2 or scores.shape[0] != nq:
+        raise ValueError("shape mismatch in index_topk_pool_build arguments")
+    if topk_idx.shape != (nq, k) or pool.shape != (nq, npool):
+        raise ValueError("topk_idx must be [nq, k] and pool [nq, npool]")
+    _check("index_topk_pool_build",
+           load().index_topk_pool_build(cache.struct, _bits16(q_idx, "q_idx"), _ptr(w, torch.float32, "w"), Hi,
+                                        _ptr(seq_of_query, torch.int32, "seq_of_query"),
+                                        _ptr(n_visible, torch.int32, "n_visible"),
+                                        _ptr(block_table, torch.int32, "block_table"), block_table.shape[1], nq,
+                                        _ptr(scores, torch.float32, "scores"), scores.shape[1], k,
+                                        _ptr(topk_idx, torch.int32, "topk_idx"), npool,
+                                        _ptr(pool, torch.int32, "pool"), _ptr(ws, torch.uint8, "ws"), ws.numel(),
+                                        _stream(stream)))
 
 
 def index_topk_pool_workspace_size(nq: int, npool: int, k: int) -> int:

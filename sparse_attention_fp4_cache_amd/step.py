@@ -70,6 +70,9 @@ class DecodeStep:
             self.scores_pool = torch.zeros((B, lib.POOL_BLOCK * P), dtype=torch.float32, device=device)
             self.ws_topk_pool = torch.zeros(lib.index_topk_pool_workspace_size(B, P, K), dtype=torch.uint8,
                                             device=device)
+            # the Full layer's top-k and pool as one call
+            self.ws_gate = torch.zeros(lib.index_topk_pool_build_workspace_size(B, self.ld, K, P), dtype=torch.uint8,
+                                       device=device)
         self.layers = []
         for li, mode in enumerate(wl.layers):
             d = wl.layer_inputs(li)
@@ -123,7 +126,15 @@ class DecodeStep:
                     L["scores"] = self.scores_pool.clone()
                 latest = L["topk"]
             elif mode in ("full", "reindex"):
-                if self.fused_index:
+                if mode == "full" and self.npool > 0 and self.fused_index:
+                    # the gatekeeper layer: top-k and candidate pool from one scan
+                    call("index_topk_pool_build", lib.index_topk_pool_build, self.cache, L["q_idx"], L["w"],
+                         self.n_visible, self.block_table, self.scores, self.wl.K, L["topk"], self.npool, self.pool,
+                         self.ws_gate)
+                    if keep_scores:
+                        L["scores"] = self.scores.clone()
+                        L["pool"] = self.pool.clone()
+                elif self.fused_index:
                     call("index_topk", lib.index_topk, self.cache, L["q_idx"], L["w"], self.n_visible,
                          self.block_table, self.scores, self.wl.K, L["topk"], self.ws_topk)
                     if keep_scores:
@@ -136,7 +147,7 @@ class DecodeStep:
                     call("topk_select", lib.topk_select, self.scores, self.n_visible, self.wl.K, L["topk"],
                          self.ws_topk)
                 latest = L["topk"]
-                if mode == "full" and self.npool > 0:
+                if mode == "full" and self.npool > 0 and not self.fused_index:
                     call("index_pool_build", lib.index_pool_build, self.scores, self.n_visible, self.npool,
                          self.pool, self.ws_pool)
                     if keep_scores:
@@ -204,6 +215,8 @@ class ScheduleDecodeStep:
                 C["scores_pool"] = torch.zeros((1, lib.POOL_BLOCK * P), dtype=torch.float32, device=device)
                 C["ws_topk_pool"] = torch.zeros(lib.index_topk_pool_workspace_size(1, P, K), dtype=torch.uint8,
                                                 device=device)
+                C["ws_gate"] = torch.zeros(lib.index_topk_pool_build_workspace_size(1, ld, K, P), dtype=torch.uint8,
+                                           device=device)
             self.caches[w] = C
         self.ws_attn = torch.zeros(max(lib.sparse_attn_decode_workspace_size(1, H, K, W),
                                        lib.sparse_attn_decode_workspace_size(1, H, 0, W)), dtype=torch.uint8,
@@ -259,17 +272,21 @@ class ScheduleDecodeStep:
                 if keep_scores:
                     L["scores"] = C["scores_pool"].clone()
                 latest[L["src"]] = L["topk"]
+            elif mode == "full" and C["pooled"]:
+                # the gatekeeper layer of a pooled cache: top-k and pool from one scan
+                call("index_topk_pool_build", lib.index_topk_pool_build, C["cache"], L["q_idx"], L["w"],
+                     C["n_visible"], C["block_table"], C["scores"], K, L["topk"], self.wl.npool, C["pool"],
+                     C["ws_gate"])
+                if keep_scores:
+                    L["scores"] = C["scores"].clone()
+                    L["pool"] = C["pool"].clone()
+                latest[L["src"]] = L["topk"]
             elif mode in ("full", "reindex"):
                 call("index_topk", lib.index_topk, C["cache"], L["q_idx"], L["w"], C["n_visible"],
                      C["block_table"], C["scores"], K, L["topk"], C["ws_topk"])
                 if keep_scores:
                     L["scores"] = C["scores"].clone()
                 latest[L["src"]] = L["topk"]
-                if mode == "full" and C["pooled"]:
-                    call("index_pool_build", lib.index_pool_build, C["scores"], C["n_visible"], self.wl.npool,
-                         C["pool"], C["ws_pool"])
-                    if keep_scores:
-                        L["pool"] = C["pool"].clone()
             if L["src"] not in latest:
                 raise ValueError("a reuse layer needs an earlier full or reindex layer on its cache")
             call("sparse_attn_decode", lib.sparse_attn_decode, C["cache"], L["q"], latest[L["src"]],

@@ -657,6 +657,73 @@ def test_index_topk_long_rows_of_different_lengths():
     assert torch.equal(i_f, i_sep), "top-k differs"
 
 
+def _gate_vs_separate(rng, n_per_seq, Hi, k, npool, key_fn=None, seq_of_query=None, reps=2):
+    """index_topk_pool_build against index_topk then index_pool_build (scores, top-k
+    and pool bit for bit), `reps` times on one workspace."""
+    B = len(n_per_seq)
+    pages = [(n + 63) // 64 for n in n_per_seq]
+    phys = rng.permutation(sum(pages))
+    bt = np.zeros((B, max(pages)), np.int32)
+    off, key, slots = 0, [], []
+    for b, n in enumerate(n_per_seq):
+        bt[b, :pages[b]] = phys[off:off + pages[b]]
+        off += pages[b]
+        j = np.arange(n)
+        slots.append(bt[b, j // 64].astype(np.int64) * 64 + j % 64)
+        kk = rng.standard_normal((n, 128)).astype(np.float32)
+        key.append(bits(key_fn(kk) if key_fn else kk))
+    g = lib.Cache(sum(pages) * 64)
+    nall = sum(n_per_seq)
+    lib.fp4_cache_write(g, dev_bits(np.zeros((nall, 512), np.uint16)), dev_bits(np.concatenate(key)),
+                        dev(np.concatenate(slots)))
+    if seq_of_query is None:
+        nq, soq, nvis = B, None, np.array(n_per_seq, np.int32)
+    else:
+        soq = np.asarray(seq_of_query, np.int32)
+        nq = len(soq)
+        nvis = np.array([max(1, n_per_seq[s] - 7 * i % 50) for i, s in enumerate(soq)], np.int32)
+    ld = ((int(nvis.max()) + 63) // 64) * 64
+    q = bits(rng.standard_normal((nq, Hi, 128)).astype(np.float32))
+    w = rng.random((nq, Hi), dtype=np.float32)
+    dq, dw, dnv, dbt = dev_bits(q), dev(w), dev(nvis), dev(bt)
+    dsoq = None if soq is None else dev(soq)
+    ws_t = torch.zeros(lib.topk_select_workspace_size(nq, ld, k), dtype=torch.uint8, device="cuda")
+    ws_p = torch.zeros(lib.index_pool_build_workspace_size(nq, ld, npool), dtype=torch.uint8, device="cuda")
+    s_sep = torch.full((nq, ld), float("nan"), device="cuda")
+    i_sep = torch.full((nq, k), -7, dtype=torch.int32, device="cuda")
+    p_sep = torch.full((nq, npool), -7, dtype=torch.int32, device="cuda")
+    lib.index_topk(g, dq, dw, dnv, dbt, s_sep, k, i_sep, ws_t, seq_of_query=dsoq)
+    lib.index_pool_build(s_sep, dnv, npool, p_sep, ws_p)
+    ws_g = torch.zeros(lib.index_topk_pool_build_workspace_size(nq, ld, k, npool), dtype=torch.uint8, device="cuda")
+    for rep in range(reps):
+        s_g = torch.full((nq, ld), float("nan"), device="cuda")
+        i_g = torch.full((nq, k), -7, dtype=torch.int32, device="cuda")
+        p_g = torch.full((nq, npool), -7, dtype=torch.int32, device="cuda")
+        lib.index_topk_pool_build(g, dq, dw, dnv, dbt, s_g, k, i_g, npool, p_g, ws_g, seq_of_query=dsoq)
+        torch.cuda.synchronize()
+        a, b = s_g.cpu().numpy(), s_sep.cpu().numpy()
+        for r in range(nq):
+            assert same_bits_f32(a[r, :nvis[r]], b[r, :nvis[r]]), f"rep {rep} row {r}: scores differ"
+        assert torch.equal(i_g, i_sep), f"rep {rep}: top-k differs"
+        assert torch.equal(p_g, p_sep), f"rep {rep}: pool differs"
+
+
+def test_index_topk_pool_build_equals_separate_calls():
+    def spread(kk):
+        kk[:, 0:32] *= 2.0 ** -12
+        kk[:, 64:96] *= 2.0 ** 6
+        return kk
+
+    say("case: index_topk_pool_build, one 300,003-entry row, pool 2048")
+    _gate_vs_separate(np.random.default_rng(320), [300003], 64, 2048, 2048)
+    say("case: index_topk_pool_build, ragged rows (some keep every block), pool 1024")
+    _gate_vs_separate(np.random.default_rng(321), [70000, 9001, 100, 8200], 64, 256, 1024)
+    say("case: index_topk_pool_build with exact-path entries, 16 heads")
+    _gate_vs_separate(np.random.default_rng(322), [40001], 16, 512, 300, key_fn=spread)
+    say("case: index_topk_pool_build, queries sharing sequences (the two calls in turn)")
+    _gate_vs_separate(np.random.default_rng(323), [5000, 3000], 32, 128, 64, seq_of_query=[0] * 40 + [1] * 30)
+
+
 def test_index_topk_query_tiles_fall_back():
     say("case: index_topk with a sequence map and 70 queries (tiles of queries, separate counting pass)")
     _fused_vs_separate(np.random.default_rng(302), [5000, 3000], 32, 128, seq_of_query=[0] * 40 + [1] * 30)

@@ -494,7 +494,7 @@ def main():
         # kernel index_topk launches), timed through index_score, which runs it with its
         # digit counting off; in decode, bursts go layer-major over the cache copies, so
         # every launch reads keys that are out of the MALL
-        "roofline": {"kernel": f"index_score_kernel<{wl.Hi // 16},1,true,false>" if wl.kind != "prefill"
+        "roofline": {"kernel": f"index_score_kernel<{wl.Hi // 16}, 1, true, false, false>" if wl.kind != "prefill"
                      else f"index_score_q2_kernel<{wl.Hi // 16}>",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,

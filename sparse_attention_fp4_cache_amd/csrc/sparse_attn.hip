@@ -437,8 +437,20 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a) {
 // one tile row (16 code bytes + 2 scale bytes, or 64 bytes of a window row).
 constexpr int kWideHeads = 64;
 constexpr int kWideMaxRows = CSA2_MAX_K + CSA2_MAX_WINDOW;
+constexpr int kWStride = kLatentDim;  // bf16 per X row: unpadded, wchunk() spreads the banks
+// Physical 16-byte chunk of logical chunk c in row r of a wide-kernel tile: xchunk's
+// spread of one row's chunks, then a row term, so that every LDS access pattern of the
+// kernel reaches distinct banks: the 8 rows {0..3, 8..11} of one chunk that a logits
+// read serves per pass, the 4 rows x 32 bytes of a transposing read, and the 8 chunks
+// of one row a dequantising store writes.  (With the padded stride and xchunk the
+// first two patterns met 2-way conflicts; the kernel gained about 1%: 2.60 against
+// 2.63 ms for a 4096-query chunk, so the bank conflicts were not what bounds it.)
+CSA2_DEV int wchunk(int r, int c) {
+  const int f = (2 * (r & 3)) | ((r >> 3) & 1) | ((((r >> 3) ^ (r >> 4)) & 1) << 3);
+  return c ^ ((c >> 3) & 7) ^ f;
+}
 struct __align__(16) WideSmem {
-  uint16_t x[3][kRT * kXStride];  // X[row][ch] of three tiles, 16-byte chunks swizzled by xchunk()
+  uint16_t x[3][kRT * kWStride];  // X[row][ch] of three tiles, 16-byte chunks swizzled by wchunk()
   float red[2][4][2][2][4][64];   // partial logits [tile parity][head group][channel half][mtile][r][lane]
   int src[kWideMaxRows];          // source of every row of the query
 };
@@ -488,7 +500,7 @@ CSA2_DEV void issue_wide(const AttnArgs& a, const int* src_rows, int tid, int ti
 template <bool W8>
 CSA2_DEV void store_wide(uint16_t* x, int tid, const WideRegs& t, bool has_main, bool has_win) {
   const int row = tid >> 4, c16 = tid & 15;
-  uint4* xr = reinterpret_cast<uint4*>(x + row * kXStride);
+  uint4* xr = reinterpret_cast<uint4*>(x + row * kWStride);
   const uint32_t wmask = t.kind == 2 ? ~0u : 0u;
   const float X = W8 ? e8m0_scale(t.wsc) : 1.0f;
   if (has_main && !has_win) {
@@ -499,18 +511,18 @@ CSA2_DEV void store_wide(uint16_t* x, int tid, const WideRegs& t, bool has_main,
     const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)sc, 0), s1 = __builtin_amdgcn_cvt_f32_fp8((int)sc, 1);
     const uint32_t cw[4] = {m ? t.code.x : 0u, m ? t.code.y : 0u, m ? t.code.z : 0u, m ? t.code.w : 0u};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xr[xchunk(4 * c16 + i)] = dequant8(cw[i], i < 2 ? s0 : s1);
+    for (int i = 0; i < 4; ++i) xr[wchunk(row, 4 * c16 + i)] = dequant8(cw[i], i < 2 ? s0 : s1);
   } else if (has_main) {
     const uint32_t mmask = t.kind == 1 ? ~0u : 0u;
     const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)t.sc, 0), s1 = __builtin_amdgcn_cvt_f32_fp8((int)t.sc, 1);
     const uint32_t cw[4] = {t.code.x, t.code.y, t.code.z, t.code.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i)  // chunk i (8 channels) of this thread's 32 uses scale byte i / 2
-      xr[xchunk(4 * c16 + i)] =
+      xr[wchunk(row, 4 * c16 + i)] =
           or4(and4(dequant8(cw[i], i < 2 ? s0 : s1), mmask), and4(win_chunk<W8>(t.win, i, X), wmask));
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xr[xchunk(4 * c16 + i)] = and4(win_chunk<W8>(t.win, i, X), wmask);
+    for (int i = 0; i < 4; ++i) xr[wchunk(row, 4 * c16 + i)] = and4(win_chunk<W8>(t.win, i, X), wmask);
   }
 }
 
@@ -581,7 +593,7 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const int xrow = 8 * (n16 >> 2) + 4 * tt + (n16 & 3);  // lane group g gets rows 8g .. 8g+7
-        const uint4 xa = reinterpret_cast<const uint4*>(xt + xrow * kXStride)[xchunk(32 * kh + 4 * ks + g)];
+        const uint4 xa = reinterpret_cast<const uint4*>(xt + xrow * kWStride)[wchunk(xrow, 32 * kh + 4 * ks + g)];
         sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(qop[ks]), sl, 0, 0, 0);
       }
 #pragma unroll
@@ -633,13 +645,14 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
       for (int mt = 0; mt < 16; ++mt) acc[mt] *= alpha;
     }
     // X^T operand of M-tile mt (channels 256*kh + 16*mt + ..), transposing LDS reads
-    const int tr_c = n16 & 3;
-    const uint16_t* tr_row = xt + (8 * g + (n16 >> 2)) * kXStride + 4 * (tr_c & 1);
+    // (rows 8g + n16/4 and 4 below it share wchunk's row term)
+    const int tr_c = n16 & 3, tr_r = 8 * g + (n16 >> 2);
+    const uint16_t* tr_row = xt + tr_r * kWStride + 4 * (tr_c & 1);
 #pragma unroll
     for (int mt = 0; mt < 16; ++mt) {
-      const uint16_t* tp = tr_row + 8 * xchunk(32 * kh + 2 * mt + (tr_c >> 1));
+      const uint16_t* tp = tr_row + 8 * wchunk(tr_r, 32 * kh + 2 * mt + (tr_c >> 1));
       const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)tp);
-      const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tp + 4 * kXStride));
+      const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tp + 4 * kWStride));
       const bf16x8 A = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bhi, acc[mt], 0, 0, 0);
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Blo, acc[mt], 0, 0, 0);

@@ -570,13 +570,23 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
 // counting the b* entries' next 12 key bits into an LDS digit-2 histogram.  The
 // eight lists, taken in wavefront order, are the row's candidates in index order;
 // the boundary and the ordered compaction follow as in the last workgroup above.
-constexpr int kRowCap = 1024;           // listed entries per wavefront segment
+// Two workgroups share a compute unit (LDS <= 80 KB and <= 128 VGPRs each), so each
+// unit keeps twice the row bytes in flight: 0.81 against 1.27 ms for 4096 rows of
+// 132K scores, where a deeper counting round with one workgroup per unit gained
+// nothing.
+constexpr int kRowCap = 1008;           // listed entries per wavefront segment
 constexpr int kRowSelectQueries = 128;  // rows from which this kernel is used ...
 // ... when they fill the chip or are short: a few long rows (a 128-token replay over
 // a 1M-token cache) would leave most compute units idle while one workgroup per row
-// streams megabytes, so they take the chunked path
+// streams megabytes, so they take the chunked path.  Rows of at most kRowShort scores
+// (a Reindex layer's candidate pool of 2048 blocks) take this kernel at any count: one
+// workgroup reads the 64 KB in about the time the chunked path spends on its
+// cross-workgroup hand-over (21.9 against 25.0 us per pooled index_topk at 1M), while
+// at 65,536 scores the chunked path is faster (43 against 55 us for the gatekeeper
+// layer's call).
+constexpr int64_t kRowShort = 16384;
 inline bool select_by_row(int32_t nq, int64_t ld) {
-  return nq >= kRowSelectQueries && (nq >= 256 || ld <= 65536);
+  return (nq >= kRowSelectQueries && (nq >= 256 || ld <= 65536)) || ld <= kRowShort;
 }
 struct RowSmem {
   unsigned long long list[kWaves][kRowCap];
@@ -588,6 +598,7 @@ struct RowSmem {
   uint32_t ncand, ovf;
   unsigned long long min_s, bnd_s;
 };
+static_assert(sizeof(RowSmem) <= 80 * 1024, "two row workgroups per compute unit");
 struct RowLists {
   const unsigned long long (*list)[kRowCap];
   const uint32_t* cnt;
@@ -600,7 +611,7 @@ struct RowLists {
 
 // ncopies == 0: no counting pass ran; the workgroup counts its row's first digits
 // itself (a read of the row that leaves it in the caches for the listing pass).
-__global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restrict__ scores, int64_t ld,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void topk_row_kernel(const float* __restrict__ scores, int64_t ld,
                                                             const int32_t* __restrict__ n_visible, int k,
                                                             int32_t* __restrict__ topk_idx, uint32_t* __restrict__ hist,
                                                             int ncopies, const int32_t* __restrict__ pool, int npool) {

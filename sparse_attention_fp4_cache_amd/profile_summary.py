@@ -12,6 +12,12 @@
       same counter reads for a plain copy kernel of known size run in the same
       process (it reads N bytes and writes N bytes).
 
+  python -m sparse_attention_fp4_cache_amd.profile_summary counters PMC_DIR \
+        --counters A,B,... --kernels K1,K2,... --command "..."
+      Mean per dispatch of each named counter for each named kernel (substring
+      match), from one `--pmc` run; derived counters (MfmaUtil) are one value per
+      dispatch, hardware counters are summed over their dimensions.
+
 Only reads CSV files; touches no GPU.
 """
 from __future__ import annotations
@@ -23,7 +29,7 @@ import glob
 import os
 import sys
 
-SCAN_KERNEL = "index_score_kernel<4, 1, true, false>"  # the indexer stage's scan (64 heads, one query)
+SCAN_KERNEL = "index_score_kernel<4, 1, true, false, false>"  # the indexer stage's scan (64 heads, one query)
 COPY_KERNEL = "MulFunctor"  # torch's elementwise multiply, used as a read-N/write-N copy
 
 
@@ -32,6 +38,11 @@ def _col(row, *names):
         if n in row:
             return row[n]
     raise KeyError(names)
+
+
+def _short(name: str, width: int = 62) -> str:
+    short = name.split("(")[0].replace("void ", "")
+    return short if len(short) <= width else short[:width - 3] + "..."
 
 
 def stats(path: str, command: str) -> str:
@@ -107,7 +118,30 @@ def traffic(a) -> str:
         f"algorithmic_bytes_per_launch: {a.bytes_per_launch}",
         f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
         f"traffic_over_algorithmic: {(fetch_b + write_b) / a.bytes_per_launch:.3f}",
+        "#",
+        "# every kernel of the run: mean L2-miss bytes per dispatch (scaled as above)",
+        f"# {'kernel':62s} {'calls':>6s} {'fetch_bytes':>13s} {'write_bytes':>13s}",
     ]
+    for name in sorted(set(fetch) & set(write), key=lambda n: -sum(fetch[n]) / len(fetch[n])):
+        f_, w_ = fetch[name], write[name]
+        lines.append(f"# {_short(name):62s} {len(f_):6d} {sum(f_) / len(f_) * 1024 * f_fetch:13.0f} "
+                     f"{sum(w_) / len(w_) * 1024 * f_write:13.0f}")
+    return "\n".join(lines) + "\n"
+
+
+def counters(a) -> str:
+    names = [c for c in a.counters.split(",") if c]
+    kernels = [k for k in a.kernels.split(",") if k]
+    per = {c: _per_dispatch(a.dir, c) for c in names}
+    lines = [f"# rocprofv3 counters, mean per dispatch", f"# command: {a.command}", "#",
+             f"{'kernel':48s} {'calls':>6s} " + " ".join(f"{c:>30s}" for c in names)]
+    for k in kernels:
+        cols, calls = [], 0
+        for c in names:
+            vals = _pick(per[c], k)
+            calls = len(vals)
+            cols.append(f"{sum(vals) / len(vals):30.6g}")
+        lines.append(f"{_short(k, 48):48s} {calls:6d} " + " ".join(cols))
     return "\n".join(lines) + "\n"
 
 
@@ -127,8 +161,15 @@ def main(argv=None):
     t.add_argument("--command-write", required=True)
     t.add_argument("--source-hash", required=True)
     t.add_argument("--kernel", default=SCAN_KERNEL)
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--counters", required=True)
+    c.add_argument("--kernels", required=True)
+    c.add_argument("--command", required=True)
     a = p.parse_args(argv)
-    sys.stdout.write(stats(a.csv, a.command) if a.cmd == "stats" else traffic(a))
+    out = {"stats": lambda: stats(a.csv, a.command), "traffic": lambda: traffic(a),
+           "counters": lambda: counters(a)}[a.cmd]()
+    sys.stdout.write(out)
 
 
 if __name__ == "__main__":

@@ -1412,9 +1412,9 @@ extern "C" int index_topk_pool_build(const csa2_fp4_cache* cache, const uint16_t
   st = launch_hi(cache, q_idx, w, Hi, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld,
                  topk_digit1_hist(ws, nq, ld), k, &copies, stream, PoolArgs(), &pb);
   if (st != CSA2_OK) return st;
-  st = topk_enqueue(scores, ld, n_visible, nq, k, topk_idx, ws, stream, true, copies, nullptr, 0);
-  if (st != CSA2_OK) return st;
-  return topk_enqueue(pw.bmax, pw.ldb, pw.nblocks, nq, npool, pool, pw.ws_topk, stream, true, copies, nullptr, 0);
+  // the top-k of the scores and the top npool blocks, one selection launch for both
+  return topk_enqueue_pair(scores, ld, n_visible, nq, k, topk_idx, ws, copies, pw.bmax, pw.ldb, pw.nblocks, nq, npool,
+                           pool, pw.ws_topk, copies, stream);
 }
 
 // the pool workspace: visible pool positions per query, then the selection's workspace

@@ -29,6 +29,13 @@ int topk_enqueue(const float* scores, int64_t ld, const int32_t* n_visible, int3
                  int32_t* topk_idx, void* ws, hipStream_t stream, bool hist_done, int copies, const int32_t* pool,
                  int npool);
 
+// Two selections whose digit-1 histograms are already counted (copies_a / copies_b
+// copies), in one launch when both take the chunked path, else one after the other.
+int topk_enqueue_pair(const float* scores_a, int64_t ld_a, const int32_t* n_visible_a, int32_t nq_a, int32_t k_a,
+                      int32_t* topk_a, void* ws_a, int copies_a, const float* scores_b, int64_t ld_b,
+                      const int32_t* n_visible_b, int32_t nq_b, int32_t k_b, int32_t* topk_b, void* ws_b,
+                      int copies_b, hipStream_t stream);
+
 // The candidate-pool workspace of index_pool_build (nq rows of ld scores): the block
 // maxima [nq][ldb] (ldb = ceil(ld / 8)), the blocks per row [nq], then the top-npool
 // selection's workspace over the block maxima.

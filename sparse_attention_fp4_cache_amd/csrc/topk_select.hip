@@ -367,14 +367,38 @@ CSA2_DEV int32_t out_index(const int32_t* __restrict__ pool_row, int64_t i) {
   return pool_row ? 8 * pool_row[i >> 3] + (int32_t)(i & 7) : (int32_t)i;
 }
 
+// One selection over nq rows: its scores, visible counts, k, output and workspace.
+struct SelectJob {
+  const float* scores;
+  int64_t ld;
+  const int32_t* n_visible;
+  int k;
+  int32_t* topk_idx;
+  TopkWs ws;
+  int nchunk, ncopies;
+  const int32_t* pool;
+  int npool;
+  int nq;
+};
+
 // ---------------------------------------------------------------- kernel 2 --
-__global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __restrict__ scores, int64_t ld,
-                                                               const int32_t* __restrict__ n_visible, int k,
-                                                               int32_t* __restrict__ topk_idx, TopkWs ws,
-                                                               int nchunk, int ncopies,
-                                                               const int32_t* __restrict__ pool, int npool) {
+// Rows 0 .. ja.nq-1 of the grid serve job ja, the rows after them job jb (two
+// independent selections in one launch; jb.nq = 0 for one).
+__global__ __launch_bounds__(kThreads) void topk_select_kernel(SelectJob ja, SelectJob jb) {
   __shared__ SelectSmem sm;
-  const int q = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const bool second = (int)blockIdx.y >= ja.nq;  // uniform
+  const SelectJob jj = second ? jb : ja;
+  const float* __restrict__ scores = jj.scores;
+  const int64_t ld = jj.ld;
+  const int32_t* __restrict__ n_visible = jj.n_visible;
+  const int k = jj.k;
+  int32_t* __restrict__ topk_idx = jj.topk_idx;
+  const TopkWs ws = jj.ws;
+  const int nchunk = jj.nchunk, ncopies = jj.ncopies;
+  const int32_t* __restrict__ pool = jj.pool;
+  const int npool = jj.npool;
+  const int q = second ? (int)blockIdx.y - ja.nq : (int)blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t n = n_visible[q];
   const int64_t base = (int64_t)blockIdx.x * kChunk;
   int32_t* out = topk_idx + (int64_t)q * k;
@@ -839,14 +863,24 @@ uint32_t* topk_digit1_hist(void* ws, int32_t nq, int64_t ld) {
   return carve(ws, nq, nchunk).hist;
 }
 
+static long long select_grid_x(int64_t ld, int32_t k) {
+  const long long nchunk = ld > 0 ? (ld + kChunk - 1) / kChunk : 1;
+  const long long kchunk = (k + kChunk - 1) / kChunk;  // the n <= k path writes k outputs
+  return nchunk > kchunk ? nchunk : kchunk;
+}
+
+static SelectJob select_job(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq, int32_t k,
+                            int32_t* topk_idx, void* ws, int ncopies, const int32_t* pool, int npool) {
+  const long long nchunk = ld > 0 ? (ld + kChunk - 1) / kChunk : 1;
+  return SelectJob{scores, ld, n_visible, k, topk_idx, carve(ws, nq, nchunk), (int)nchunk, ncopies, pool, npool, nq};
+}
+
 int topk_enqueue(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq, int32_t k,
                  int32_t* topk_idx, void* ws, hipStream_t stream, bool hist_done, int copies, const int32_t* pool,
                  int npool) {
   const long long nchunk = ld > 0 ? (ld + kChunk - 1) / kChunk : 1;
-  const long long kchunk = (k + kChunk - 1) / kChunk;  // the n <= k path writes k outputs
-  const long long grid_x = nchunk > kchunk ? nchunk : kchunk;
   const TopkWs w = carve(ws, nq, nchunk);
-  const dim3 grid((unsigned)grid_x, (unsigned)nq);
+  const dim3 grid((unsigned)select_grid_x(ld, k), (unsigned)nq);
   const int ncopies = hist_done ? copies : topk_hist_copies(nchunk);
   const bool by_row = select_by_row(nq, ld);
   if (ld > 0 && !hist_done && !by_row)
@@ -856,8 +890,27 @@ int topk_enqueue(const float* scores, int64_t ld, const int32_t* n_visible, int3
                        topk_idx, w.hist, hist_done ? ncopies : 0, pool, npool);
     return launch_status();
   }
-  hipLaunchKernelGGL(topk_select_kernel, grid, dim3(kThreads), 0, stream, scores, ld, n_visible, k, topk_idx, w,
-                     (int)nchunk, ncopies, pool, npool);
+  SelectJob none{};
+  hipLaunchKernelGGL(topk_select_kernel, grid, dim3(kThreads), 0, stream,
+                     select_job(scores, ld, n_visible, nq, k, topk_idx, ws, ncopies, pool, npool), none);
+  return launch_status();
+}
+
+int topk_enqueue_pair(const float* scores_a, int64_t ld_a, const int32_t* n_visible_a, int32_t nq_a, int32_t k_a,
+                      int32_t* topk_a, void* ws_a, int copies_a, const float* scores_b, int64_t ld_b,
+                      const int32_t* n_visible_b, int32_t nq_b, int32_t k_b, int32_t* topk_b, void* ws_b,
+                      int copies_b, hipStream_t stream) {
+  if (select_by_row(nq_a, ld_a) || select_by_row(nq_b, ld_b) || ld_a <= 0 || ld_b <= 0) {
+    const int st = topk_enqueue(scores_a, ld_a, n_visible_a, nq_a, k_a, topk_a, ws_a, stream, true, copies_a,
+                                nullptr, 0);
+    if (st != CSA2_OK) return st;
+    return topk_enqueue(scores_b, ld_b, n_visible_b, nq_b, k_b, topk_b, ws_b, stream, true, copies_b, nullptr, 0);
+  }
+  const long long ga = select_grid_x(ld_a, k_a), gb = select_grid_x(ld_b, k_b);
+  const dim3 grid((unsigned)(ga > gb ? ga : gb), (unsigned)(nq_a + nq_b));
+  hipLaunchKernelGGL(topk_select_kernel, grid, dim3(kThreads), 0, stream,
+                     select_job(scores_a, ld_a, n_visible_a, nq_a, k_a, topk_a, ws_a, copies_a, nullptr, 0),
+                     select_job(scores_b, ld_b, n_visible_b, nq_b, k_b, topk_b, ws_b, copies_b, nullptr, 0));
   return launch_status();
 }
 

@@ -720,6 +720,8 @@ def test_index_topk_pool_build_equals_separate_calls():
     _gate_vs_separate(np.random.default_rng(321), [70000, 9001, 100, 8200], 64, 256, 1024)
     say("case: index_topk_pool_build with exact-path entries, 16 heads")
     _gate_vs_separate(np.random.default_rng(322), [40001], 16, 512, 300, key_fn=spread)
+    say("case: index_topk_pool_build, three rows in one paired selection launch (one keeps every block)")
+    _gate_vs_separate(np.random.default_rng(324), [300003, 140001, 5000], 64, 2048, 2048)
     say("case: index_topk_pool_build, queries sharing sequences (the two calls in turn)")
     _gate_vs_separate(np.random.default_rng(323), [5000, 3000], 32, 128, 64, seq_of_query=[0] * 40 + [1] * 30)
 

@@ -34,6 +34,7 @@
 #include "topk_internal.hpp"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace csa2 {
 
@@ -250,6 +251,13 @@ struct SelectSmem {
   unsigned long long min_s, bnd_s;
 };
 
+// LDS of a chunk workgroup that leaves the final pass to topk_select_kernel<2>.
+struct ChunkSmem {
+  uint32_t wsum[4][kWaves];
+  Digit dig[4];
+  int is_last;
+};
+
 // Candidates of the boundary: the listed entries in LDS, or (slow path) the score row.
 struct LdsCands {
   const unsigned long long* c;
@@ -384,8 +392,14 @@ struct SelectJob {
 // ---------------------------------------------------------------- kernel 2 --
 // Rows 0 .. ja.nq-1 of the grid serve job ja, the rows after them job jb (two
 // independent selections in one launch; jb.nq = 0 for one).
+// MODE 0: chunk workgroups, and the last one to arrive finishes its row (one launch).
+// MODE 1: chunk workgroups only; MODE 2: the finishing pass, one workgroup per row,
+// launched after MODE 1.  Only the finishing pass holds the 96 KB list in LDS, so the
+// chunk workgroups of MODE 1 run several to a compute unit: with thousands of chunks
+// (many rows) the single-launch form runs them one per unit.
+template <int MODE>
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(SelectJob ja, SelectJob jb) {
-  __shared__ SelectSmem sm;
+  __shared__ typename std::conditional<MODE == 1, ChunkSmem, SelectSmem>::type sm;
   const bool second = (int)blockIdx.y >= ja.nq;  // uniform
   const SelectJob jj = second ? jb : ja;
   const float* __restrict__ scores = jj.scores;
@@ -403,10 +417,12 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(SelectJob ja, Sel
   const int64_t base = (int64_t)blockIdx.x * kChunk;
   int32_t* out = topk_idx + (int64_t)q * k;
   const int32_t* pool_row = pool ? pool + (int64_t)q * npool : nullptr;
-  if (n <= k) {  // everything visible is selected, then -1 padding
-    for (int64_t i = base + tid; i < min(base + (int64_t)kChunk, n); i += kThreads) out[i] = out_index(pool_row, i);
-    if (blockIdx.x == 0)
-      for (int64_t i = n + tid; i < k; i += kThreads) out[i] = -1;
+  if (n <= k) {  // everything visible is selected, then -1 padding (by the chunk workgroups)
+    if (MODE != 2) {
+      for (int64_t i = base + tid; i < min(base + (int64_t)kChunk, n); i += kThreads) out[i] = out_index(pool_row, i);
+      if (blockIdx.x == 0)
+        for (int64_t i = n + tid; i < k; i += kThreads) out[i] = -1;
+    }
     return;
   }
   if (base >= n) return;
@@ -421,7 +437,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(SelectJob ja, Sel
   const float* row = scores + (int64_t)q * ld;
 
   uint32_t key[kPer];
-  load_keys(row, base, n, key);
+  if (MODE != 2) load_keys(row, base, n, key);
   uint32_t hb[kPerBins];
   uint32_t nz1 = 0;  // bit r: one of this thread's bins of copy r is nonzero (cleared at the end)
   {
@@ -452,6 +468,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(SelectJob ja, Sel
   const Digit d1 = find_digit(hb, (uint32_t)k, sm.wsum[0], &sm.dig[0]);
   const uint32_t bstar = (uint32_t)d1.d, above_b = d1.above;
 
+  if constexpr (MODE != 2) {
   // this chunk's entries in bins >= b*, in index order, into its region; its b*
   // entries also go into the digit-2 histogram
   uint32_t m = 0;
@@ -473,12 +490,18 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(SelectJob ja, Sel
       ++p;
     }
   if (tid == 0) st_agent(gcount + blockIdx.x, tot);
-  wait_all_memory();  // this workgroup's list entries, count and histogram adds are done
-  __syncthreads();
-  if (tid == 0) sm.is_last = (atomicAdd(&ctl->arrive, 1u) == (uint32_t)(nch - 1));
-  __syncthreads();
-  if (!sm.is_last) return;
+  if constexpr (MODE == 1) {
+    return;  // the finishing pass is the next launch
+  } else {
+    wait_all_memory();  // this workgroup's list entries, count and histogram adds are done
+    __syncthreads();
+    if (tid == 0) sm.is_last = (atomicAdd(&ctl->arrive, 1u) == (uint32_t)(nch - 1));
+    __syncthreads();
+    if (!sm.is_last) return;
+  }
+  }  // MODE != 2
 
+  if constexpr (MODE != 1) {
   // ---- last workgroup of this query: every region, count and histogram is in place
   const uint32_t need = (uint32_t)k - above_b;  // 1 <= need <= entries in b*
   // one round of device-coherent loads: the chunk counts, the digit-2 histogram and
@@ -584,6 +607,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(SelectJob ja, Sel
     reinterpret_cast<uint4*>(gh2 + bins_lo())[1] = z4;
   }
   if (tid == 0) ctl->arrive = 0u;
+  }  // MODE != 1
 }
 
 // ------------------------------------------------------- one row per workgroup --
@@ -602,15 +626,15 @@ constexpr int kRowCap = 1008;           // listed entries per wavefront segment
 constexpr int kRowSelectQueries = 128;  // rows from which this kernel is used ...
 // ... when they fill the chip or are short: a few long rows (a 128-token replay over
 // a 1M-token cache) would leave most compute units idle while one workgroup per row
-// streams megabytes, so they take the chunked path.  Rows of at most kRowShort scores
-// (a Reindex layer's candidate pool of 2048 blocks) take this kernel at any count: one
-// workgroup reads the 64 KB in about the time the chunked path spends on its
-// cross-workgroup hand-over (21.9 against 25.0 us per pooled index_topk at 1M), while
-// at 65,536 scores the chunked path is faster (43 against 55 us for the gatekeeper
-// layer's call).
+// streams megabytes, so they take the chunked path.  Rows of more than one chunk and
+// at most kRowShort scores (a Reindex layer's candidate pool of 2048 blocks) take this
+// kernel at any count: one workgroup reads the 64 KB in about the time the chunked
+// path spends on its cross-workgroup hand-over (21.9 against 25.0 us per pooled
+// index_topk at 1M), while at 65,536 scores the chunked path is faster (43 against
+// 55 us for the gatekeeper layer's call).  A row of one chunk has no hand-over.
 constexpr int64_t kRowShort = 16384;
 inline bool select_by_row(int32_t nq, int64_t ld) {
-  return (nq >= kRowSelectQueries && (nq >= 256 || ld <= 65536)) || ld <= kRowShort;
+  return (nq >= kRowSelectQueries && (nq >= 256 || ld <= 65536)) || (ld > kChunk && ld <= kRowShort);
 }
 struct RowSmem {
   unsigned long long list[kWaves][kRowCap];
@@ -869,6 +893,21 @@ static long long select_grid_x(int64_t ld, int32_t k) {
   return nchunk > kchunk ? nchunk : kchunk;
 }
 
+// Chunk workgroups in one launch with their finishing pass while they fit the chip
+// about twice; beyond that the chunks run as their own launch (several workgroups per
+// compute unit) and one workgroup per row finishes: topk_select over 128 rows of 524K
+// scores (16,384 chunks) takes 215 against 544 us, the 8-sequence 1M decode step 674
+// against 735 us.
+constexpr long long kSplitChunks = 512;
+static void launch_select(dim3 grid, const SelectJob& ja, const SelectJob& jb, hipStream_t stream) {
+  if ((long long)grid.x * grid.y <= kSplitChunks) {
+    hipLaunchKernelGGL(topk_select_kernel<0>, grid, dim3(kThreads), 0, stream, ja, jb);
+    return;
+  }
+  hipLaunchKernelGGL(topk_select_kernel<1>, grid, dim3(kThreads), 0, stream, ja, jb);
+  hipLaunchKernelGGL(topk_select_kernel<2>, dim3(1u, grid.y), dim3(kThreads), 0, stream, ja, jb);
+}
+
 static SelectJob select_job(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq, int32_t k,
                             int32_t* topk_idx, void* ws, int ncopies, const int32_t* pool, int npool) {
   const long long nchunk = ld > 0 ? (ld + kChunk - 1) / kChunk : 1;
@@ -891,8 +930,7 @@ int topk_enqueue(const float* scores, int64_t ld, const int32_t* n_visible, int3
     return launch_status();
   }
   SelectJob none{};
-  hipLaunchKernelGGL(topk_select_kernel, grid, dim3(kThreads), 0, stream,
-                     select_job(scores, ld, n_visible, nq, k, topk_idx, ws, ncopies, pool, npool), none);
+  launch_select(grid, select_job(scores, ld, n_visible, nq, k, topk_idx, ws, ncopies, pool, npool), none, stream);
   return launch_status();
 }
 
@@ -908,9 +946,8 @@ int topk_enqueue_pair(const float* scores_a, int64_t ld_a, const int32_t* n_visi
   }
   const long long ga = select_grid_x(ld_a, k_a), gb = select_grid_x(ld_b, k_b);
   const dim3 grid((unsigned)(ga > gb ? ga : gb), (unsigned)(nq_a + nq_b));
-  hipLaunchKernelGGL(topk_select_kernel, grid, dim3(kThreads), 0, stream,
-                     select_job(scores_a, ld_a, n_visible_a, nq_a, k_a, topk_a, ws_a, copies_a, nullptr, 0),
-                     select_job(scores_b, ld_b, n_visible_b, nq_b, k_b, topk_b, ws_b, copies_b, nullptr, 0));
+  launch_select(grid, select_job(scores_a, ld_a, n_visible_a, nq_a, k_a, topk_a, ws_a, copies_a, nullptr, 0),
+                select_job(scores_b, ld_b, n_visible_b, nq_b, k_b, topk_b, ws_b, copies_b, nullptr, 0), stream);
   return launch_status();
 }
 

@@ -347,7 +347,9 @@ def test_topk_many_long_rows_one_workgroup_per_row():
 
 def test_topk_few_long_rows_take_chunks():
     """130 rows of 70,000 scores (too few rows to fill the chip with one workgroup
-    each): the chunked path with many rows, ragged, tied and short rows included."""
+    each): the chunked path with many rows, ragged, tied and short rows included.
+    Its 2,340 chunk workgroups take the split form (chunk launch, then one finishing
+    workgroup per row), and the all-equal row its slow path."""
     rng = np.random.default_rng(331)
     nq, ld = 130, 70_000
     s = rng.standard_normal((nq, ld)).astype(np.float32)

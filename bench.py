@@ -56,6 +56,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="decode_1m_10layer")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-threads", type=int, default=0,
+                   help="threads of the CPU oracle baseline (0: the OpenMP default of the host)")
     p.add_argument("--graph", type=int, default=1, help="replay the step as one HIP graph (1) or launch eagerly (0)")
     p.add_argument("--replicas", type=int, default=0,
                    help="cache copies rotated in cold mode (0: enough that the other copies' touched bytes "
@@ -525,6 +527,9 @@ def main():
                                       "frac": attn_flop / (attn_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                                       "flop_per_launch": attn_flop}
     if not args.no_cpu_baseline:
+        import oracle  # the CPU baseline leg only
+
+        oracle.set_num_threads(args.cpu_threads)
         res["cpu_baseline"] = cpu_baseline(wl)
         res["cpu_baseline"]["cpu_model"] = cpu_model()
     print(json.dumps(res), flush=True)

@@ -85,6 +85,7 @@ def lib():
         L.oracle_global_bytes_per_token.argtypes = [_P, _P, _I32]
         L.oracle_global_bytes_per_token.restype = ctypes.c_double
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_num_threads.argtypes = [_I32]
         L.oracle_causal_n_visible.argtypes = [_P, _I64, _I32, _P]
         _lib = L
     return _lib
@@ -103,6 +104,11 @@ def _arr(a, dtype) -> np.ndarray:
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from now on (n <= 0: the OpenMP default)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------- formats --

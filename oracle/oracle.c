@@ -617,3 +617,7 @@ double oracle_global_bytes_per_token(const int32_t* mode, const int32_t* m, int3
 /* Number of OpenMP threads a parallel region of the oracle uses. */
 #include <omp.h>
 int oracle_num_threads(void) { return omp_get_max_threads(); }
+/* threads of the parallel loops from now on (n <= 0 leaves the OpenMP default) */
+void oracle_set_num_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
+}

@@ -724,6 +724,8 @@ def test_index_topk_pool_build_equals_separate_calls():
     _gate_vs_separate(np.random.default_rng(322), [40001], 16, 512, 300, key_fn=spread)
     say("case: index_topk_pool_build, three rows in one paired selection launch (one keeps every block)")
     _gate_vs_separate(np.random.default_rng(324), [300003, 140001, 5000], 64, 2048, 2048)
+    say("case: index_topk_pool_build, six 200,003-entry rows (the paired launch in its split form)")
+    _gate_vs_separate(np.random.default_rng(325), [200003] * 6, 64, 2048, 2048, reps=1)
     say("case: index_topk_pool_build, queries sharing sequences (the two calls in turn)")
     _gate_vs_separate(np.random.default_rng(323), [5000, 3000], 32, 128, 64, seq_of_query=[0] * 40 + [1] * 30)
 

@@ -621,7 +621,8 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(SelectJob ja, Sel
 // Two workgroups share a compute unit (LDS <= 80 KB and <= 128 VGPRs each), so each
 // unit keeps twice the row bytes in flight: 0.81 against 1.27 ms for 4096 rows of
 // 132K scores, where a deeper counting round with one workgroup per unit gained
-// nothing.
+// nothing.  The listing walks 4 x 256 entries per step (70 VGPRs, no scratch): 8 x 256
+// needed spills at 128 VGPRs and was no faster.
 constexpr int kRowCap = 1008;           // listed entries per wavefront segment
 constexpr int kRowSelectQueries = 128;  // rows from which this kernel is used ...
 // ... when they fill the chip or are short: a few long rows (a 128-token replay over
@@ -734,7 +735,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 
   // this wavefront's segment [s0, s1), U x 256 entries per step (thread: 4 consecutive
   // entries per 256); order within a step: u, then lane, then the 4 entries
-  constexpr int U = 8;
+  constexpr int U = 4;
   const int64_t seg = (((n + kWaves - 1) / kWaves) + 255) & ~(int64_t)255;
   const int64_t s0 = min(n, (int64_t)wid * seg), s1 = min(n, s0 + seg);
   const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;

@@ -150,6 +150,26 @@ int index_topk(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* 
                int32_t nq, float* scores, int64_t ld, int32_t k, int32_t* topk_idx, void* ws, size_t ws_bytes,
                hipStream_t stream);
 
+/* index_score_counted, topk_select_counted -- index_topk as two calls, for callers
+ * that want the scores before the selection runs (or time the two apart).
+ * Source: as for index_topk.
+ * index_score_counted: index_score (same arguments and scores) that also leaves the
+ *   selection's first-digit histogram of each row with n_visible > k in ws (the
+ *   topk_select workspace for (nq, ld, k), same zero-fill contract).  With one query
+ *   per workgroup it counts as it scores, the kernel index_topk runs; otherwise a
+ *   counting pass follows the scan.
+ * topk_select_counted: topk_select (same arguments and indices) that takes those
+ *   counts from ws instead of counting; call it next on the same scores, k and ws,
+ *   with no other use of ws in between.  It returns ws to its zero state.
+ * Together they give scores and indices bit-identical to index_topk.  Errors as for
+ * index_score and topk_select. */
+int index_score_counted(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
+                        const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* block_table,
+                        int32_t max_pages, int32_t nq, float* scores, int64_t ld, int32_t k, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+int topk_select_counted(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq, int32_t k,
+                        int32_t* topk_idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* index_topk_noalloc -- index_topk for callers that cannot allocate device memory:
  * code under HIP graph capture, tight serving loops, harnesses that forbid it.  The
  * same arguments without ws / ws_bytes and the same results (bit for bit): the

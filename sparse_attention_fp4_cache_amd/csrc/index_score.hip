@@ -1156,7 +1156,7 @@ template <int MT>
 static int launch_mt(const csa2_fp4_cache* c, const uint16_t* q_idx, const float* w, const int32_t* soq,
                      const int32_t* nvis, const int32_t* bt, int32_t max_pages, int32_t nq, float* scores, int64_t ld,
                      uint32_t* hist, int k, int* copies, const PoolArgs& pa, hipStream_t stream,
-                     const PoolBuildArgs* pb = nullptr) {
+                     const PoolBuildArgs* pb = nullptr, int force_copies = 0) {
   const int total_groups = (int)ceil_div(ld, kPage);
   if (total_groups == 0 || nq == 0) return CSA2_OK;
   // queries per workgroup: several queries of one sequence share each loaded page
@@ -1172,7 +1172,7 @@ static int launch_mt(const csa2_fp4_cache* c, const uint16_t* q_idx, const float
   const unsigned gx = ceil_div(total_groups, (long long)kWaves * gpw);
   const dim3 grid(gx, (unsigned)qtiles), block(kThreads);
   const size_t lds = sizeof(QStage<MT>) * qt;
-  const int ncopies = topk_hist_copies(gx);
+  const int ncopies = force_copies > 0 ? force_copies : topk_hist_copies(gx);
   if (copies != nullptr) *copies = ncopies;
   if (pb != nullptr) {  // one query per workgroup, with its digit-1 counts (the caller checked)
     hipLaunchKernelGGL((index_score_kernel<MT, 1, true, false, true>), grid, block,
@@ -1235,7 +1235,7 @@ static int launch_hi(const csa2_fp4_cache* cache, const uint16_t* q_idx, const f
                      const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* block_table,
                      int32_t max_pages, int32_t nq, float* scores, int64_t ld, uint32_t* hist, int k,
                      int* copies, hipStream_t stream, const PoolArgs& pa = PoolArgs(),
-                     const PoolBuildArgs* pb = nullptr) {
+                     const PoolBuildArgs* pb = nullptr, int force_copies = 0) {
   // queries that share sequences, at most 64 heads: two queries per wavefront (two
   // score rows within one buffer resource's 2^31-byte range)
   if (pa.pool == nullptr && hist == nullptr && query_tile(seq_of_query, nq, 0) > 1 && Hi <= 64 &&
@@ -1252,7 +1252,7 @@ static int launch_hi(const csa2_fp4_cache* cache, const uint16_t* q_idx, const f
 #define CSA2_MT(m) \
   case m:          \
     return launch_mt<m>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, hist, k, \
-                        copies, pa, stream, pb);
+                        copies, pa, stream, pb, force_copies);
     CSA2_MT(1)
     CSA2_MT(2)
     CSA2_MT(3)
@@ -1261,7 +1261,7 @@ static int launch_hi(const csa2_fp4_cache* cache, const uint16_t* q_idx, const f
     CSA2_MT(6)
     CSA2_MT(7)
     default: return launch_mt<8>(cache, q_idx, w, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld,
-                                 hist, k, copies, pa, stream, pb);
+                                 hist, k, copies, pa, stream, pb, force_copies);
 #undef CSA2_MT
   }
 }
@@ -1328,6 +1328,29 @@ extern "C" int index_topk(const csa2_fp4_cache* cache, const uint16_t* q_idx, co
     if (st != CSA2_OK) return st;
   }
   return topk_enqueue(scores, ld, n_visible, nq, k, topk_idx, ws, stream, fuse, copies, nullptr, 0);
+}
+
+// ---- index_topk as two calls: the counting scan, then the selection --------------
+// index_score_counted leaves the selection's first-digit histogram (always in all
+// kTopkHistCopies copies, so that topk_select_counted needs no knowledge of how it was
+// counted) in the top-k workspace; with one query per workgroup the scan counts as it
+// scores, as inside index_topk, otherwise a counting pass follows the scan.
+extern "C" int index_score_counted(const csa2_fp4_cache* cache, const uint16_t* q_idx, const float* w, int32_t Hi,
+                                   const int32_t* seq_of_query, const int32_t* n_visible, const int32_t* block_table,
+                                   int32_t max_pages, int32_t nq, float* scores, int64_t ld, int32_t k, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  int st = check_args(cache, q_idx, w, Hi, n_visible, block_table, max_pages, nq, scores, ld);
+  if (st != CSA2_OK) return st;
+  if (k < 1 || k > CSA2_MAX_K || ld >= ((int64_t)1 << 31)) return CSA2_ERR_SHAPE;
+  if (nq == 0 || ld == 0) return CSA2_OK;
+  if (!ws || ws_bytes < topk_select_workspace_size(nq, ld, k)) return CSA2_ERR_WORKSPACE;
+  if (query_tile(seq_of_query, nq, 0) == 1)
+    return launch_hi(cache, q_idx, w, Hi, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld,
+                     topk_digit1_hist(ws, nq, ld), k, nullptr, stream, PoolArgs(), nullptr, kTopkHistCopies);
+  st = launch_hi(cache, q_idx, w, Hi, seq_of_query, n_visible, block_table, max_pages, nq, scores, ld, nullptr, k,
+                 nullptr, stream);
+  if (st != CSA2_OK) return st;
+  return topk_count(scores, ld, n_visible, nq, k, ws, kTopkHistCopies, stream);
 }
 
 // ---- index_topk without allocation: the workspace in a static device array --------

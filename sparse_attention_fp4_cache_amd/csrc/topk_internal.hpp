@@ -29,6 +29,11 @@ int topk_enqueue(const float* scores, int64_t ld, const int32_t* n_visible, int3
                  int32_t* topk_idx, void* ws, hipStream_t stream, bool hist_done, int copies, const int32_t* pool,
                  int npool);
 
+// The counting pass alone: each row's digit-1 histogram into `copies` copies of the
+// top-k workspace ws (rows with n_visible <= k are not counted).
+int topk_count(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq, int32_t k, void* ws,
+               int copies, hipStream_t stream);
+
 // Two selections whose digit-1 histograms are already counted (copies_a / copies_b
 // copies), in one launch when both take the chunked path, else one after the other.
 int topk_enqueue_pair(const float* scores_a, int64_t ld_a, const int32_t* n_visible_a, int32_t nq_a, int32_t k_a,

@@ -935,6 +935,16 @@ int topk_enqueue(const float* scores, int64_t ld, const int32_t* n_visible, int3
   return launch_status();
 }
 
+int topk_count(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq, int32_t k, void* ws,
+               int copies, hipStream_t stream) {
+  if (ld <= 0 || nq == 0) return CSA2_OK;
+  const long long nchunk = (ld + kChunk - 1) / kChunk;
+  const dim3 grid((unsigned)select_grid_x(ld, k), (unsigned)nq);
+  hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kThreads), 0, stream, scores, ld, n_visible, k,
+                     carve(ws, nq, nchunk), copies);
+  return launch_status();
+}
+
 int topk_enqueue_pair(const float* scores_a, int64_t ld_a, const int32_t* n_visible_a, int32_t nq_a, int32_t k_a,
                       int32_t* topk_a, void* ws_a, int copies_a, const float* scores_b, int64_t ld_b,
                       const int32_t* n_visible_b, int32_t nq_b, int32_t k_b, int32_t* topk_b, void* ws_b,
@@ -1022,6 +1032,16 @@ extern "C" int index_pool_build(const float* scores, int64_t ld, const int32_t* 
   hipLaunchKernelGGL(pool_bmax_kernel, grid, dim3(kBmaxThreads), 0, stream, scores, ld, n_visible, bmax, ldb, nb);
   if (launch_status() != CSA2_OK) return CSA2_ERR_LAUNCH;
   return topk_enqueue(bmax, ldb, nb, nq, npool, pool, ws_topk, stream, false, 1, nullptr, 0);
+}
+
+extern "C" int topk_select_counted(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq,
+                                   int32_t k, int32_t* topk_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (nq < 0 || ld < 0 || k < 1 || k > CSA2_MAX_K) return CSA2_ERR_SHAPE;
+  if (ld >= ((int64_t)1 << 31)) return CSA2_ERR_SHAPE;
+  if (nq == 0) return CSA2_OK;
+  if (!n_visible || !topk_idx || (ld > 0 && !scores)) return CSA2_ERR_NULL;
+  if (!ws || ws_bytes < topk_select_workspace_size(nq, ld, k)) return CSA2_ERR_WORKSPACE;
+  return topk_enqueue(scores, ld, n_visible, nq, k, topk_idx, ws, stream, true, kTopkHistCopies, nullptr, 0);
 }
 
 extern "C" int topk_select(const float* scores, int64_t ld, const int32_t* n_visible, int32_t nq, int32_t k,

@@ -29,6 +29,8 @@ EXPORTS = (
     "topk_select_workspace_size",
     "topk_select",
     "index_topk",
+    "index_score_counted",
+    "topk_select_counted",
     "index_pool_build_workspace_size",
     "index_pool_build",
     "index_topk_pool_build_workspace_size",
@@ -88,6 +90,9 @@ def load() -> ctypes.CDLL:
         L.topk_select.argtypes = [_P, _I64, _P, _I32, _I32, _P, _P, _SZ, _P]
         L.index_topk.argtypes = [ctypes.POINTER(_CacheStruct), _P, _P, _I32, _P, _P, _P, _I32, _I32, _P, _I64, _I32,
                                  _P, _P, _SZ, _P]
+        L.index_score_counted.argtypes = [ctypes.POINTER(_CacheStruct), _P, _P, _I32, _P, _P, _P, _I32, _I32, _P,
+                                          _I64, _I32, _P, _SZ, _P]
+        L.topk_select_counted.argtypes = [_P, _I64, _P, _I32, _I32, _P, _P, _SZ, _P]
         L.index_pool_build_workspace_size.argtypes = [_I32, _I64, _I32]
         L.index_pool_build_workspace_size.restype = _SZ
         L.index_pool_build.argtypes = [_P, _I64, _P, _I32, _I32, _P, _P, _SZ, _P]
@@ -246,6 +251,35 @@ def index_topk(cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, n_visible: to
                                            _ptr(scores, torch.float32, "scores"), scores.shape[1], k,
                                            _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(ws, torch.uint8, "ws"),
                                            ws.numel(), _stream(stream)))
+
+
+def index_score_counted(cache: Cache, q_idx: torch.Tensor, w: torch.Tensor, n_visible: torch.Tensor,
+                        block_table: torch.Tensor, scores: torch.Tensor, k: int, ws: torch.Tensor,
+                        seq_of_query: torch.Tensor | None = None, stream=None):
+    """index_score that also leaves the selection's first-digit counts in ws (the first
+    half of index_topk)."""
+    nq, Hi, d = q_idx.shape
+    if d != INDEX_DIM or w.shape != (nq, Hi) or n_visible.shape != (nq,) or scores.dim() != 2 or scores.shape[0] != nq:
+        raise ValueError("shape mismatch in index_score_counted arguments")
+    _check("index_score_counted",
+           load().index_score_counted(cache.struct, _bits16(q_idx, "q_idx"), _ptr(w, torch.float32, "w"), Hi,
+                                      _ptr(seq_of_query, torch.int32, "seq_of_query"),
+                                      _ptr(n_visible, torch.int32, "n_visible"),
+                                      _ptr(block_table, torch.int32, "block_table"), block_table.shape[1], nq,
+                                      _ptr(scores, torch.float32, "scores"), scores.shape[1], k,
+                                      _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+
+
+def topk_select_counted(scores: torch.Tensor, n_visible: torch.Tensor, k: int, topk_idx: torch.Tensor,
+                        ws: torch.Tensor, stream=None):
+    """topk_select taking its first-digit counts from ws (the second half of index_topk)."""
+    nq, ld = scores.shape
+    if n_visible.shape != (nq,) or topk_idx.shape != (nq, k):
+        raise ValueError("shape mismatch in topk_select_counted arguments")
+    _check("topk_select_counted",
+           load().topk_select_counted(_ptr(scores, torch.float32, "scores"), ld, _ptr(n_visible, torch.int32, "n_visible"),
+                                      nq, k, _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(ws, torch.uint8, "ws"),
+                                      ws.numel(), _stream(stream)))
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20  # CSA2_NOALLOC_SCRATCH_BYTES

@@ -151,6 +151,30 @@ def test_index_topk_validation(L):
     assert call(args(nq=0)) == 0
 
 
+def test_counted_pair_validation(L):
+    ws = L.topk_select_workspace_size(1, 4096, 64)
+    args = lambda **kw: dict(dict(cache=_cache(), q=FAKE, w=FAKE, Hi=64, soq=None, nv=FAKE, bt=FAKE, mp=64, nq=1,
+                                  sc=FAKE, ld=4096, k=64, ws=FAKE, wsb=ws), **kw)
+    score = lambda a: L.index_score_counted(a["cache"], a["q"], a["w"], a["Hi"], a["soq"], a["nv"], a["bt"], a["mp"],
+                                            a["nq"], a["sc"], a["ld"], a["k"], a["ws"], a["wsb"], None)
+    assert score(args(cache=_cache(null=True))) == -1
+    assert score(args(Hi=40)) == -2
+    assert score(args(k=0)) == -2
+    assert score(args(k=4097)) == -2
+    assert score(args(ws=None)) == -4
+    assert score(args(wsb=ws - 1)) == -4
+    assert score(args(mp=10)) == -2
+    assert score(args(nq=0)) == 0
+    sel = lambda k=64, idx=FAKE, w_=FAKE, wsb=ws, nq=1: L.topk_select_counted(FAKE, 4096, FAKE, nq, k, idx, w_, wsb,
+                                                                              None)
+    assert sel(k=0) == -2
+    assert sel(k=4097) == -2
+    assert sel(idx=None) == -1
+    assert sel(w_=None) == -4
+    assert sel(wsb=ws - 1) == -4
+    assert sel(nq=0) == 0
+
+
 def test_attention_validation(L):
     c = _cache()
     ws = L.sparse_attn_decode_workspace_size(1, 64, 2048, 128)

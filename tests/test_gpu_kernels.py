@@ -528,9 +528,10 @@ def test_index_score_reveals_query_quantisation():
     assert len(bad) == 0, f"{len(bad)} differ, first {bad[:5].tolist()}: {got[tuple(bad[0])]} vs {ref[tuple(bad[0])]}"
 
 
-def _fused_vs_separate(rng, n_per_seq, Hi, k, key_fn=None, seq_of_query=None, reps=2):
-    """index_topk against index_score followed by topk_select (bit for bit), on a
-    paged cache; called `reps` times on one workspace (it must be left clean)."""
+def _fused_vs_separate(rng, n_per_seq, Hi, k, key_fn=None, seq_of_query=None, reps=2, counted=False):
+    """index_topk (or, with counted, index_score_counted then topk_select_counted)
+    against index_score followed by topk_select (bit for bit), on a paged cache;
+    called `reps` times on one workspace (it must be left clean)."""
     B = len(n_per_seq)
     pages = [(n + 63) // 64 for n in n_per_seq]
     phys = rng.permutation(sum(pages))
@@ -565,7 +566,11 @@ def _fused_vs_separate(rng, n_per_seq, Hi, k, key_fn=None, seq_of_query=None, re
     for rep in range(reps):
         s_f = torch.full((nq, ld), float("nan"), device="cuda")
         i_f = torch.full((nq, k), -7, dtype=torch.int32, device="cuda")
-        lib.index_topk(g, dq, dw, dnv, dbt, s_f, k, i_f, ws, seq_of_query=dsoq)
+        if counted:
+            lib.index_score_counted(g, dq, dw, dnv, dbt, s_f, k, ws, seq_of_query=dsoq)
+            lib.topk_select_counted(s_f, dnv, k, i_f, ws)
+        else:
+            lib.index_topk(g, dq, dw, dnv, dbt, s_f, k, i_f, ws, seq_of_query=dsoq)
         torch.cuda.synchronize()
         a, b = s_f.cpu().numpy(), s_sep.cpu().numpy()
         for r in range(nq):
@@ -585,6 +590,18 @@ def test_index_topk_fused_equals_separate_calls():
     _fused_vs_separate(rng, [20000, 200, 9000], 64, 256)
     say("case: index_topk fused, one long row (many chunks)")
     _fused_vs_separate(rng, [70000], 64, 2048)
+
+
+def test_index_score_counted_then_topk_select_counted_equal_separate_calls():
+    rng = np.random.default_rng(303)
+    say("case: counted pair (3 ragged sequences, one with n <= k), twice on one workspace")
+    _fused_vs_separate(rng, [20000, 200, 9000], 64, 256, counted=True)
+    say("case: counted pair, one long row (many chunks)")
+    _fused_vs_separate(rng, [300003], 64, 2048, counted=True)
+    say("case: counted pair, queries sharing sequences (a counting pass after the scan)")
+    _fused_vs_separate(rng, [5000, 3000], 32, 128, seq_of_query=[0] * 40 + [1] * 30, counted=True)
+    say("case: counted pair, 16 index heads, one chunk per row")
+    _fused_vs_separate(rng, [3000, 4096, 50], 16, 64, counted=True)
 
 
 def test_index_topk_fused_exact_path_entries():

@@ -369,6 +369,21 @@ def test_topk_large_row_many_chunks():
     _topk_case(s, np.array([600_000], np.int32), 2048, "600k")
 
 
+def test_topk_largest_k():
+    """k = 4096, the largest supported: rows longer than k, equal to it, one short of
+    it and empty, with ties (chunked path and one workgroup per row)."""
+    rng = np.random.default_rng(333)
+    nq, ld = 6, 70_000
+    s = rng.standard_normal((nq, ld)).astype(np.float32)
+    s[1] = rng.integers(0, 200, ld).astype(np.float32)  # many ties around the boundary
+    nvis = np.array([ld, ld, 5000, 4096, 4095, 0], np.int32)
+    say("case: top-k with k = 4096 (chunked)")
+    _topk_case(s, nvis, 4096, "k=4096 chunked")
+    s2 = rng.standard_normal((3, 12_000)).astype(np.float32)
+    say("case: top-k with k = 4096 (rows of 12,000: one workgroup per row)")
+    _topk_case(s2, np.array([12_000, 4097, 4096], np.int32), 4096, "k=4096 by row")
+
+
 # --------------------------------------------------------------- attention --
 def _attn_cache(rng, n, outliers=False):
     x = rng.standard_normal((n, 512)).astype(np.float32)
@@ -495,6 +510,52 @@ def test_attention_decode_many_sequences():
     lib.sparse_attn_decode(g, dev_bits(q), dev(idx), dev(bt), dev_bits(swa), dev(swa_len), scale, out, lse, ws)
     ro, rl = oracle.sparse_attn_decode(o, q, idx, bt, swa, swa_len, scale)
     attn_close(out.cpu().numpy(), ro, lse.cpu().numpy(), rl, "decode 64 sequences")
+
+
+@pytest.mark.timeout(600)
+def test_attention_largest_k_and_window():
+    """k = 4096 selected entries plus a 128-row window (4,224 rows, the most a query
+    attends to): decode (row ranges and the merge) and a prefill chunk of 64 queries
+    (one workgroup per query over all 4,224 rows)."""
+    rng = np.random.default_rng(450)
+    n, H, k, W = 9000, 64, 4096, 128
+    g, o = _attn_cache(rng, n)
+    scale = 1 / math.sqrt(512)
+    B = 2
+    bt = np.tile(np.arange((n + 63) // 64, dtype=np.int32), (B, 1))
+    idx = np.stack([np.sort(rng.choice(n, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    idx[1, 4000:] = -1
+    q = bits(rng.standard_normal((B, H, 512)))
+    swa = bits(rng.standard_normal((B, W, 512)))
+    swa_len = np.array([128, 77], np.int32)
+    out = torch.zeros((B, H, 512), device="cuda")
+    lse = torch.zeros((B, H), device="cuda")
+    ws = torch.zeros(lib.sparse_attn_decode_workspace_size(B, H, k, W), dtype=torch.uint8, device="cuda")
+    say("case: attention decode, k = 4096 and a full window")
+    lib.sparse_attn_decode(g, dev_bits(q), dev(idx), dev(bt), dev_bits(swa), dev(swa_len), scale, out, lse, ws)
+    ro, rl = oracle.sparse_attn_decode(o, q, idx, bt, swa, swa_len, scale)
+    attn_close(out.cpu().numpy(), ro, lse.cpu().numpy(), rl, "decode k=4096")
+    T = 64
+    bt1 = np.arange((n + 63) // 64, dtype=np.int32)
+    idx = np.stack([np.sort(rng.choice(n, k, replace=False)) for _ in range(T)]).astype(np.int32)
+    idx[7, 3000:] = -1
+    q = bits(rng.standard_normal((T, H, 512)))
+    swa = bits(rng.standard_normal((W - 1 + T, 512)))
+    out = torch.zeros((T, H, 512), device="cuda")
+    lse = torch.zeros((T, H), device="cuda")
+    ws = torch.zeros(max(256, lib.sparse_attn_prefill_chunk_workspace_size(T, H, k, W)), dtype=torch.uint8,
+                     device="cuda")
+    say("case: attention prefill, k = 4096 and a full window, 64 queries")
+    lib.sparse_attn_prefill_chunk(g, dev_bits(q), dev(idx), dev(bt1), 20000, dev_bits(swa), 0, W, scale, out, lse,
+                                  ws)
+    ro, rl = oracle.sparse_attn_prefill_chunk(o, q, idx, bt1, swa, 0, W, scale)
+    attn_close(out.cpu().numpy(), ro, lse.cpu().numpy(), rl, "prefill k=4096")
+
+
+def test_index_topk_largest_k():
+    rng = np.random.default_rng(304)
+    say("case: index_topk with k = 4096 (rows longer, equal and shorter than k)")
+    _fused_vs_separate(rng, [70000, 4096, 3000, 20000], 64, 4096)
 
 
 def test_index_score_reveals_query_quantisation():

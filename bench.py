@@ -257,8 +257,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
-                                   "not part of the measured path", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only; sharding the path over several GPUs "
+                                   "is described, not implemented", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch

@@ -639,8 +639,9 @@ inline bool select_by_row(int32_t nq, int64_t ld) {
 }
 struct RowSmem {
   unsigned long long list[kWaves][kRowCap];
-  uint32_t h[kBins];  // digit-2 histogram of the b* entries, then radix-round scratch
+  uint32_t h[kBins];  // digit-1 or digit-2 counts, then radix-round scratch
   uint32_t cnt[kWaves];
+  uint32_t wtot[kWaves];  // entries each wavefront selected, past kRowCap too
   uint32_t wsum[4][kWaves];
   Digit dig[4];
   unsigned long long cand[64];
@@ -658,14 +659,138 @@ struct RowLists {
   }
 };
 
-// ncopies == 0: no counting pass ran; the workgroup counts its row's first digits
-// itself (a read of the row that leaves it in the caches for the listing pass).
+// One walk of a wavefront's segment [s0, s1) of the row, U x 256 entries per step
+// (thread: 4 consecutive entries per 256; order within a step: u, then lane, then the
+// 4 entries): the entries whose keys `sel` accepts go, in index order, to the
+// wavefront's LDS list (its first kRowCap of them), and `tally` sees every key.
+// Returns how many entries were accepted (uniform).  On a 16-byte aligned row the
+// whole steps take unguarded 16-byte loads, each step's issued before the step ahead
+// of it is listed, so two steps of the row are in flight per wavefront; a partial
+// last step (and an unaligned row) takes loads guarded per element.
+constexpr int kListU = 4;
+template <typename Sel, typename Tally>
+CSA2_DEV void row_list_step(const uint32_t (&key)[kListU][4], int64_t e0, int64_t s1, unsigned long long* __restrict__ list,
+                            int lane, uint32_t& wcount, Sel& sel, Tally& tally) {
+  constexpr int U = kListU;
+  uint32_t keep = 0;  // bit 4u + i
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (e0 + 256 * u + 4 * lane + i < s1) {
+        if (sel(key[u][i])) keep |= 1u << (4 * u + i);
+        tally(key[u][i]);
+      }
+    }
+  // positions: a DPP prefix sum over the lanes of each u's counts, two u per scan
+  // (16-bit halves: at most 256 per half)
+  uint32_t before = wcount;
+#pragma unroll
+  for (int u = 0; u < U; u += 2) {
+    const uint32_t c0 = (uint32_t)__popc((keep >> (4 * u)) & 15u), c1 = (uint32_t)__popc((keep >> (4 * u + 4)) & 15u);
+    const uint32_t incl = wave_incl_scan(c0 | (c1 << 16));
+    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    const uint32_t ex0 = (incl & 0xFFFFu) - c0, ex1 = (incl >> 16) - c1;
+    uint32_t p0 = before + ex0, p1 = before + (tot & 0xFFFFu) + ex1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (keep & (1u << (4 * u + i))) {
+        if (p0 < (uint32_t)kRowCap) list[p0] = composite(key[u][i], (uint32_t)(e0 + 256 * u + 4 * lane + i));
+        ++p0;
+      }
+      if (keep & (1u << (4 * u + 4 + i))) {
+        if (p1 < (uint32_t)kRowCap) list[p1] = composite(key[u + 1][i], (uint32_t)(e0 + 256 * (u + 1) + 4 * lane + i));
+        ++p1;
+      }
+    }
+    before += (tot & 0xFFFFu) + (tot >> 16);
+  }
+  wcount = before;
+}
+
+template <typename Sel, typename Tally>
+CSA2_DEV uint32_t row_list_pass(const float* __restrict__ row, int64_t s0, int64_t s1, bool aligned,
+                                unsigned long long* __restrict__ list, int lane, Sel sel, Tally tally) {
+  constexpr int U = kListU;
+  uint32_t wcount = 0;
+  uint32_t key[U][4];
+  int64_t e0 = s0;
+  if (aligned) {
+    const int64_t whole = s0 + (s1 - s0) / (256 * U) * (256 * U);  // end of the whole steps
+    // two register sets in turn: the next step's loads go out before this step is listed
+    float4 a[U], b[U];
+    auto load = [&](float4 (&v)[U], int64_t at) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const float4*>(row + at + 256 * u + 4 * lane);
+    };
+    auto list_step = [&](const float4 (&v)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        key[u][0] = score_key(v[u].x), key[u][1] = score_key(v[u].y);
+        key[u][2] = score_key(v[u].z), key[u][3] = score_key(v[u].w);
+      }
+      row_list_step(key, e0, s1, list, lane, wcount, sel, tally);
+      e0 += 256 * U;
+    };
+    // Every step loads the next one unconditionally (the last whole step re-reads
+    // itself, unused): with no load under a condition, each wait counts exactly the
+    // loads issued after the ones it waits for.
+    if (e0 < whole) {  // uniform branches throughout
+      const int64_t last = whole - 256 * U;
+      load(a, e0);
+      while (true) {
+        load(b, min(e0 + 256 * U, last));
+        list_step(a);
+        if (e0 >= whole) break;
+        load(a, min(e0 + 256 * U, last));
+        list_step(b);
+        if (e0 >= whole) break;
+      }
+    }
+  }
+  for (; e0 < s1; e0 += 256 * U) {  // a partial step, or an unaligned row
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = e0 + 256 * u + 4 * lane;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) key[u][i] = score_key(j + i < s1 ? row[j + i] : 0.0f);
+    }
+    row_list_step(key, e0, s1, list, lane, wcount, sel, tally);
+  }
+  return wcount;
+}
+
+CSA2_DEV void zero_bins(uint32_t* h) {
+#pragma unroll
+  for (int i = 0; i < kBins / kThreads; ++i) h[threadIdx.x + i * kThreads] = 0u;
+}
+
+// Sampled gate for long rows with no counts given.  The row's own first-digit count
+// would cost a whole read of the row before the listing pass; instead the workgroup
+// reads kGateSamples scores spread evenly over the row and takes as gate G the
+// sample's r-th largest key, cut to its top 24 bits, with r about twice the share
+// k / n of the sample.  One pass then lists every entry with key >= G and counts
+// their first digits.  When at least k entries pass, the k-th largest of the row is
+// among them, the counts give its first digit exactly, and the boundary and the
+// output come from the lists alone.  Otherwise the exact path runs: a gate above the
+// k-th largest (rare: the sample holds twice the expected number) costs the counting
+// pass after all, and a list that overflowed its kRowCap slots costs a second
+// listing pass from the now known first digit.  Either way the selection is the
+// exact one; the gate only decides how many passes over the row it takes.
+constexpr int64_t kGateMinRow = 32768;  // rows from which the gate is tried
+constexpr int kGateMaxK = 2048;         // k up to which twice its share fits the lists
+constexpr int kGateSamples = 4 * kThreads;
+
+// ncopies == 0: no counting pass ran.  Long rows try the sampled gate above; the
+// others (and rows where the gate falls short) count their first digits themselves,
+// in a read of the row that leaves it in the caches for the listing pass.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void topk_row_kernel(const float* __restrict__ scores, int64_t ld,
                                                             const int32_t* __restrict__ n_visible, int k,
                                                             int32_t* __restrict__ topk_idx, uint32_t* __restrict__ hist,
                                                             int ncopies, const int32_t* __restrict__ pool, int npool) {
   __shared__ RowSmem sm;
-  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wavefront
   const int64_t n = n_visible[q];
   int32_t* out = topk_idx + (int64_t)q * k;
   const int32_t* pool_row = pool ? pool + (int64_t)q * npool : nullptr;
@@ -675,126 +800,151 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   }
   const float* row = scores + (int64_t)q * ld;
   uint32_t* gh = hist + (size_t)q * kTopkHistCopies * kBins;
-  uint32_t hb[kPerBins] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-  if (ncopies == 0) {
-#pragma unroll
-    for (int i = 0; i < kBins / kThreads; ++i) sm.h[tid + i * kThreads] = 0u;
-    lds_barrier();
-    // four 16-byte loads in flight per thread per round (8192 entries per round)
-    const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
-    for (int64_t r0 = 0; r0 < n; r0 += 4 * 4 * kThreads) {
-      float v[4][4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t j = r0 + 4 * (tid + u * kThreads);
-        if (aligned && j + 4 <= n) {
-          const float4 f = *reinterpret_cast<const float4*>(row + j);
-          v[u][0] = f.x, v[u][1] = f.y, v[u][2] = f.z, v[u][3] = f.w;
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[u][i] = j + i < n ? row[j + i] : 0.0f;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (r0 + 4 * (tid + u * kThreads) + i < n) atomicAdd(&sm.h[score_key(v[u][i]) >> kBinShift], 1u);
-    }
-    lds_barrier();
-    bins_from_lds(sm.h, hb);
-    lds_barrier();  // every thread has its bins before the digit-2 histogram is cleared below
-  }
-  uint4 hc[kTopkHistCopies][2];
-#pragma unroll
-  for (int r = 0; r < kTopkHistCopies; ++r)
-    if (r < ncopies) {  // uniform
-      hc[r][0] = reinterpret_cast<const uint4*>(gh + r * kBins + bins_lo())[0];
-      hc[r][1] = reinterpret_cast<const uint4*>(gh + r * kBins + bins_lo())[1];
-    }
-#pragma unroll
-  for (int r = 0; r < kTopkHistCopies; ++r)
-    if (r < ncopies) {
-      const uint4 a0 = hc[r][0], a1 = hc[r][1];
-      hb[0] += a0.x, hb[1] += a0.y, hb[2] += a0.z, hb[3] += a0.w;
-      hb[4] += a1.x, hb[5] += a1.y, hb[6] += a1.z, hb[7] += a1.w;
-      // only this workgroup reads the row's histogram: return it to zero
-      if ((a0.x | a0.y | a0.z | a0.w | a1.x | a1.y | a1.z | a1.w) != 0u) {
-        reinterpret_cast<uint4*>(gh + r * kBins + bins_lo())[0] = make_uint4(0u, 0u, 0u, 0u);
-        reinterpret_cast<uint4*>(gh + r * kBins + bins_lo())[1] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-#pragma unroll
-  for (int i = 0; i < kBins / kThreads; ++i) sm.h[tid + i * kThreads] = 0u;
-  if (tid == 0) {
-    sm.ovf = 0u;
-    sm.ncand = 0u;
-  }
-  const Digit d1 = find_digit(hb, (uint32_t)k, sm.wsum[0], &sm.dig[0]);  // its barriers publish the zeroing
-  const uint32_t bstar = (uint32_t)d1.d, above_b = d1.above;
-
-  // this wavefront's segment [s0, s1), U x 256 entries per step (thread: 4 consecutive
-  // entries per 256); order within a step: u, then lane, then the 4 entries
-  constexpr int U = 4;
+  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+  // this wavefront's segment [s0, s1) of the listing passes
   const int64_t seg = (((n + kWaves - 1) / kWaves) + 255) & ~(int64_t)255;
   const int64_t s0 = min(n, (int64_t)wid * seg), s1 = min(n, s0 + seg);
-  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
-  uint32_t wcount = 0;  // entries listed by this wavefront so far (uniform)
-  for (int64_t e0 = s0; e0 < s1; e0 += 256 * U) {
-    uint32_t key[U][4];
+  uint32_t bstar = 0, above_b = 0;
+  bool known = false;   // bstar / above_b hold the row's first digit of the boundary
+  bool listed = false;  // the lists hold every entry of digit >= bstar, sm.h its b* digit-2 counts
+
+  if (ncopies == 0 && n >= kGateMinRow && k <= kGateMaxK) {
+    // the gate: two radix rounds over the samples (first digit, then the next 12 bits)
+    uint32_t sk[kGateSamples / kThreads];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t j = e0 + 256 * u + 4 * lane;
-      float v[4];
-      if (aligned && j + 4 <= s1) {
-        const float4 f = *reinterpret_cast<const float4*>(row + j);
-        v[0] = f.x, v[1] = f.y, v[2] = f.z, v[3] = f.w;
-      } else {
+    for (int i = 0; i < kGateSamples / kThreads; ++i)
+      sk[i] = score_key(row[((int64_t)(tid + kThreads * i) * n) / kGateSamples]);
+    const uint32_t r = (uint32_t)min<int64_t>(kGateSamples, (2 * (int64_t)kGateSamples * k + n - 1) / n + 4);
+    zero_bins(sm.h);
+    lds_barrier();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = j + i < s1 ? row[j + i] : 0.0f;
-      }
+    for (int i = 0; i < kGateSamples / kThreads; ++i) atomicAdd(&sm.h[sk[i] >> kBinShift], 1u);
+    lds_barrier();
+    uint32_t hs[kPerBins];
+    bins_from_lds(sm.h, hs);
+    const Digit g1 = find_digit(hs, r, sm.wsum[0], &sm.dig[0]);  // its barriers: every thread has read its bins
+    zero_bins(sm.h);
+    lds_barrier();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) key[u][i] = score_key(v[i]);
+    for (int i = 0; i < kGateSamples / kThreads; ++i)
+      if ((sk[i] >> kBinShift) == (uint32_t)g1.d) atomicAdd(&sm.h[(sk[i] >> 8) & (kBins - 1)], 1u);
+    lds_barrier();
+    bins_from_lds(sm.h, hs);
+    const Digit g2 = find_digit(hs, r - g1.above, sm.wsum[1], &sm.dig[1]);
+    const uint32_t gate = ((uint32_t)g1.d << kBinShift) | ((uint32_t)g2.d << 8);
+    zero_bins(sm.h);
+    lds_barrier();
+    // one pass: every entry with key >= gate listed, its first digit counted
+    const uint32_t wc = row_list_pass(
+        row, s0, s1, aligned, sm.list[wid], lane, [&](uint32_t key) { return key >= gate; },
+        [&](uint32_t key) {
+          if (key >= gate) atomicAdd(&sm.h[key >> kBinShift], 1u);
+        });
+    if (lane == 0) {
+      sm.cnt[wid] = min(wc, (uint32_t)kRowCap);
+      sm.wtot[wid] = wc;
     }
-    uint32_t keep = 0;  // bit 4u + i
+    lds_barrier();
+    uint32_t passed = 0;
+    bool ovf = false;
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool valid = e0 + 256 * u + 4 * lane + i < s1;
-        const uint32_t bin = key[u][i] >> kBinShift;
-        if (valid && bin >= bstar) keep |= 1u << (4 * u + i);
-        if (valid && bin == bstar) atomicAdd(&sm.h[(key[u][i] >> 8) & (kBins - 1)], 1u);
-      }
-    // positions: a DPP prefix sum over the lanes of each u's counts, two u per scan
-    // (16-bit halves: at most 256 per half)
-    uint32_t before = wcount;
-#pragma unroll
-    for (int u = 0; u < U; u += 2) {
-      const uint32_t c0 = (uint32_t)__popc((keep >> (4 * u)) & 15u), c1 = (uint32_t)__popc((keep >> (4 * u + 4)) & 15u);
-      const uint32_t incl = wave_incl_scan(c0 | (c1 << 16));
-      const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-      const uint32_t ex0 = (incl & 0xFFFFu) - c0, ex1 = (incl >> 16) - c1;
-      uint32_t p0 = before + ex0, p1 = before + (tot & 0xFFFFu) + ex1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (keep & (1u << (4 * u + i))) {
-          if (p0 < (uint32_t)kRowCap) sm.list[wid][p0] = composite(key[u][i], (uint32_t)(e0 + 256 * u + 4 * lane + i));
-          ++p0;
-        }
-        if (keep & (1u << (4 * u + 4 + i))) {
-          if (p1 < (uint32_t)kRowCap)
-            sm.list[wid][p1] = composite(key[u + 1][i], (uint32_t)(e0 + 256 * (u + 1) + 4 * lane + i));
-          ++p1;
-        }
-      }
-      before += (tot & 0xFFFFu) + (tot >> 16);
+    for (int w = 0; w < kWaves; ++w) {
+      passed += sm.wtot[w];
+      ovf |= sm.wtot[w] > (uint32_t)kRowCap;
     }
-    wcount = before;
+    if (passed >= (uint32_t)k) {  // uniform: the boundary's first digit, exactly
+      uint32_t hv[kPerBins];
+      bins_from_lds(sm.h, hv);
+      const Digit d1 = find_digit(hv, (uint32_t)k, sm.wsum[2], &sm.dig[2]);  // its barriers: the counts are read
+      bstar = (uint32_t)d1.d;
+      above_b = d1.above;
+      known = true;
+      zero_bins(sm.h);
+      if (tid == 0) {
+        sm.ovf = 0u;
+        sm.ncand = 0u;
+      }
+      lds_barrier();
+      if (!ovf) {  // the lists hold every entry >= gate: the b* entries' digit-2 counts from them
+        const RowLists src{sm.list, sm.cnt};
+        src.each([&](unsigned long long x) {
+          if ((uint32_t)(x >> 52) == bstar) atomicAdd(&sm.h[(uint32_t)(x >> 40) & (kBins - 1)], 1u);
+        });
+        listed = true;
+      }
+    }
   }
-  if (lane == 0) {
-    sm.cnt[wid] = min(wcount, (uint32_t)kRowCap);
-    if (wcount > (uint32_t)kRowCap) sm.ovf = 1u;
+
+  if (!known) {
+    uint32_t hb[kPerBins] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    if (ncopies == 0) {
+      zero_bins(sm.h);
+      lds_barrier();
+      // four 16-byte loads in flight per thread per round (8192 entries per round)
+      for (int64_t r0 = 0; r0 < n; r0 += 4 * 4 * kThreads) {
+        float v[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t j = r0 + 4 * (tid + u * kThreads);
+          if (aligned && j + 4 <= n) {
+            const float4 f = *reinterpret_cast<const float4*>(row + j);
+            v[u][0] = f.x, v[u][1] = f.y, v[u][2] = f.z, v[u][3] = f.w;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[u][i] = j + i < n ? row[j + i] : 0.0f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (r0 + 4 * (tid + u * kThreads) + i < n) atomicAdd(&sm.h[score_key(v[u][i]) >> kBinShift], 1u);
+      }
+      lds_barrier();
+      bins_from_lds(sm.h, hb);
+      lds_barrier();  // every thread has its bins before the digit-2 histogram is cleared below
+    }
+    uint4 hc[kTopkHistCopies][2];
+#pragma unroll
+    for (int r = 0; r < kTopkHistCopies; ++r)
+      if (r < ncopies) {  // uniform
+        hc[r][0] = reinterpret_cast<const uint4*>(gh + r * kBins + bins_lo())[0];
+        hc[r][1] = reinterpret_cast<const uint4*>(gh + r * kBins + bins_lo())[1];
+      }
+#pragma unroll
+    for (int r = 0; r < kTopkHistCopies; ++r)
+      if (r < ncopies) {
+        const uint4 a0 = hc[r][0], a1 = hc[r][1];
+        hb[0] += a0.x, hb[1] += a0.y, hb[2] += a0.z, hb[3] += a0.w;
+        hb[4] += a1.x, hb[5] += a1.y, hb[6] += a1.z, hb[7] += a1.w;
+        // only this workgroup reads the row's histogram: return it to zero
+        if ((a0.x | a0.y | a0.z | a0.w | a1.x | a1.y | a1.z | a1.w) != 0u) {
+          reinterpret_cast<uint4*>(gh + r * kBins + bins_lo())[0] = make_uint4(0u, 0u, 0u, 0u);
+          reinterpret_cast<uint4*>(gh + r * kBins + bins_lo())[1] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+    zero_bins(sm.h);
+    if (tid == 0) {
+      sm.ovf = 0u;
+      sm.ncand = 0u;
+    }
+    const Digit d1 = find_digit(hb, (uint32_t)k, sm.wsum[0], &sm.dig[0]);  // its barriers publish the zeroing
+    bstar = (uint32_t)d1.d;
+    above_b = d1.above;
+  }
+
+  if (!listed) {
+    // this wavefront's entries in bins >= b*, in index order, into its list; the b*
+    // entries' next 12 key bits into the digit-2 histogram
+    const uint32_t wc = row_list_pass(
+        row, s0, s1, aligned, sm.list[wid], lane, [&](uint32_t key) { return (key >> kBinShift) >= bstar; },
+        [&](uint32_t key) {
+          if ((key >> kBinShift) == bstar) atomicAdd(&sm.h[(key >> 8) & (kBins - 1)], 1u);
+        });
+    if (lane == 0) {
+      sm.cnt[wid] = min(wc, (uint32_t)kRowCap);
+      if (wc > (uint32_t)kRowCap) sm.ovf = 1u;
+    }
   }
   lds_barrier();
   const uint32_t need = (uint32_t)k - above_b;  // 1 <= need <= entries in b*

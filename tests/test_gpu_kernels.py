@@ -345,6 +345,39 @@ def test_topk_many_long_rows_one_workgroup_per_row():
     _topk_case(s, nvis, 64, "long rows k=64")
 
 
+def test_topk_rows_sampled_gate_and_its_fallbacks():
+    """Rows of at least 32,768 scores with k <= 2048 and no counts given take the
+    sampled gate: 2048 evenly spread scores set a gate, one pass lists the entries at
+    or above it, and the selection is resolved from the lists.  Every branch is
+    reached, each compared with the oracle:
+    * the gate holds (N(0,1) rows, all lengths from 32,768 up);
+    * the samples hold the row's largest scores, so fewer than k entries pass the
+      gate and the row is counted after all;
+    * a score that grows (or falls) along the row packs the passing entries into one
+      wavefront's segment, whose list overflows: the row is listed again from the now
+      known first digit (k = 512), or that listing overflows too and the row itself
+      is scanned (k = 2048);
+    * all-equal, tied and all-negative rows;
+    * rows just under 32,768 scores beside them, which count their digits as before."""
+    rng = np.random.default_rng(333)
+    nq, ld = 136, 40_000
+    s = rng.standard_normal((nq, ld)).astype(np.float32)
+    nvis = np.full(nq, ld, np.int32)
+    nvis[:3] = [32_768, 32_767, 20_000]
+    for q in (3, 4):  # the gate's sample positions hold the row's largest scores
+        pos = (np.arange(2048, dtype=np.int64) * int(nvis[q])) // 2048
+        s[q, pos] = 100.0 + rng.random(2048).astype(np.float32)
+    ramp = np.exp2(np.arange(ld) / 1000.0).astype(np.float32)
+    s[5] = ramp              # grows along the row: the best entries in the last segment
+    s[6] = ramp[::-1]        # falls: the best entries in the first segment
+    s[7] = 3.0               # all equal
+    s[8] = rng.integers(0, 200, ld).astype(np.float32)  # many ties
+    s[9] = -np.abs(s[9])     # all negative
+    say("case: top-k 136 rows of up to 40,000 (sampled gate and its fallbacks)")
+    for k in (2048, 512, 17):
+        _topk_case(s, nvis, k, f"gated rows k={k}")
+
+
 def test_topk_few_long_rows_take_chunks():
     """130 rows of 70,000 scores (too few rows to fill the chip with one workgroup
     each): the chunked path with many rows, ragged, tied and short rows included.

@@ -418,7 +418,10 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(AttnArgs a) {
       if (c4 == 0) a.lse[(int64_t)qrow * a.H + hd] = (L > 0.0f) ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
     } else {
       const int64_t pidx = ((int64_t)qrow * a.nsplit + split) * a.H + hd;
-      reinterpret_cast<float4*>(a.part_o + pidx * kLatentDim)[c4] = o;
+      // streaming (nt) stores: the partials are read once, by the merge on other
+      // compute units, so they need not stay in this L2 (the kernel's end then has
+      // fewer dirty lines to write back: 11.6 -> 11.0 us per decode call at 1M)
+      __builtin_nontemporal_store(v4f{o.x, o.y, o.z, o.w}, reinterpret_cast<v4f*>(a.part_o + pidx * kLatentDim) + c4);
       if (c4 == 0) {
         a.part_ml[2 * pidx] = M;
         a.part_ml[2 * pidx + 1] = L;

@@ -36,6 +36,8 @@
 #include "common.hpp"
 #include "host_common.hpp"
 
+#include <type_traits>
+
 namespace csa2 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -585,9 +587,13 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
   store_wide<W8>(smem.x[0], tid, cur, has_main(0), has_win(0));
   if (ntiles > 1) issue_wide<W8>(a, smem.src, tid, kRT, has_main(kRT), has_win(kRT), cur);
   lds_barrier();
-  for (int t = 0; t < ntiles; ++t) {
+  // The loop is unrolled by the three X buffers, so that each step's buffer is a
+  // compile-time constant and its LDS addresses take immediate offsets instead of
+  // per-read address arithmetic.
+  auto tile_step = [&](const int t, auto bsel) __attribute__((always_inline)) {
+    constexpr int B = decltype(bsel)::value;
     const int row0 = t * kRT;
-    const uint16_t* xt = smem.x[t % 3];
+    const uint16_t* xt = smem.x[B];  // a constant buffer: LDS offsets fold into the instructions
     float(&red)[4][2][2][4][64] = smem.red[t & 1];
     // ---- partial logits over this wavefront's 256 channels, two 16-row M-tiles
 #pragma unroll
@@ -602,7 +608,7 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
 #pragma unroll
       for (int r = 0; r < 4; ++r) red[hg][kh][tt][r][lane] = sl[r];
     }
-    if (t + 1 < ntiles) store_wide<W8>(smem.x[(t + 1) % 3], tid, cur, has_main(row0 + kRT), has_win(row0 + kRT));
+    if (t + 1 < ntiles) store_wide<W8>(smem.x[(B + 1) % 3], tid, cur, has_main(row0 + kRT), has_win(row0 + kRT));
     if (t + 2 < ntiles)
       issue_wide<W8>(a, smem.src, tid, row0 + 2 * kRT, has_main(row0 + 2 * kRT), has_win(row0 + 2 * kRT), cur);
     lds_barrier();
@@ -615,7 +621,9 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
         const float v = red[hg][0][tt][r][lane] + red[hg][1][tt][r][lane];
         const int rl = row0 + 8 * g + 4 * tt + r;
         const bool valid = smem.src[rl] != -1;
-        z[tt][r] = valid ? v * a.scale_log2 : -INFINITY;
+        // v * scale once rounded (+ 0), or -inf for a row with no source: a select of
+        // constants, so the logit loads stay unconditional (no branch per row)
+        z[tt][r] = __builtin_fmaf(v, a.scale_log2, valid ? 0.0f : -INFINITY);
         tmax = fmaxf(tmax, z[tt][r]);
       }
     tmax = max_rows(tmax);
@@ -660,6 +668,11 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bhi, acc[mt], 0, 0, 0);
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Blo, acc[mt], 0, 0, 0);
     }
+  };
+  for (int t = 0; t < ntiles; t += 3) {  // ntiles is uniform: every wavefront takes the same steps
+    tile_step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) tile_step(t + 1, std::integral_constant<int, 1>{});
+    if (t + 2 < ntiles) tile_step(t + 2, std::integral_constant<int, 2>{});
   }
 
   // ---- write: lane holds head `head`, channels 256*kh + 16*mt + 4*g + r

@@ -1024,11 +1024,12 @@ __global__ __launch_bounds__(kThreads) void index_score_q2_kernel(
           bsc[nt][kh] = (int)sb[4 * e + c];
         }
       float acc[2] = {0.0f, 0.0f};
-      // step t = (N-tile t / NM, M-tile t % NM); its two MFMAs (K-halves) go out
-      // around the VALU work of step t-2, so neither the accumulate nor the VALU
-      // waits on an MFMA result (the barriers fix that order)
+      // step t = (N-tile t % 2, M-tile t / 2), taken in pairs (both N-tiles of one
+      // M-tile); a pair's two MFMAs per K-half go out around the VALU work of the pair
+      // before it, whose two fma chains (one per N-tile, each in head order) are
+      // interleaved so that neither waits on its own previous fma
       auto mf = [&](int t, int kh, const v16f& c) __attribute__((always_inline)) -> v16f {
-        const int nt = t / NM, mt = t % NM, sl = 2 * mt + kh;
+        const int nt = t & 1, mt = t >> 1, sl = 2 * mt + kh;
         switch (sl & 3) {
           case 0: return mfma32_fp4<0>(A[mt][kh], b[nt][kh], c, (int)asc[sl >> 2], bsc[nt][kh]);
           case 1: return mfma32_fp4<1>(A[mt][kh], b[nt][kh], c, (int)asc[sl >> 2], bsc[nt][kh]);
@@ -1037,19 +1038,33 @@ __global__ __launch_bounds__(kThreads) void index_score_q2_kernel(
         }
       };
       const v16f zero = {};
-      v16f D[2];
+      v16f D0, D1;
 #pragma unroll
-      for (int t = 0; t < S + 2; ++t) {
-        v16f T;
-        if (t < S) T = mf(t, 0, zero);
-        __builtin_amdgcn_sched_barrier(0);
-        if (t >= 2) {
-          const int u = t - 2, nt = u / NM, mt = u % NM;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[nt] = fmaf(wr[16 * mt + r], relu(D[t & 1][r]), acc[nt]);
+      for (int p = 0; p <= NM; ++p) {
+        v16f T0, T1;
+        if (p < NM) {
+          T0 = mf(2 * p, 0, zero);
+          T1 = mf(2 * p + 1, 0, zero);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (t < S) D[t & 1] = mf(t, 1, T);
+        if (p >= 1) {
+          const int mt = p - 1;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            D0[r] = relu(D0[r]);
+            D1[r] = relu(D1[r]);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            acc[0] = fmaf(wr[16 * mt + r], D0[r], acc[0]);
+            acc[1] = fmaf(wr[16 * mt + r], D1[r], acc[1]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (p < NM) {
+          D0 = mf(2 * p, 1, T0);
+          D1 = mf(2 * p + 1, 1, T1);
+        }
       }
       // the sums are complete here for every lane: the MFMAs (which read every lane's
       // operands) must not move into the masked stores below

@@ -585,6 +585,10 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
   WideRegs cur;
   issue_wide<W8>(a, smem.src, tid, 0, has_main(0), has_win(0), cur);
   store_wide<W8>(smem.x[0], tid, cur, has_main(0), has_win(0));
+  // the Q operand is complete before the tile loop, whose waits then cover only the
+  // tile loads in flight
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qop[ks].x), "v"(qop[ks].y), "v"(qop[ks].z), "v"(qop[ks].w));
   if (ntiles > 1) issue_wide<W8>(a, smem.src, tid, kRT, has_main(kRT), has_win(kRT), cur);
   lds_barrier();
   // The loop is unrolled by the three X buffers, so that each step's buffer is a
@@ -595,18 +599,22 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
     const int row0 = t * kRT;
     const uint16_t* xt = smem.x[B];  // a constant buffer: LDS offsets fold into the instructions
     float(&red)[4][2][2][4][64] = smem.red[t & 1];
-    // ---- partial logits over this wavefront's 256 channels, two 16-row M-tiles
+    // ---- partial logits over this wavefront's 256 channels, two 16-row M-tiles whose
+    // MFMA chains alternate (no MFMA waits on the one just before it)
+    {
+      v4f sl[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      v4f sl = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int xrow = 8 * (n16 >> 2) + 4 * tt + (n16 & 3);  // lane group g gets rows 8g .. 8g+7
-        const uint4 xa = reinterpret_cast<const uint4*>(xt + xrow * kWStride)[wchunk(xrow, 32 * kh + 4 * ks + g)];
-        sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(qop[ks]), sl, 0, 0, 0);
-      }
+        for (int tt = 0; tt < 2; ++tt) {
+          const int xrow = 8 * (n16 >> 2) + 4 * tt + (n16 & 3);  // lane group g gets rows 8g .. 8g+7
+          const uint4 xa = reinterpret_cast<const uint4*>(xt + xrow * kWStride)[wchunk(xrow, 32 * kh + 4 * ks + g)];
+          sl[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(qop[ks]), sl[tt], 0, 0, 0);
+        }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[hg][kh][tt][r][lane] = sl[r];
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[hg][kh][tt][r][lane] = sl[tt][r];
     }
     if (t + 1 < ntiles) store_wide<W8>(smem.x[(B + 1) % 3], tid, cur, has_main(row0 + kRT), has_win(row0 + kRT));
     if (t + 2 < ntiles)
@@ -659,14 +667,22 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
     // (rows 8g + n16/4 and 4 below it share wchunk's row term)
     const int tr_c = n16 & 3, tr_r = 8 * g + (n16 >> 2);
     const uint16_t* tr_row = xt + tr_r * kWStride + 4 * (tr_c & 1);
+    // two M-tiles at a time, so that each accumulator's second MFMA (P's remainder)
+    // is not issued right behind its first
 #pragma unroll
-    for (int mt = 0; mt < 16; ++mt) {
-      const uint16_t* tp = tr_row + 8 * wchunk(tr_r, 32 * kh + 2 * mt + (tr_c >> 1));
-      const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)tp);
-      const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tp + 4 * kWStride));
-      const bf16x8 A = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bhi, acc[mt], 0, 0, 0);
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Blo, acc[mt], 0, 0, 0);
+    for (int mt = 0; mt < 16; mt += 2) {
+      bf16x8 A[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint16_t* tp = tr_row + 8 * wchunk(tr_r, 32 * kh + 2 * (mt + u) + (tr_c >> 1));
+        const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)tp);
+        const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tp + 4 * kWStride));
+        A[u] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) acc[mt + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[u], Bhi, acc[mt + u], 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) acc[mt + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[u], Blo, acc[mt + u], 0, 0, 0);
     }
   };
   for (int t = 0; t < ntiles; t += 3) {  // ntiles is uniform: every wavefront takes the same steps

@@ -50,6 +50,7 @@ constexpr int kRT = 32;              // rows per tile
 constexpr int kXStride = 512 + 8;    // bf16 elements per row of X in LDS (padding vs bank conflicts)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazyMax = 8.0f;  // prefill: largest weight 2^8 before the reference maximum moves
 
 // 2^x with V_EXP_F32 alone: exact where the library exp2f is (results of normal
 // magnitude), it only skips the library's rescaling for results below 2^-126, which
@@ -635,7 +636,10 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_wide_kernel(AttnArgs a) 
         tmax = fmaxf(tmax, z[tt][r]);
       }
     tmax = max_rows(tmax);
-    const float m_new = fmaxf(m_run, tmax);
+    // the reference maximum moves only when a tile's maximum passes it by more than
+    // kLazyMax (log2 units), so the weights stay <= 2^kLazyMax and O is rescaled on a
+    // few tiles per query instead of on most
+    const float m_new = (tmax > m_run + kLazyMax) ? tmax : m_run;
     const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
     float p[2][4];
     float psum = 0.0f;

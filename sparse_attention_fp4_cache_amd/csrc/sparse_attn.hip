@@ -50,7 +50,7 @@ constexpr int kRT = 32;              // rows per tile
 constexpr int kXStride = 512 + 8;    // bf16 elements per row of X in LDS (padding vs bank conflicts)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazyMax = 8.0f;  // prefill: largest weight 2^8 before the reference maximum moves
+constexpr float kLazyMax = 8.0f;  // one-range kernel: largest weight 2^8 before the reference maximum moves
 
 // 2^x with V_EXP_F32 alone: exact where the library exp2f is (results of normal
 // magnitude), it only skips the library's rescaling for results below 2^-126, which

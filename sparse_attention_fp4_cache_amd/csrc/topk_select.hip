@@ -668,7 +668,8 @@ struct RowLists {
 // of it is listed, so two steps of the row are in flight per wavefront; a partial
 // last step (and an unaligned row) takes loads guarded per element.
 constexpr int kListU = 4;
-template <typename Sel, typename Tally>
+// FULL: the whole step lies inside the segment, so no entry needs its bound checked.
+template <bool FULL, typename Sel, typename Tally>
 CSA2_DEV void row_list_step(const uint32_t (&key)[kListU][4], int64_t e0, int64_t s1, unsigned long long* __restrict__ list,
                             int lane, uint32_t& wcount, Sel& sel, Tally& tally) {
   constexpr int U = kListU;
@@ -677,7 +678,7 @@ CSA2_DEV void row_list_step(const uint32_t (&key)[kListU][4], int64_t e0, int64_
   for (int u = 0; u < U; ++u)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (e0 + 256 * u + 4 * lane + i < s1) {
+      if (FULL || e0 + 256 * u + 4 * lane + i < s1) {
         if (sel(key[u][i])) keep |= 1u << (4 * u + i);
         tally(key[u][i]);
       }
@@ -729,7 +730,7 @@ CSA2_DEV uint32_t row_list_pass(const float* __restrict__ row, int64_t s0, int64
         key[u][0] = score_key(v[u].x), key[u][1] = score_key(v[u].y);
         key[u][2] = score_key(v[u].z), key[u][3] = score_key(v[u].w);
       }
-      row_list_step(key, e0, s1, list, lane, wcount, sel, tally);
+      row_list_step<true>(key, e0, s1, list, lane, wcount, sel, tally);
       e0 += 256 * U;
     };
     // Every step loads the next one unconditionally (the last whole step re-reads
@@ -755,7 +756,7 @@ CSA2_DEV uint32_t row_list_pass(const float* __restrict__ row, int64_t s0, int64
 #pragma unroll
       for (int i = 0; i < 4; ++i) key[u][i] = score_key(j + i < s1 ? row[j + i] : 0.0f);
     }
-    row_list_step(key, e0, s1, list, lane, wcount, sel, tally);
+    row_list_step<false>(key, e0, s1, list, lane, wcount, sel, tally);
   }
   return wcount;
 }
